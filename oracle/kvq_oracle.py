@@ -1,0 +1,371 @@
+"""Plain NumPy oracle for KIVI-style quantized-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY: used by tests/, by the smoke check and by the bench's
+CPU-baseline leg; never by the library.  Shares no code with the HIP path.
+
+Sources (web pages, cited by title and section):
+  [KIVI]  juejin.cn, "大模型量化技术原理：KIVI、IntactKV、KVQuant", part KIVI,
+          sections 背景 (background), 为什么键和值缓存应该沿着不同的维度进行量化
+          (why K and V are quantized along different axes) and 工作原理
+          (how it works: grouped part + full-precision residual, the R-token
+          key flush, the value queue, prefill).
+  [HFQ]   pgsm.cn news 20017, KV-cache quantization article, section 2.1
+          (affine quantization X_Q = round(X/S) - Z with scale S and zero-point
+          offset Z, symmetric vs asymmetric), 2.2 (keys per channel, values per
+          token), 3.1 (fixed-size fp16 residual cache, batch-quantized into the
+          main cache when full), 3.2 (bytes per token for Llama-2-7B), 4.1
+          (knobs nbits / group_size / residual_length).
+
+Precision: the quantizer runs in float32 on fp16 inputs (every step is one
+correctly rounded IEEE float32 operation, rounding half to even); attention is
+accumulated in float64 on the float32 dequantized cache.
+
+Parity status of each function (pins live in tests/test_oracle_*.py):
+  quantize_groups        pinned: on-grid exactness (recovers S, Z, codes of a
+                         lattice exactly), code(min) == 0, code(max) in
+                         {2^b-2, 2^b-1}, monotone codes, |x - x_hat| <= S/2 + eps,
+                         nearest-level brute force, constant groups exact.
+  dequantize             pinned with quantize_groups (round trip).
+  pack_rows/unpack_rows  pinned: literal words from the layout definition,
+                         brute-force enumeration of all codes in a word.
+  QuantizedKVCache       pinned: (l - r) % G == 0 after every call, one flush
+                         per R appends, prefill(L)+appends == prefill(L+m),
+                         FIFO and chunked value codes agree per token, cache
+                         with R > n reduces to plain fp16 attention.
+  attention              pinned: torch float64 SDPA on the same operands,
+                         q == 0 gives the mean of V, n == 1 gives v_0,
+                         brute-force scalar loops on tiny inputs.
+  byte accounting        pinned: the per-token byte table for Llama-2-7B
+                         (524,288 / 262,144 / 131,072 / 65,536 bytes) and the
+                         ~5 GB for 10k fp16 tokens in [HFQ] 1 and 3.2.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
+    "attention", "kv_code_bytes_per_token", "attention_call_bytes", "flush_bytes",
+    "CHUNK", "FIFO",
+]
+
+CHUNK = 0   # value residual flushed as a block of R tokens, like the keys ([HFQ] 3.1)
+FIFO = 1    # value residual kept as a queue of the R most recent tokens ([KIVI] 工作原理)
+
+_F32 = np.float32
+
+
+# --------------------------------------------------------------------------- quantizer
+def quantize_groups(x, bits: int):
+    """Asymmetric affine quantization of each group along the last axis.
+
+    [HFQ] 2.1 writes the quantizer as X_Q = round(X / S) - Z with scale S and
+    zero-point offset Z; the asymmetric form maps each group's own [min, max]
+    range onto the 2^b integer levels ([KIVI] 背景: 2-bit asymmetric).
+
+      S      = (max - min) / (2^b - 1)       (float32, one rounding each)
+               a constant group (max == min) takes S = |min|, or 1 when min == 0,
+               so it reconstructs exactly
+      Z      = rint(min / S)                 (integer, stored as int16)
+      code_i = clamp(rint(x_i / S) - Z, 0, 2^b - 1)
+
+    x: float16 array, groups along the last axis.
+    Returns (codes uint8 same shape, S float32 [...], Z int16 [...]).
+    """
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    xf = np.asarray(x, dtype=np.float16).astype(_F32)
+    qmax = _F32((1 << bits) - 1)
+    mn = xf.min(axis=-1)
+    mx = xf.max(axis=-1)
+    span = (mx - mn).astype(_F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s_range = (span / qmax).astype(_F32)
+    s_const = np.where(mn != 0, np.abs(mn), _F32(1.0)).astype(_F32)
+    scale = np.where(mx > mn, s_range, s_const).astype(_F32)
+    zero = np.rint((mn / scale).astype(_F32)).astype(_F32)
+    q = np.rint((xf / scale[..., None]).astype(_F32)).astype(_F32) - zero[..., None]
+    codes = np.clip(q, _F32(0), qmax).astype(np.uint8)
+    if np.any(np.abs(zero) > 32767):
+        raise OverflowError("zero-point does not fit int16")
+    return codes, scale, zero.astype(np.int16)
+
+
+def dequantize(codes, scale, zero):
+    """x_hat = S * (code + Z), float32: the inverse of the [HFQ] 2.1 map.
+
+    codes [..., G]; scale and zero broadcast over the last axis.
+    """
+    c = np.asarray(codes).astype(_F32)
+    z = np.asarray(zero).astype(_F32)[..., None]
+    s = np.asarray(scale, dtype=_F32)[..., None]
+    return ((c + z) * s).astype(_F32)
+
+
+# --------------------------------------------------------------------------- packing
+def pack_rows(codes, bits: int):
+    """Pack the d codes of each token row into d*bits/32 little-endian words.
+
+    Channel c of a row sits at bits [(c*bits) % 32, +bits) of word (c*bits)//32.
+    codes uint8 [..., d]  ->  uint32 [..., d*bits//32].
+    """
+    codes = np.asarray(codes, dtype=np.uint32)
+    per = 32 // bits
+    d = codes.shape[-1]
+    assert d % per == 0
+    grouped = codes.reshape(codes.shape[:-1] + (d // per, per))
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    return np.bitwise_or.reduce(grouped << shifts, axis=-1).astype(np.uint32)
+
+
+def unpack_rows(words, bits: int, d: int):
+    """Inverse of :func:`pack_rows`."""
+    words = np.asarray(words, dtype=np.uint32)
+    per = 32 // bits
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))
+    mask = np.uint32((1 << bits) - 1)
+    out = (words[..., None] >> shifts) & mask
+    return out.reshape(words.shape[:-1] + (d,)).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------- cache
+class QuantizedKVCache:
+    """One layer's KV cache for every (batch, kv-head) unit; all units share n.
+
+    Keys ([KIVI] 工作原理): the token axis is split into a grouped part
+    X_Kg = X_K[:l-r], kept only as per-channel group quantizations over G
+    tokens, and a full-precision remainder X_Kr = X_K[l-r:], with l - r
+    divisible by G.  A new key joins X_Kr; when X_Kr holds R tokens it is
+    quantized, appended to the grouped part and emptied (R % G == 0).
+
+    Values: quantized per token over groups of G channels ([HFQ] 2.2).  The
+    chunked policy treats the value residual exactly like the key residual,
+    which is the fixed-size fp16 residual cache of [HFQ] 3.1.  The FIFO policy
+    follows the queue of [KIVI] 工作原理: a new value is pushed and, once the
+    queue would exceed R entries, the oldest one is popped, quantized and
+    appended.
+
+    Prefill ([KIVI] 工作原理, prefill paragraph) stores only the quantized part
+    plus the residual; it never changes the fp16 inputs.
+    """
+
+    def __init__(self, bits, group, residual, batch, kv_heads, head_dim, v_policy=CHUNK):
+        if bits not in (2, 4):
+            raise ValueError("bits must be 2 or 4")
+        if residual <= 0 or residual % group:
+            raise ValueError("R must be a positive multiple of G")
+        if head_dim % group:
+            raise ValueError("head_dim must be a multiple of G")
+        self.bits, self.G, self.R = bits, group, residual
+        self.B, self.H, self.d = batch, kv_heads, head_dim
+        self.v_policy = v_policy
+        B, H, d, G = batch, kv_heads, head_dim, group
+        self.kq_codes = np.zeros((B, H, 0, d), np.uint8)
+        self.kq_scale = np.zeros((B, H, 0, d), _F32)   # [.., group, channel]
+        self.kq_zero = np.zeros((B, H, 0, d), np.int16)
+        self.kr = np.zeros((B, H, 0, d), np.float16)    # X_Kr, token order
+        self.vq_codes = np.zeros((B, H, 0, d), np.uint8)
+        self.vq_scale = np.zeros((B, H, 0, d // G), _F32)  # [.., token, channel group]
+        self.vq_zero = np.zeros((B, H, 0, d // G), np.int16)
+        self.vr = np.zeros((B, H, 0, d), np.float16)    # value residual / queue
+        self.n = 0
+        self.flushes = 0
+        self.started = False
+
+    # counters -----------------------------------------------------------------
+    @property
+    def nq_k(self):
+        return self.kq_codes.shape[2]
+
+    @property
+    def nq_v(self):
+        return self.vq_codes.shape[2]
+
+    # quantization of token blocks ----------------------------------------------
+    def _quantize_keys(self, k):
+        """k fp16 [B,H,m,d], m % G == 0 -> per-channel groups of G tokens."""
+        B, H, m, d = k.shape
+        G = self.G
+        assert m % G == 0
+        grp = k.reshape(B, H, m // G, G, d).transpose(0, 1, 2, 4, 3)   # [.., g, c, t]
+        codes, s, z = quantize_groups(grp, self.bits)
+        codes = codes.transpose(0, 1, 2, 4, 3).reshape(B, H, m, d)
+        return codes, s, z                                            # s,z [.., g, c]
+
+    def _quantize_values(self, v):
+        """v fp16 [B,H,m,d] -> per-token groups of G channels."""
+        B, H, m, d = v.shape
+        G = self.G
+        grp = v.reshape(B, H, m, d // G, G)
+        codes, s, z = quantize_groups(grp, self.bits)
+        return codes.reshape(B, H, m, d), s, z                        # s,z [.., t, j]
+
+    def _append_keys(self, k):
+        c, s, z = self._quantize_keys(k)
+        self.kq_codes = np.concatenate([self.kq_codes, c], axis=2)
+        self.kq_scale = np.concatenate([self.kq_scale, s], axis=2)
+        self.kq_zero = np.concatenate([self.kq_zero, z], axis=2)
+
+    def _append_values(self, v):
+        c, s, z = self._quantize_values(v)
+        self.vq_codes = np.concatenate([self.vq_codes, c], axis=2)
+        self.vq_scale = np.concatenate([self.vq_scale, s], axis=2)
+        self.vq_zero = np.concatenate([self.vq_zero, z], axis=2)
+
+    # public state transitions --------------------------------------------------
+    def prefill(self, k, v):
+        """k, v fp16 [B,H,L,d]; only allowed on an empty cache."""
+        if self.started:
+            raise RuntimeError("prefill on a non-empty cache")
+        k = np.asarray(k, np.float16)
+        v = np.asarray(v, np.float16)
+        L = k.shape[2]
+        r = L % self.R                      # residual count; l - r divisible by R (hence G)
+        nq = L - r
+        self._append_keys(k[:, :, :nq])
+        self.kr = k[:, :, nq:].copy()
+        if self.v_policy == CHUNK:
+            nv = nq
+        else:
+            nv = max(0, L - self.R)         # the queue keeps the R most recent values
+        self._append_values(v[:, :, :nv])
+        self.vr = v[:, :, nv:].copy()
+        self.n = L
+        self.started = True
+
+    def append(self, k_new, v_new):
+        """k_new, v_new fp16 [B,H,d]: one decode step's new key and value."""
+        if not self.started:
+            raise RuntimeError("append before prefill")
+        k_new = np.asarray(k_new, np.float16)[:, :, None, :]
+        v_new = np.asarray(v_new, np.float16)[:, :, None, :]
+        self.kr = np.concatenate([self.kr, k_new], axis=2)
+        flushed = False
+        if self.kr.shape[2] == self.R:      # X_Kr reached R: quantize, append, reset
+            self._append_keys(self.kr)
+            self.kr = self.kr[:, :, :0]
+            flushed = True
+        self.vr = np.concatenate([self.vr, v_new], axis=2)
+        if self.v_policy == CHUNK:
+            if self.vr.shape[2] == self.R:
+                self._append_values(self.vr)
+                self.vr = self.vr[:, :, :0]
+        else:
+            if self.vr.shape[2] > self.R:   # pop the oldest value and quantize it
+                self._append_values(self.vr[:, :, :1])
+                self.vr = self.vr[:, :, 1:]
+        self.flushes += int(flushed)
+        self.n += 1
+
+    # views ------------------------------------------------------------------------
+    def dequantized(self):
+        """(K_hat, V_hat) float32 [B,H,n,d] in token order."""
+        B, H, d, G = self.B, self.H, self.d, self.G
+        nqk, nqv = self.nq_k, self.nq_v
+        kc = self.kq_codes.reshape(B, H, nqk // G, G, d).transpose(0, 1, 2, 4, 3)
+        kh = dequantize(kc, self.kq_scale, self.kq_zero)                  # [.., g, c, t]
+        kh = kh.transpose(0, 1, 2, 4, 3).reshape(B, H, nqk, d)
+        vc = self.vq_codes.reshape(B, H, nqv, d // G, G)
+        vh = dequantize(vc, self.vq_scale, self.vq_zero).reshape(B, H, nqv, d)
+        K = np.concatenate([kh, self.kr.astype(_F32)], axis=2)
+        V = np.concatenate([vh, self.vr.astype(_F32)], axis=2)
+        return K, V
+
+    def buffers(self, max_tokens):
+        """The cache serialized in the library's device layout.
+
+        k_codes u32 [B,H,cap,d*b/32]   token rows of packed per-channel codes
+        k_scale f32 [B,H,cap/G,d]      one scale per (token group, channel)
+        k_zero  i16 [B,H,cap/G,d]
+        v_codes u32 [B,H,cap,d*b/32]
+        v_scale f32 [B,H,cap,d/G]      one scale per (token, channel group)
+        v_zero  i16 [B,H,cap,d/G]
+        k_resid, v_resid f16 [B,H,R,d] token t at slot t mod R (live slots only;
+                                       the others hold whatever was there)
+        """
+        B, H, d, G, R, b = self.B, self.H, self.d, self.G, self.R, self.bits
+        cap = max_tokens
+        W = d * b // 32
+        out = {
+            "k_codes": np.zeros((B, H, cap, W), np.uint32),
+            "k_scale": np.zeros((B, H, cap // G, d), _F32),
+            "k_zero": np.zeros((B, H, cap // G, d), np.int16),
+            "v_codes": np.zeros((B, H, cap, W), np.uint32),
+            "v_scale": np.zeros((B, H, cap, d // G), _F32),
+            "v_zero": np.zeros((B, H, cap, d // G), np.int16),
+            "k_resid": np.zeros((B, H, R, d), np.float16),
+            "v_resid": np.zeros((B, H, R, d), np.float16),
+        }
+        nqk, nqv = self.nq_k, self.nq_v
+        out["k_codes"][:, :, :nqk] = pack_rows(self.kq_codes, b)
+        out["k_scale"][:, :, :nqk // G] = self.kq_scale
+        out["k_zero"][:, :, :nqk // G] = self.kq_zero
+        out["v_codes"][:, :, :nqv] = pack_rows(self.vq_codes, b)
+        out["v_scale"][:, :, :nqv] = self.vq_scale
+        out["v_zero"][:, :, :nqv] = self.vq_zero
+        for i in range(self.kr.shape[2]):
+            out["k_resid"][:, :, (nqk + i) % R] = self.kr[:, :, i]
+        for i in range(self.vr.shape[2]):
+            out["v_resid"][:, :, (nqv + i) % R] = self.vr[:, :, i]
+        return out
+
+    def live_resid_slots(self):
+        """Ring slots that hold live residual tokens: (k_slots, v_slots)."""
+        R = self.R
+        ks = [(self.nq_k + i) % R for i in range(self.kr.shape[2])]
+        vs = [(self.nq_v + i) % R for i in range(self.vr.shape[2])]
+        return ks, vs
+
+
+# --------------------------------------------------------------------------- attention
+def attention(q, K, V, softmax_scale):
+    """Decode attention of one query per head over the whole cache, float64.
+
+    out = softmax(scale * q K^T) V with no mask (the new token is part of the
+    cache and attends to every cached token, itself included).  Query head h
+    reads kv head h // (Hq / Hkv).
+
+    q fp16/float [B,Hq,d]; K, V float32 [B,Hkv,n,d]  ->  float64 [B,Hq,d].
+    """
+    q = np.asarray(q).astype(np.float64)
+    K = np.asarray(K).astype(np.float64)
+    V = np.asarray(V).astype(np.float64)
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    rep = Hq // Hkv
+    Kx = np.repeat(K, rep, axis=1)                  # [B,Hq,n,d]
+    Vx = np.repeat(V, rep, axis=1)
+    s = np.einsum("bhd,bhnd->bhn", q, Kx) * float(softmax_scale)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return np.einsum("bhn,bhnd->bhd", p, Vx)
+
+
+# --------------------------------------------------------------------------- bytes
+def kv_code_bytes_per_token(layers, kv_heads, head_dim, bits):
+    """Cache bytes one token adds for a whole model, codes only ([HFQ] 3.2)."""
+    return layers * 2 * kv_heads * head_dim * bits // 8
+
+
+def attention_call_bytes(batch, q_heads, kv_heads, head_dim, bits, group, n, nq_k, nq_v):
+    """Algorithmic bytes one decode-attention call must move.
+
+    Per unit: key codes + key metadata (fp32 scale + int16 zero per
+    (group, channel)) + value codes + value metadata (per (token, channel
+    group)) + the fp16 residual keys and values; plus the fp16 query and the
+    fp32 output of every query head.
+    """
+    d, b, G = head_dim, bits, group
+    per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6
+                + nq_v * d * b // 8 + nq_v * (d // G) * 6
+                + ((n - nq_k) + (n - nq_v)) * d * 2)
+    return batch * kv_heads * per_unit + batch * q_heads * d * (2 + 4)
+
+
+def flush_bytes(batch, kv_heads, head_dim, bits, group, residual):
+    """Bytes of one residual flush: read R fp16 keys and values, write codes + metadata."""
+    d, b, G, R = head_dim, bits, group, residual
+    read = R * d * 2 * 2
+    write = 2 * R * d * b // 8 + (R // G) * d * 6 + R * (d // G) * 6
+    return batch * kv_heads * (read + write)
