@@ -1,0 +1,225 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode step of the whole batch through every layer of the
+workload: per layer, kvq_append_token (residual write, eager flush when due)
+then kvq_decode_attention (split kernel + merge).  Caches are prefilled before
+timing; inputs for every step are resident in HBM when timing starts.
+
+Prints one JSON line:
+  value        effective KV GB/s of the whole timed loop (algorithmic bytes of
+               every attention call / loop time)
+  tokens_per_s batch * steps / loop time
+  roofline     split-kernel bytes per launch / its average duration (HIP
+               events on the library's stream), against 8 TB/s
+  cpu_baseline the NumPy oracle's decode-attention call on a sample of units,
+               timed on this host, scaled to the same byte formula
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import decode_attention_token_amd as kvq  # noqa: E402
+from workloads import WORKLOADS, LLAMA7B_2BIT, gen_new_tokens, gen_prefill, gen_queries  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn effective KV GB/s (% HBM peak) + tokens/s, Llama-2-7B shape 2-bit"
+
+
+def attn_bytes(w, n, nq_k, nq_v):
+    """Algorithmic bytes of one decode-attention call (codes, fp32 scale + int16
+    zero per group, fp16 residual, fp16 q, fp32 out)."""
+    d, b, G = w.head_dim, w.bits, w.group
+    per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6 + nq_v * d * b // 8 + nq_v * (d // G) * 6
+                + ((n - nq_k) + (n - nq_v)) * d * 2)
+    return w.batch * w.num_kv_heads * per_unit + w.batch * w.num_q_heads * d * 6
+
+
+def build_caches(w, layers, max_tokens, dev):
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, max_tokens, w.v_policy)
+    caches = []
+    for layer in range(layers):
+        k, v = gen_prefill(w, layer, dev)
+        c = kvq.KVCache(cfg, dev)
+        c.prefill(k, v)
+        torch.cuda.synchronize()
+        del k, v
+        caches.append(c)
+    torch.cuda.empty_cache()
+    return cfg, caches
+
+
+def sample_units(w, count=64, seed=7):
+    return [int(u) for u in np.random.default_rng(seed).permutation(w.units)[:count]]
+
+
+def host_sample(w, units, dev):
+    """Host copies of the sampled units' layer-0 inputs (the same fp16 bits the GPU caches use)."""
+    k, v = gen_prefill(w, 0, dev)
+    kn, vn = gen_new_tokens(w, 0, dev, steps=1)
+    q = gen_queries(w, 0, dev, steps=1)[0]
+    hpg = w.num_q_heads // w.num_kv_heads
+    out = []
+    for u in units:
+        b, h = divmod(u, w.num_kv_heads)
+        out.append((k[b:b + 1, h:h + 1].cpu().numpy(), v[b:b + 1, h:h + 1].cpu().numpy(),
+                    kn[0][b:b + 1, h:h + 1].cpu().numpy(), vn[0][b:b + 1, h:h + 1].cpu().numpy(),
+                    q[b:b + 1, h * hpg:(h + 1) * hpg].cpu().numpy()))
+    del k, v
+    return out
+
+
+def cpu_baseline(w, sample, budget_s=12.0):
+    """The oracle's decode-attention call (dequantize + float64 attention) on
+    sampled units, one NumPy thread, scaled by the algorithmic byte formula."""
+    import oracle
+    hpg = w.num_q_heads // w.num_kv_heads
+    unit_w = w.scaled(batch=1, num_kv_heads=1, num_q_heads=hpg)
+    t_total, done, nbytes = 0.0, 0, 0
+    for k, v, kn, vn, q in sample:
+        ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+        ref.prefill(k, v)
+        ref.append(kn, vn)
+        t0 = time.perf_counter()
+        K, V = ref.dequantized()
+        oracle.attention(q, K, V, 1.0 / math.sqrt(w.head_dim))
+        t_total += time.perf_counter() - t0
+        done += 1
+        nbytes += attn_bytes(unit_w, ref.n, ref.nq_k, ref.nq_v)
+        if t_total >= budget_s:
+            break
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.units} (batch, kv-head) units, one decode-attention call each "
+                      f"(dequantize + float64 attention) at n={w.context + 1}, same fp16 inputs as the "
+                      f"GPU caches; {t_total:.1f} s on one host thread",
+            "seconds_per_call_extrapolated": round(t_total / done * w.units, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=LLAMA7B_2BIT.config_id,
+                    help="workload id (2 = Llama-2-7B layer shape, 2-bit)")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    steps = w.steps if args.steps is None else args.steps
+    layers = w.layers if args.layers is None else args.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    need = w.context + args.warmup + steps
+    max_tokens = ((need + w.residual - 1) // w.residual) * w.residual
+    sample = None
+    if not args.no_cpu:
+        sample = host_sample(w, sample_units(w), dev)
+    print(f"# workload {w.name}: prefill {layers} layer caches", file=sys.stderr, flush=True)
+    cfg, caches = build_caches(w, layers, max_tokens, dev)
+    total = args.warmup + steps
+    news = [gen_new_tokens(w, layer, dev, steps=total) for layer in range(layers)]
+    qs = [gen_queries(w, layer, dev, steps=total) for layer in range(layers)]
+    outs = [torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+            for _ in range(layers)]
+    ws = caches[0].workspace(max_tokens, args.splits)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    stream = torch.cuda.current_stream()
+
+    def step(i, count_bytes):
+        nb = 0
+        for layer in range(layers):
+            c = caches[layer]
+            kn, vn = news[layer]
+            c.append(kn[i], vn[i])
+            c.attention(qs[layer][i], scale, outs[layer], ws, args.splits)
+            if count_bytes:
+                nb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
+        return nb
+
+    print("# warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    print("# timed loop", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    nbytes = 0
+    for i in range(args.warmup, total):
+        nbytes += step(i, True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    # attention-only passes, timed with HIP events on the library's stream
+    print("# kernel timing", file=sys.stderr, flush=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    last = total - 1
+    calls, cb = 0, 0
+    ev0.record(stream)
+    for _ in range(args.reps):
+        for layer in range(layers):
+            c = caches[layer]
+            c.attention(qs[layer][last], scale, outs[layer], ws, args.splits)
+            calls += 1
+            cb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    call_us = ev0.elapsed_time(ev1) * 1e3 / calls
+    call_bytes = cb / calls
+    achieved = call_bytes / (call_us * 1e-6) / 1e9
+
+    splits_used = args.splits or kvq.kvq_auto_splits(cfg, caches[0].n_tokens)
+    res = {
+        "metric": METRIC,
+        "value": round(nbytes / dt / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "tokens_per_s": round(w.batch * steps / dt, 1),
+        "hbm_peak_frac": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": w.context,
+                   "bits": w.bits, "group": w.group, "residual": w.residual, "layers": layers,
+                   "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode attention call (split + merge)", "avg_call_us": round(call_us, 2),
+                     "bytes_per_call": int(call_bytes)},
+    }
+    if not args.no_cpu:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        del caches, news, qs
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(w, sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

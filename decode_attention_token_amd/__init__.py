@@ -1,0 +1,224 @@
+"""Python binding of libkvq: quantized KV cache + decode attention on MI355X.
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+behind the C ABI declared in include/kvq.h.  PyTorch supplies device memory
+and the current HIP stream.  There is no CPU fallback: if libkvq.so is not
+built, importing the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_DEVICE, KVQ_ERR_UNSUPPORTED = range(6)
+KVQ_V_CHUNK, KVQ_V_FIFO = 0, 1
+
+EXPORTED = [
+    "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
+    "kvq_append_token", "kvq_decode_attention", "kvq_status_string", "kvq_last_error",
+]
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "bits", "group", "residual", "batch", "num_q_heads", "num_kv_heads", "head_dim",
+        "max_tokens", "v_policy")]
+
+
+class kvq_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
+        ("n_tokens", ctypes.c_int64), ("nq_k", ctypes.c_int64), ("nq_v", ctypes.c_int64),
+        ("started", ctypes.c_int32), ("flushes", ctypes.c_int32),
+    ]
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvq status {status}: {msg}")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libkvq.so (built in-tree) and declares its signatures."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.kvq_layout_bytes.argtypes = [P(kvq_config), P(kvq_layout)]
+    lib.kvq_layout_bytes.restype = ctypes.c_int
+    lib.kvq_auto_splits.argtypes = [P(kvq_config), ctypes.c_int64]
+    lib.kvq_auto_splits.restype = ctypes.c_int32
+    lib.kvq_workspace_bytes.argtypes = [P(kvq_config), ctypes.c_int64, ctypes.c_int32]
+    lib.kvq_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_quantize_prefill.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, ctypes.c_int64, vp]
+    lib.kvq_quantize_prefill.restype = ctypes.c_int
+    lib.kvq_append_token.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, vp]
+    lib.kvq_append_token.restype = ctypes.c_int
+    lib.kvq_decode_attention.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_float, vp, vp,
+                                         ctypes.c_size_t, ctypes.c_int32, vp]
+    lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_status_string.argtypes = [ctypes.c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    lib.kvq_last_error.argtypes = []
+    lib.kvq_last_error.restype = ctypes.c_char_p
+    _lib_handle = lib
+    return lib
+
+
+def _check(status: int):
+    if status != KVQ_OK:
+        lib = load_library()
+        raise KVQError(status, lib.kvq_last_error().decode() or lib.kvq_status_string(status).decode())
+
+
+def make_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
+                v_policy=KVQ_V_CHUNK) -> kvq_config:
+    return kvq_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
+                      v_policy)
+
+
+def kvq_layout_bytes(cfg: kvq_config) -> kvq_layout:
+    out = kvq_layout()
+    _check(load_library().kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out
+
+
+def kvq_auto_splits(cfg: kvq_config, n_tokens: int) -> int:
+    return int(load_library().kvq_auto_splits(ctypes.byref(cfg), int(n_tokens)))
+
+
+def kvq_workspace_bytes(cfg: kvq_config, n_tokens: int, splits: int = 0) -> int:
+    return int(load_library().kvq_workspace_bytes(ctypes.byref(cfg), int(n_tokens), int(splits)))
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _f16_ptr(t: Optional[torch.Tensor], shape, name) -> int:
+    if t is None:
+        return 0
+    if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp16 CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+class KVCache:
+    """One layer's quantized KV cache in caller-owned (torch) device memory."""
+
+    _DT = {"k_codes": torch.int32, "k_scale": torch.float32, "k_zero": torch.int16,
+           "v_codes": torch.int32, "v_scale": torch.float32, "v_zero": torch.int16,
+           "k_resid": torch.float16, "v_resid": torch.float16}
+
+    def __init__(self, cfg: kvq_config, device="cuda"):
+        self.cfg = cfg
+        lay = kvq_layout_bytes(cfg)
+        B, H, d, cap, G, R = (cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.max_tokens,
+                              cfg.group, cfg.residual)
+        W = d * cfg.bits // 32
+        shapes = {"k_codes": (B, H, cap, W), "k_scale": (B, H, cap // G, d),
+                  "k_zero": (B, H, cap // G, d), "v_codes": (B, H, cap, W),
+                  "v_scale": (B, H, cap, d // G), "v_zero": (B, H, cap, d // G),
+                  "k_resid": (B, H, R, d), "v_resid": (B, H, R, d)}
+        self.tensors = {}
+        for name, shp in shapes.items():
+            t = torch.zeros(shp, dtype=self._DT[name], device=device)
+            assert t.numel() * t.element_size() == getattr(lay, name), name
+            self.tensors[name] = t
+        self.c = kvq_cache()
+        for name, t in self.tensors.items():
+            setattr(self.c, name, t.data_ptr())
+
+    # counters
+    @property
+    def n_tokens(self):
+        return self.c.n_tokens
+
+    @property
+    def nq_k(self):
+        return self.c.nq_k
+
+    @property
+    def nq_v(self):
+        return self.c.nq_v
+
+    @property
+    def flushes(self):
+        return self.c.flushes
+
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        kvq_quantize_prefill(self.cfg, self, k, v, stream)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        kvq_append_token(self.cfg, self, k_new, v_new, stream)
+
+    def workspace(self, n_tokens=None, splits=0) -> torch.Tensor:
+        n = self.cfg.max_tokens if n_tokens is None else n_tokens
+        nbytes = kvq_workspace_bytes(self.cfg, n, splits)
+        return torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=self.tensors["k_codes"].device)
+
+    def attention(self, q, softmax_scale=None, out=None, workspace=None, splits=0, stream=None):
+        cfg = self.cfg
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(cfg.head_dim)
+        if out is None:
+            out = torch.empty(cfg.batch, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(self.n_tokens, splits)
+        kvq_decode_attention(cfg, self, q, softmax_scale, out, workspace, splits, stream)
+        return out
+
+
+def kvq_quantize_prefill(cfg, cache: KVCache, k, v, stream=None):
+    L = 0 if k is None else int(k.shape[2])
+    shape = (cfg.batch, cfg.num_kv_heads, L, cfg.head_dim)
+    kp = _f16_ptr(k, shape, "k") if L else 0
+    vp = _f16_ptr(v, shape, "v") if L else 0
+    _check(load_library().kvq_quantize_prefill(ctypes.byref(cfg), ctypes.byref(cache.c), kp, vp, L,
+                                               _stream_ptr(stream)))
+
+
+def kvq_append_token(cfg, cache: KVCache, k_new, v_new, stream=None):
+    shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
+    _check(load_library().kvq_append_token(ctypes.byref(cfg), ctypes.byref(cache.c),
+                                           _f16_ptr(k_new, shape, "k_new"), _f16_ptr(v_new, shape, "v_new"),
+                                           _stream_ptr(stream)))
+
+
+def kvq_decode_attention(cfg, cache: KVCache, q, softmax_scale, out, workspace, splits=0, stream=None):
+    qp = _f16_ptr(q, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or \
+            tuple(out.shape) != (cfg.batch, cfg.num_q_heads, cfg.head_dim):
+        raise ValueError("out must be a contiguous fp32 CUDA tensor [batch][num_q_heads][head_dim]")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be device memory")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cache.c), qp,
+                                               float(softmax_scale), out.data_ptr(), workspace.data_ptr(),
+                                               nbytes, int(splits), _stream_ptr(stream)))

@@ -1,0 +1,288 @@
+// Host side of libkvq: argument validation, buffer layout, host counters and
+// stream-ordered kernel launches.  See include/kvq.h for the contract.
+//
+// Cache state machine (KIVI part of the juejin.cn page "大模型量化技术原理：
+// KIVI、IntactKV、KVQuant", how it works; pgsm.cn KV-cache quantization
+// article, 3.1): the key cache is split into a grouped part of nq_k tokens
+// (a multiple of G, here also of R) and an fp16 remainder of n - nq_k < R
+// tokens; a new key joins the remainder, and when the remainder holds R
+// tokens it is quantized, appended and emptied in the same call.  Values use
+// the same chunked rule, or a FIFO queue of the R most recent tokens.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvq_status check_config(const kvq_config *c) {
+  if (!c) return fail(KVQ_ERR_ARG, "config is null");
+  if (c->bits != 2 && c->bits != 4) return fail(KVQ_ERR_ARG, "bits must be 2 or 4 (got %d)", c->bits);
+  if (c->group <= 0) return fail(KVQ_ERR_ARG, "group must be positive");
+  if (c->residual <= 0 || c->residual % c->group)
+    return fail(KVQ_ERR_ARG, "residual (%d) must be a positive multiple of group (%d)", c->residual, c->group);
+  if (c->head_dim <= 0 || c->head_dim % c->group)
+    return fail(KVQ_ERR_ARG, "head_dim (%d) must be a multiple of group (%d)", c->head_dim, c->group);
+  if ((c->group * c->bits) % 32) return fail(KVQ_ERR_ARG, "group * bits must be a multiple of 32");
+  if (c->batch <= 0 || c->num_kv_heads <= 0 || c->num_q_heads <= 0)
+    return fail(KVQ_ERR_ARG, "batch and head counts must be positive");
+  if (c->num_q_heads % c->num_kv_heads) return fail(KVQ_ERR_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (c->max_tokens <= 0 || c->max_tokens % c->residual)
+    return fail(KVQ_ERR_ARG, "max_tokens (%d) must be a positive multiple of residual (%d)", c->max_tokens,
+                c->residual);
+  if (c->v_policy != KVQ_V_CHUNK && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "unknown v_policy");
+  if (c->head_dim != kvq::kHeadDim) return fail(KVQ_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
+  if (c->group != 32 && c->group != 64 && c->group != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "only group 32, 64 or 128 is implemented");
+  const int hpg = c->num_q_heads / c->num_kv_heads;
+  if (hpg != 1 && hpg != 2 && hpg != 4)
+    return fail(KVQ_ERR_UNSUPPORTED, "only 1, 2 or 4 query heads per kv head are implemented");
+  if (c->residual > 512) return fail(KVQ_ERR_UNSUPPORTED, "residual above 512 is not implemented");
+  if ((int64_t)c->batch * c->num_kv_heads > 65535) return fail(KVQ_ERR_UNSUPPORTED, "more than 65535 units");
+  if ((int64_t)c->batch * c->num_q_heads > 2147483647LL) return fail(KVQ_ERR_UNSUPPORTED, "too many query heads");
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache *k) {
+  if (!k) return fail(KVQ_ERR_ARG, "cache is null");
+  if (!k->k_codes || !k->k_scale || !k->k_zero || !k->v_codes || !k->v_scale || !k->v_zero || !k->k_resid ||
+      !k->v_resid)
+    return fail(KVQ_ERR_ARG, "a cache buffer pointer is null");
+  return KVQ_OK;
+}
+
+kvq::CacheView view_of(const kvq_config *c, const kvq_cache *k) {
+  kvq::CacheView v;
+  v.k_codes = k->k_codes;
+  v.k_scale = k->k_scale;
+  v.k_zero = k->k_zero;
+  v.v_codes = k->v_codes;
+  v.v_scale = k->v_scale;
+  v.v_zero = k->v_zero;
+  v.k_resid = k->k_resid;
+  v.v_resid = k->v_resid;
+  v.cap = c->max_tokens;
+  v.bits = c->bits;
+  v.group = c->group;
+  v.residual = c->residual;
+  return v;
+}
+
+kvq_status device_error(hipError_t e, const char *what) {
+  return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t main_tokens(const kvq_config *c, const kvq_cache *k) {
+  const int64_t m = k->nq_k < k->nq_v ? k->nq_k : k->nq_v;
+  return (m / c->group) * c->group;
+}
+
+int32_t auto_splits_for(const kvq_config *c, int64_t n_main) {
+  const int64_t units = (int64_t)c->batch * c->num_kv_heads;
+  const int64_t groups = n_main / c->group;
+  // aim for about four workgroups per compute unit of a 256-CU part, but keep
+  // at least eight key groups (two per wave) in every split
+  int64_t s = (1024 + units - 1) / units;
+  const int64_t by_work = groups / 8;
+  if (s > by_work) s = by_work;
+  if (s < 1) s = 1;
+  if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
+  return (int32_t)s;
+}
+
+size_t workspace_for(const kvq_config *c, int32_t splits) {
+  return (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if (!out) return fail(KVQ_ERR_ARG, "layout output is null");
+  const size_t units = (size_t)cfg->batch * cfg->num_kv_heads;
+  const size_t cap = (size_t)cfg->max_tokens;
+  const size_t d = (size_t)cfg->head_dim;
+  const size_t words = d * cfg->bits / 32;
+  const size_t G = (size_t)cfg->group;
+  out->k_codes = units * cap * words * 4;
+  out->k_scale = units * (cap / G) * d * 4;
+  out->k_zero = units * (cap / G) * d * 2;
+  out->v_codes = units * cap * words * 4;
+  out->v_scale = units * cap * (d / G) * 4;
+  out->v_zero = units * cap * (d / G) * 2;
+  out->k_resid = units * (size_t)cfg->residual * d * 2;
+  out->v_resid = out->k_resid;
+  g_err[0] = 0;
+  return KVQ_OK;
+}
+
+int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens) {
+  if (check_config(cfg) != KVQ_OK || n_tokens < 0) return 0;
+  // the split kernel covers the whole key groups of the quantized part; an
+  // upper bound of n_tokens keeps this a pure function of the length
+  const int64_t nq = n_tokens - (n_tokens % cfg->residual);
+  return auto_splits_for(cfg, nq);
+}
+
+size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t splits) {
+  if (check_config(cfg) != KVQ_OK || splits < 0 || splits > kvq::kMaxSplits) return 0;
+  if (splits == 0) splits = kvq_auto_splits(cfg, n_tokens);
+  return workspace_for(cfg, splits);
+}
+
+kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k, const uint16_t *v,
+                                int64_t len, hipStream_t stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if (cache->started) return fail(KVQ_ERR_STATE, "prefill on a cache that already holds tokens");
+  if (len < 0) return fail(KVQ_ERR_ARG, "negative length");
+  if (len > cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "len %lld exceeds max_tokens %d", (long long)len,
+                                         cfg->max_tokens);
+  if (len > 0 && (!k || !v)) return fail(KVQ_ERR_ARG, "k or v is null");
+  const int R = cfg->residual, G = cfg->group;
+  const int units = cfg->batch * cfg->num_kv_heads;
+  const int64_t nq_k = len - (len % R);
+  const int64_t nq_v = (cfg->v_policy == KVQ_V_CHUNK) ? nq_k : (len > R ? len - R : 0);
+  const kvq::CacheView cv = view_of(cfg, cache);
+  hipError_t e;
+  if (nq_k > 0) {
+    e = kvq::launch_quantize_keys(cv, units, k, len, 0, (int)(nq_k / G), 0, stream);
+    if (e != hipSuccess) return device_error(e, "quantize keys");
+  }
+  if (nq_v > 0) {
+    e = kvq::launch_quantize_values(cv, units, v, len, 0, (int)nq_v, 0, stream);
+    if (e != hipSuccess) return device_error(e, "quantize values");
+  }
+  if (len > nq_k) {
+    e = kvq::launch_copy_to_residual(cv, units, k, nullptr, len, nq_k, (int)(len - nq_k), (int)(nq_k % R), true,
+                                     false, stream);
+    if (e != hipSuccess) return device_error(e, "copy key residual");
+  }
+  if (len > nq_v) {
+    e = kvq::launch_copy_to_residual(cv, units, nullptr, v, len, nq_v, (int)(len - nq_v), (int)(nq_v % R), false,
+                                     true, stream);
+    if (e != hipSuccess) return device_error(e, "copy value residual");
+  }
+  cache->n_tokens = len;
+  cache->nq_k = nq_k;
+  cache->nq_v = nq_v;
+  cache->started = 1;
+  cache->flushes = 0;
+  g_err[0] = 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new,
+                            const uint16_t *v_new, hipStream_t stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if (!cache->started) return fail(KVQ_ERR_STATE, "append before prefill");
+  if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new or v_new is null");
+  if (cache->n_tokens >= cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "cache is full (%d tokens)", cfg->max_tokens);
+  const int R = cfg->residual, G = cfg->group;
+  const int units = cfg->batch * cfg->num_kv_heads;
+  const kvq::CacheView cv = view_of(cfg, cache);
+  int64_t n = cache->n_tokens, nq_k = cache->nq_k, nq_v = cache->nq_v;
+  int32_t flushes = cache->flushes;
+  hipError_t e;
+  // FIFO: the value queue would exceed R, so quantize its oldest entry before
+  // its ring slot (the same slot the new token takes) is overwritten
+  if (cfg->v_policy == KVQ_V_FIFO && (n + 1) - nq_v > R) {
+    e = kvq::launch_quantize_values(cv, units, cache->v_resid, R, nq_v % R, 1, nq_v, stream);
+    if (e != hipSuccess) return device_error(e, "quantize popped value");
+    nq_v += 1;
+  }
+  e = kvq::launch_copy_to_residual(cv, units, k_new, v_new, 1, 0, 1, (int)(n % R), true, true, stream);
+  if (e != hipSuccess) return device_error(e, "append to residual");
+  n += 1;
+  if (n - nq_k == R) {
+    // the key residual holds R tokens, slots 0..R-1 in token order
+    e = kvq::launch_quantize_keys(cv, units, cache->k_resid, R, 0, R / G, nq_k / G, stream);
+    if (e != hipSuccess) return device_error(e, "flush keys");
+    nq_k += R;
+    flushes += 1;
+  }
+  if (cfg->v_policy == KVQ_V_CHUNK && n - nq_v == R) {
+    e = kvq::launch_quantize_values(cv, units, cache->v_resid, R, 0, R, nq_v, stream);
+    if (e != hipSuccess) return device_error(e, "flush values");
+    nq_v += R;
+  }
+  cache->n_tokens = n;
+  cache->nq_k = nq_k;
+  cache->nq_v = nq_v;
+  cache->flushes = flushes;
+  g_err[0] = 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                int32_t splits, hipStream_t stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if (!cache->started) return fail(KVQ_ERR_STATE, "attention before prefill");
+  if (cache->n_tokens < 1) return fail(KVQ_ERR_STATE, "attention over an empty cache");
+  if (!q || !out || !workspace) return fail(KVQ_ERR_ARG, "q, out or workspace is null");
+  if (splits < 0 || splits > kvq::kMaxSplits) return fail(KVQ_ERR_ARG, "splits must be in [0, %d]", kvq::kMaxSplits);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_ARG, "softmax_scale must be finite");
+  const int64_t n_main = main_tokens(cfg, cache);
+  if (splits == 0) splits = auto_splits_for(cfg, n_main);
+  const size_t need = workspace_for(cfg, splits);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  kvq::AttnArgs a;
+  a.c = view_of(cfg, cache);
+  a.q = q;
+  a.out = out;
+  a.partials = static_cast<float *>(workspace);
+  a.batch = cfg->batch;
+  a.hq = cfg->num_q_heads;
+  a.hkv = cfg->num_kv_heads;
+  a.n = cache->n_tokens;
+  a.nq_k = cache->nq_k;
+  a.nq_v = cache->nq_v;
+  a.n_main = n_main;
+  a.splits = splits;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  hipError_t e = kvq::launch_decode_attention(a, stream);
+  if (e != hipSuccess) return device_error(e, "decode attention");
+  g_err[0] = 0;
+  return KVQ_OK;
+}
+
+const char *kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_CAPACITY: return "capacity exceeded";
+    case KVQ_ERR_STATE: return "invalid cache state";
+    case KVQ_ERR_DEVICE: return "device error";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char *kvq_last_error(void) { return g_err; }
+
+}  // extern "C"

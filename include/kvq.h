@@ -1,0 +1,172 @@
+/*
+ * kvq.h - C ABI of libkvq: KIVI-style 2/4-bit quantized KV cache and decode
+ * attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages, cited by title and section):
+ *   [KIVI] juejin.cn, "大模型量化技术原理：KIVI、IntactKV、KVQuant", KIVI part:
+ *          background (2-bit asymmetric, keys per channel, values per token),
+ *          工作原理 / how it works (grouped part X_Kg = X_K[:l-r] quantized in
+ *          groups of G tokens, full-precision remainder X_Kr, flush of X_Kr
+ *          once it holds R tokens with R % G == 0, value queue, prefill keeps
+ *          only the quantized cache).
+ *   [HFQ]  pgsm.cn news 20017, KV-cache quantization article: 2.1 affine map
+ *          X_Q = round(X / S) - Z, 2.2 keys per channel / values per token,
+ *          3.1 fp16 residual cache batch-quantized when full, 4.1 knobs
+ *          nbits, group_size, residual_length.
+ *
+ * Conventions
+ *   - fp16 tensors are passed as uint16_t bit patterns; every pointer named
+ *     "device" is HIP device memory owned by the caller.  The library never
+ *     allocates or frees device memory and keeps no global state other than a
+ *     thread-local error string.
+ *   - Every call is stream-ordered on the given hipStream_t and never
+ *     synchronizes the device.  The host-side counters in kvq_cache are
+ *     updated at enqueue time, so calls on one cache must be serialized by
+ *     the caller (one host thread, one stream).
+ *   - A call that fails validation returns a non-zero status, enqueues
+ *     nothing and leaves kvq_cache unchanged; kvq_last_error() explains why.
+ *     A failed kernel launch returns KVQ_ERR_DEVICE; counters are then
+ *     undefined and the cache must be rebuilt.
+ *   - Only head_dim == 128, bits in {2, 4}, G in {32, 64, 128} and a query to
+ *     key head ratio in {1, 2, 4} are implemented; other valid shapes return
+ *     KVQ_ERR_UNSUPPORTED.
+ *
+ * Device layout of one layer's cache (U = batch * num_kv_heads units, unit
+ * u = b * num_kv_heads + h; cap = max_tokens; W = head_dim * bits / 32):
+ *   k_codes u32 [U][cap][W]        token-major rows; channel c's code sits at
+ *                                  bits [(c*bits) % 32, +bits) of word
+ *                                  (c*bits) / 32 of the token's row
+ *   k_scale f32 [U][cap/G][head_dim]  per (group of G tokens, channel)
+ *   k_zero  i16 [U][cap/G][head_dim]
+ *   v_codes u32 [U][cap][W]        same row format as keys
+ *   v_scale f32 [U][cap][head_dim/G]  per (token, group of G channels)
+ *   v_zero  i16 [U][cap][head_dim/G]
+ *   k_resid, v_resid f16 [U][R][head_dim]  fp16 residual ring, token t in
+ *                                  slot t mod R
+ *   Dequantized value of a code: S * (code + Z) (inverse of [HFQ] 2.1).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = 1,          /* invalid argument or null pointer */
+  KVQ_ERR_CAPACITY = 2,     /* the call would exceed max_tokens / workspace */
+  KVQ_ERR_STATE = 3,        /* prefill on a started cache, append/attend before prefill */
+  KVQ_ERR_DEVICE = 4,       /* a HIP launch failed */
+  KVQ_ERR_UNSUPPORTED = 5   /* valid but not implemented shape */
+} kvq_status;
+
+/* Value-residual policy.  KVQ_V_CHUNK: values flushed as a block of R tokens
+ * together with the keys ([HFQ] 3.1).  KVQ_V_FIFO: values kept as a queue of
+ * the R most recent tokens; once a push makes it exceed R, the oldest value is
+ * quantized and appended ([KIVI] how it works, value queue). */
+typedef enum { KVQ_V_CHUNK = 0, KVQ_V_FIFO = 1 } kvq_v_policy;
+
+/* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
+ * plus the attention shape.  Constraints: bits in {2,4}; residual > 0 and
+ * residual % group == 0 ([KIVI] how it works); head_dim % group == 0;
+ * group * bits % 32 == 0; num_q_heads % num_kv_heads == 0;
+ * max_tokens > 0 and max_tokens % residual == 0. */
+typedef struct {
+  int32_t bits;
+  int32_t group;        /* G */
+  int32_t residual;     /* R */
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_tokens;   /* capacity per unit, prompt plus generated tokens */
+  int32_t v_policy;     /* kvq_v_policy */
+} kvq_config;
+
+/* Byte sizes of the eight caller-allocated device buffers of one cache. */
+typedef struct {
+  size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid;
+} kvq_layout;
+
+/* One layer's cache: caller-owned device buffers (sized by kvq_layout_bytes)
+ * and host counters.  Zero-initialize the struct, set the pointers, and leave
+ * the counters to the library.  n_tokens = tokens cached; nq_k / nq_v = tokens
+ * in the quantized key / value part; started = prefill has run. */
+typedef struct {
+  uint32_t *k_codes;
+  float *k_scale;
+  int16_t *k_zero;
+  uint32_t *v_codes;
+  float *v_scale;
+  int16_t *v_zero;
+  uint16_t *k_resid;
+  uint16_t *v_resid;
+  int64_t n_tokens;
+  int64_t nq_k;
+  int64_t nq_v;
+  int32_t started;
+  int32_t flushes;      /* key-residual flushes performed since prefill */
+} kvq_cache;
+
+/* Validates cfg and fills *out with the buffer sizes.  Host only. */
+kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out);
+
+/* Split count kvq_decode_attention uses for a cache of n_tokens tokens when
+ * it is passed splits == 0.  Host only; returns 0 on an invalid cfg. */
+int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens);
+
+/* Workspace bytes kvq_decode_attention needs for `splits` splits (0 = the
+ * automatic count for n_tokens): partial (max, sum, acc[head_dim]) records,
+ * fp32, for every query head and split.  Host only; 0 on an invalid cfg. */
+size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t splits);
+
+/* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
+ * device [batch][num_kv_heads][len][head_dim], read only (the full-precision
+ * tensors stay valid for the caller, as the page's prefill paragraph
+ * requires).  The first len - (len mod R) tokens are quantized, keys per
+ * channel over groups of G tokens and values per token over groups of G
+ * channels; the last len mod R tokens go to the residual ring.  With
+ * KVQ_V_FIFO the last min(len, R) values stay fp16 instead.  Needs a cache
+ * with started == 0 and len <= max_tokens; len == 0 is allowed. */
+kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache,
+                                const uint16_t *k, const uint16_t *v, int64_t len,
+                                hipStream_t stream);
+
+/* One decode step's new key and value, fp16 device [batch][num_kv_heads]
+ * [head_dim], written to residual slot n mod R; n += 1.  When the key
+ * residual reaches R tokens it is quantized and appended to the grouped part
+ * in the same call (eager flush, [KIVI] how it works; [HFQ] 3.1); values
+ * follow the cache's kvq_v_policy.  Needs started and n < max_tokens. */
+kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
+                            const uint16_t *k_new, const uint16_t *v_new,
+                            hipStream_t stream);
+
+/* Decode attention of one query per head over the whole cache, including the
+ * token appended in the same step: out = softmax(softmax_scale * q K^T) V
+ * with K, V dequantized inside the kernels (fused dequantization into the
+ * q.K^T and P.V products).  q fp16 device [batch][num_q_heads][head_dim];
+ * out fp32 device [batch][num_q_heads][head_dim]; query head h uses key head
+ * h / (num_q_heads / num_kv_heads).  workspace: device, at least
+ * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, no initialization needed.
+ * splits: 0 = automatic, else 1..64.  Needs started and n_tokens >= 1. */
+kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
+                                const uint16_t *q, float softmax_scale, float *out,
+                                void *workspace, size_t workspace_bytes, int32_t splits,
+                                hipStream_t stream);
+
+/* Static description of a status code. */
+const char *kvq_status_string(kvq_status s);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

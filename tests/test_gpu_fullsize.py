@@ -1,0 +1,56 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench
+times (automatic split count): sampled units are checked bit-exact against the
+oracle run on just those units, and their query heads' outputs within 2e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_token_amd as kvq
+import oracle
+from workloads import GQA_LONG, LLAMA7B_2BIT, LLAMA7B_4BIT, LONG_4BIT, gen_new_tokens, gen_prefill, gen_queries
+from gpu_helpers import ATOL, compare_unit_buffers, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_units(w, k=6, seed=0):
+    U = w.units
+    rng = np.random.default_rng(seed + w.config_id)
+    picks = {0, U - 1} | set(int(x) for x in rng.integers(0, U, size=k))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("w", [LLAMA7B_2BIT, LLAMA7B_4BIT, GQA_LONG, LONG_4BIT], ids=lambda w: w.name)
+def test_fullsize_sampled_parity(w):
+    print(f"workload {w.name}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda", steps=1)
+    q = gen_queries(w, 0, "cuda", steps=1)[0].contiguous()
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, w.max_tokens, w.v_policy)
+    cache = kvq.KVCache(cfg, "cuda")
+    cache.prefill(k, v)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out = cache.attention(q, scale)
+    torch.cuda.synchronize()
+    hpg = w.num_q_heads // w.num_kv_heads
+    worst = 0.0
+    for u in _sample_units(w):
+        b, h = divmod(u, w.num_kv_heads)
+        ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+        ref.prefill(host(k[b:b + 1, h:h + 1]), host(v[b:b + 1, h:h + 1]))
+        ref.append(host(kn[0][b:b + 1, h:h + 1]), host(vn[0][b:b + 1, h:h + 1]))
+        compare_unit_buffers(cache, ref, b, h, 0, 0)
+        K, V = ref.dequantized()
+        qh = host(q[b:b + 1, h * hpg:(h + 1) * hpg])
+        want = oracle.attention(qh, K, V, scale)
+        got = host(out[b:b + 1, h * hpg:(h + 1) * hpg]).astype(np.float64)
+        err = float(np.abs(got - want).max())
+        worst = max(worst, err)
+        assert err <= ATOL, (u, err)
+    print(f"  sampled units ok, worst attention err {worst:.2e}", flush=True)
+    del k, v, cache
+    torch.cuda.empty_cache()
