@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -145,14 +147,15 @@ def main():
     ws = caches[0].workspace(max_tokens, args.splits)
     scale = 1.0 / math.sqrt(w.head_dim)
     stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
 
     def step(i, count_bytes):
         nb = 0
         for layer in range(layers):
             c = caches[layer]
             kn, vn = news[layer]
-            c.append(kn[i], vn[i])
-            c.attention(qs[layer][i], scale, outs[layer], ws, args.splits)
+            c.append(kn[i], vn[i], sp)
+            c.attention(qs[layer][i], scale, outs[layer], ws, args.splits, sp)
             if count_bytes:
                 nb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
         return nb
@@ -179,7 +182,7 @@ def main():
     for _ in range(args.reps):
         for layer in range(layers):
             c = caches[layer]
-            c.attention(qs[layer][last], scale, outs[layer], ws, args.splits)
+            c.attention(qs[layer][last], scale, outs[layer], ws, args.splits, sp)
             calls += 1
             cb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
     ev1.record(stream)
@@ -187,6 +190,14 @@ def main():
     call_us = ev0.elapsed_time(ev1) * 1e3 / calls
     call_bytes = cb / calls
     achieved = call_bytes / (call_us * 1e-6) / 1e9
+
+    if args.copy_probe:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     splits_used = args.splits or kvq.kvq_auto_splits(cfg, caches[0].n_tokens)
     res = {
@@ -210,7 +221,7 @@ def main():
                    "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode attention call (split + merge)", "avg_call_us": round(call_us, 2),
+                     "kernel": "decode_attn_kernel (one launch per call)", "avg_call_us": round(call_us, 2),
                      "bytes_per_call": int(call_bytes)},
     }
     if not args.no_cpu:

@@ -116,6 +116,8 @@ def kvq_workspace_bytes(cfg: kvq_config, n_tokens: int, splits: int = 0) -> int:
 def _stream_ptr(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
     return int(stream.cuda_stream)
 
 
@@ -124,7 +126,7 @@ def _f16_ptr(t: Optional[torch.Tensor], shape, name) -> int:
         return 0
     if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous fp16 CUDA tensor")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
 
@@ -154,6 +156,11 @@ class KVCache:
         self.c = kvq_cache()
         for name, t in self.tensors.items():
             setattr(self.c, name, t.data_ptr())
+        # per-call marshalling state, built once
+        self._cfg_ref = ctypes.byref(cfg)
+        self._c_ref = ctypes.byref(self.c)
+        self._q_shape = torch.Size((cfg.batch, cfg.num_q_heads, cfg.head_dim))
+        self._kv_shape = torch.Size((cfg.batch, cfg.num_kv_heads, cfg.head_dim))
 
     # counters
     @property
@@ -205,20 +212,21 @@ def kvq_quantize_prefill(cfg, cache: KVCache, k, v, stream=None):
 
 
 def kvq_append_token(cfg, cache: KVCache, k_new, v_new, stream=None):
-    shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
-    _check(load_library().kvq_append_token(ctypes.byref(cfg), ctypes.byref(cache.c),
-                                           _f16_ptr(k_new, shape, "k_new"), _f16_ptr(v_new, shape, "v_new"),
-                                           _stream_ptr(stream)))
+    if cfg is not cache.cfg:
+        raise ValueError("cfg must be the cache's own config")
+    shape = cache._kv_shape
+    _check(_lib_handle.kvq_append_token(cache._cfg_ref, cache._c_ref, _f16_ptr(k_new, shape, "k_new"),
+                                        _f16_ptr(v_new, shape, "v_new"), _stream_ptr(stream)))
 
 
 def kvq_decode_attention(cfg, cache: KVCache, q, softmax_scale, out, workspace, splits=0, stream=None):
-    qp = _f16_ptr(q, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
-    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or \
-            tuple(out.shape) != (cfg.batch, cfg.num_q_heads, cfg.head_dim):
+    if cfg is not cache.cfg:
+        raise ValueError("cfg must be the cache's own config")
+    qp = _f16_ptr(q, cache._q_shape, "q")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.shape != cache._q_shape:
         raise ValueError("out must be a contiguous fp32 CUDA tensor [batch][num_q_heads][head_dim]")
     if not workspace.is_cuda:
         raise ValueError("workspace must be device memory")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(load_library().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cache.c), qp,
-                                               float(softmax_scale), out.data_ptr(), workspace.data_ptr(),
-                                               nbytes, int(splits), _stream_ptr(stream)))
+    _check(_lib_handle.kvq_decode_attention(cache._cfg_ref, cache._c_ref, qp, softmax_scale, out.data_ptr(),
+                                            workspace.data_ptr(), nbytes, splits, _stream_ptr(stream)))

@@ -95,16 +95,18 @@ int64_t main_tokens(const kvq_config *c, const kvq_cache *k) {
 int32_t auto_splits_for(const kvq_config *c, int64_t n_main) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
   const int64_t groups = n_main / c->group;
-  // aim for about four workgroups per compute unit of a 256-CU part, but keep
-  // at least eight key groups (two per wave) in every split
-  int64_t s = (1024 + units - 1) / units;
-  const int64_t by_work = groups / 8;
+  // aim for two 8-wave workgroups per compute unit of a 256-CU part, but
+  // keep at least sixteen key groups (two per wave) in every split
+  int64_t s = (512 + units - 1) / units;
+  const int64_t by_work = groups / 16;
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;
   if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
   return (int32_t)s;
 }
 
+// Workspace: fp32 partial (acc[128], max, sum) records, (splits + 1) per
+// query head.
 size_t workspace_for(const kvq_config *c, int32_t splits) {
   return (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
 }
@@ -263,7 +265,14 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, c
   a.nq_k = cache->nq_k;
   a.nq_v = cache->nq_v;
   a.n_main = n_main;
-  a.splits = splits;
+  // tokens [n_main, n): all fp16 (chunked residual) -> the last split takes
+  // them; keys quantized but values fp16 (FIFO queue) -> a tail workgroup
+  const bool has_rest = cache->n_tokens > n_main;
+  const bool all_fp16 = cache->nq_k == n_main && cache->nq_v == n_main;
+  a.resid_main = (has_rest && all_fp16) ? 1 : 0;
+  a.tail_wg = (has_rest && !all_fp16) ? 1 : 0;
+  a.splits = n_main > 0 ? splits : a.resid_main;
+  a.nparts = a.splits + a.tail_wg;
   a.qscale = softmax_scale * 1.4426950408889634f;
   hipError_t e = kvq::launch_decode_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");

@@ -47,11 +47,14 @@ struct AttnArgs {
   CacheView c;
   const uint16_t *q;     // [B][Hq][128]
   float *out;            // [B][Hq][128]
-  float *partials;       // [B][Hq][splits + 1][kPartialStride]
+  float *partials;       // [B][Hq][nparts][kPartialStride]
   int batch, hq, hkv;
   int64_t n, nq_k, nq_v;
-  int64_t n_main;        // tokens [0, n_main) handled by the split kernel (multiple of G)
-  int splits;
+  int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups
+  int splits;            // workgroups per unit over [0, n_main) (>= 1 when resid_main)
+  int tail_wg;           // 1: an extra workgroup per unit runs the mixed tail [n_main, n)
+  int resid_main;        // 1: [n_main, n) is all-fp16 and the last split takes it
+  int nparts;            // splits + tail_wg; 1 means the kernel writes out directly
   float qscale;          // softmax_scale * log2(e)
 };
 

@@ -121,8 +121,10 @@ kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out);
 int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens);
 
 /* Workspace bytes kvq_decode_attention needs for `splits` splits (0 = the
- * automatic count for n_tokens): partial (max, sum, acc[head_dim]) records,
- * fp32, for every query head and split.  Host only; 0 on an invalid cfg. */
+ * automatic count for n_tokens; more tokens never need fewer splits, so the
+ * size for max_tokens covers every call): fp32 partial (acc[head_dim], max,
+ * sum) records for every query head and part.  Host only; 0 on an invalid
+ * cfg. */
 size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t splits);
 
 /* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
@@ -152,8 +154,10 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
  * q.K^T and P.V products).  q fp16 device [batch][num_q_heads][head_dim];
  * out fp32 device [batch][num_q_heads][head_dim]; query head h uses key head
  * h / (num_q_heads / num_kv_heads).  workspace: device, at least
- * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, no initialization needed.
- * splits: 0 = automatic, else 1..64.  Needs started and n_tokens >= 1. */
+ * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, no initialization needed;
+ * calls that share a workspace must be ordered on one stream.  splits: 0 =
+ * automatic, else 1..64.  One kernel launch when every unit fits one part,
+ * else a second (merge) launch.  Needs started and n_tokens >= 1. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                 const uint16_t *q, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, int32_t splits,
