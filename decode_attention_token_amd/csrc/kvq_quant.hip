@@ -129,14 +129,23 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   }
 }
 
-// Copies fp16 rows into the residual rings: 16 bytes per thread.
-__global__ __launch_bounds__(256) void copy_rows_kernel(uint16_t *__restrict__ ring, int ring_rows,
-                                                        const uint16_t *__restrict__ src, int64_t src_rows,
+// Copies fp16 rows into the residual rings, 16 bytes per thread; the second
+// half of the grid (when both are given) copies the value rows.
+__global__ __launch_bounds__(256) void copy_rows_kernel(uint16_t *__restrict__ kring, uint16_t *__restrict__ vring,
+                                                        int ring_rows, const uint16_t *__restrict__ ksrc,
+                                                        const uint16_t *__restrict__ vsrc, int64_t src_rows,
                                                         int64_t row0, int count, int slot0, int units) {
   constexpr int CHUNKS = kHeadDim * 2 / 16;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)units * count * CHUNKS;
-  if (idx >= total) return;
+  uint16_t *ring = kring;
+  const uint16_t *src = ksrc;
+  if (ring == nullptr || idx >= total) {
+    if (ring != nullptr) idx -= total;
+    ring = vring;
+    src = vsrc;
+  }
+  if (ring == nullptr || idx >= total) return;
   const int ch = (int)(idx % CHUNKS);
   const int64_t r = idx / CHUNKS;
   const int i = (int)(r % count);
@@ -178,14 +187,11 @@ hipError_t launch_copy_to_residual(const CacheView &c, int units, const uint16_t
                                    int64_t src_rows, int64_t row0, int count, int slot0, bool keys, bool values,
                                    hipStream_t s) {
   if (count <= 0 || units <= 0) return hipSuccess;
-  const int64_t total = (int64_t)units * count * (kHeadDim * 2 / 16);
+  if (!keys && !values) return hipSuccess;
+  const int64_t total = (int64_t)units * count * (kHeadDim * 2 / 16) * ((keys && values) ? 2 : 1);
   const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (keys)
-    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, c.k_resid, c.residual, ksrc, src_rows,
-                       row0, count, slot0, units);
-  if (values)
-    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, c.v_resid, c.residual, vsrc, src_rows,
-                       row0, count, slot0, units);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, keys ? c.k_resid : nullptr,
+                     values ? c.v_resid : nullptr, c.residual, ksrc, vsrc, src_rows, row0, count, slot0, units);
   return hipGetLastError();
 }
 
