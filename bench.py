@@ -1,8 +1,8 @@
 """Decode-attention benchmark on one MI355X.
 
 A step is one decode step of the whole batch through every layer of the
-workload: per layer, kvq_append_token (residual write, eager flush when due)
-then kvq_decode_attention (split kernel + merge).  Caches are prefilled before
+workload: per layer, kvq_decode_step = kvq_append_token (residual write, eager
+flush when due) + kvq_decode_attention, one kernel launch when no flush is due.  Caches are prefilled before
 timing; inputs for every step are resident in HBM when timing starts.
 
 Prints one JSON line:
@@ -190,8 +190,7 @@ def main():
         for layer in range(layers):
             c = caches[layer]
             kn, vn = news[layer]
-            c.append(kn[i], vn[i], sp)
-            c.attention(qs[layer][i], scale, outs[layer], ws, args.splits, sp)
+            c.step(kn[i], vn[i], qs[layer][i], scale, outs[layer], ws, args.splits, sp)
             if count_bytes:
                 nb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
         return nb

@@ -22,7 +22,7 @@ KVQ_V_CHUNK, KVQ_V_FIFO = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
-    "kvq_append_token", "kvq_decode_attention", "kvq_status_string", "kvq_last_error",
+    "kvq_append_token", "kvq_decode_attention", "kvq_decode_step", "kvq_status_string", "kvq_last_error",
 ]
 
 
@@ -79,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_float, vp, vp,
                                          ctypes.c_size_t, ctypes.c_int32, vp]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_decode_step.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, vp, ctypes.c_float, vp, vp,
+                                    ctypes.c_size_t, ctypes.c_int32, vp]
+    lib.kvq_decode_step.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_last_error.argtypes = []
@@ -190,6 +193,18 @@ class KVCache:
         nbytes = kvq_workspace_bytes(self.cfg, n, splits)
         return torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=self.tensors["k_codes"].device)
 
+    def step(self, k_new, v_new, q, softmax_scale=None, out=None, workspace=None, splits=0, stream=None):
+        """Append one token and attend (one launch when no flush is due)."""
+        cfg = self.cfg
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(cfg.head_dim)
+        if out is None:
+            out = torch.empty(cfg.batch, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(self.n_tokens + 1, splits)
+        kvq_decode_step(cfg, self, k_new, v_new, q, softmax_scale, out, workspace, splits, stream)
+        return out
+
     def attention(self, q, softmax_scale=None, out=None, workspace=None, splits=0, stream=None):
         cfg = self.cfg
         if softmax_scale is None:
@@ -230,3 +245,19 @@ def kvq_decode_attention(cfg, cache: KVCache, q, softmax_scale, out, workspace, 
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib_handle.kvq_decode_attention(cache._cfg_ref, cache._c_ref, qp, softmax_scale, out.data_ptr(),
                                             workspace.data_ptr(), nbytes, splits, _stream_ptr(stream)))
+
+
+def kvq_decode_step(cfg, cache: KVCache, k_new, v_new, q, softmax_scale, out, workspace, splits=0, stream=None):
+    if cfg is not cache.cfg:
+        raise ValueError("cfg must be the cache's own config")
+    kv = cache._kv_shape
+    qp = _f16_ptr(q, cache._q_shape, "q")
+    kp = _f16_ptr(k_new, kv, "k_new")
+    vp = _f16_ptr(v_new, kv, "v_new")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.shape != cache._q_shape:
+        raise ValueError("out must be a contiguous fp32 CUDA tensor [batch][num_q_heads][head_dim]")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be device memory")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib_handle.kvq_decode_step(cache._cfg_ref, cache._c_ref, kp, vp, qp, softmax_scale, out.data_ptr(),
+                                       workspace.data_ptr(), nbytes, splits, _stream_ptr(stream)))

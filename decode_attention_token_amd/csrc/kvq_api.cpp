@@ -237,18 +237,29 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
   return KVQ_OK;
 }
 
-kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
-                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-                                int32_t splits, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status check_attention_args(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q, float *out,
+                                void *workspace, int32_t splits, float softmax_scale) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
   if ((s = check_cache(cache)) != KVQ_OK) return s;
   if (!cache->started) return fail(KVQ_ERR_STATE, "attention before prefill");
-  if (cache->n_tokens < 1) return fail(KVQ_ERR_STATE, "attention over an empty cache");
   if (!q || !out || !workspace) return fail(KVQ_ERR_ARG, "q, out or workspace is null");
   if (splits < 0 || splits > kvq::kMaxSplits) return fail(KVQ_ERR_ARG, "splits must be in [0, %d]", kvq::kMaxSplits);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_ARG, "softmax_scale must be finite");
-  const int64_t n_main = main_tokens(cfg, cache);
+  return KVQ_OK;
+}
+
+// Enqueues attention over a cache of n_tokens tokens; with k_new/v_new the
+// last token is taken from them and stored into its residual slot.
+kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64_t n_tokens, const uint16_t *k_new,
+                            const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
+                            void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream) {
+  const int64_t m = cache->nq_k < cache->nq_v ? cache->nq_k : cache->nq_v;
+  const int64_t n_main = (m / cfg->group) * cfg->group;
   if (splits == 0) splits = auto_splits_for(cfg, n_main);
   const size_t need = workspace_for(cfg, splits);
   if (workspace_bytes < need)
@@ -261,21 +272,65 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, c
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;
-  a.n = cache->n_tokens;
+  a.n = n_tokens;
   a.nq_k = cache->nq_k;
   a.nq_v = cache->nq_v;
   a.n_main = n_main;
   // tokens [n_main, n): all fp16 (chunked residual) -> the last split takes
   // them; keys quantized but values fp16 (FIFO queue) -> a tail workgroup
-  const bool has_rest = cache->n_tokens > n_main;
+  const bool has_rest = n_tokens > n_main;
   const bool all_fp16 = cache->nq_k == n_main && cache->nq_v == n_main;
   a.resid_main = (has_rest && all_fp16) ? 1 : 0;
   a.tail_wg = (has_rest && !all_fp16) ? 1 : 0;
   a.splits = n_main > 0 ? splits : a.resid_main;
   a.nparts = a.splits + a.tail_wg;
   a.qscale = softmax_scale * 1.4426950408889634f;
+  a.k_new = k_new;
+  a.v_new = v_new;
   hipError_t e = kvq::launch_decode_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                int32_t splits, hipStream_t stream) {
+  kvq_status s = check_attention_args(cfg, cache, q, out, workspace, splits, softmax_scale);
+  if (s != KVQ_OK) return s;
+  if (cache->n_tokens < 1) return fail(KVQ_ERR_STATE, "attention over an empty cache");
+  s = launch_attention(cfg, cache, cache->n_tokens, nullptr, nullptr, q, softmax_scale, out, workspace,
+                       workspace_bytes, splits, stream);
+  if (s == KVQ_OK) g_err[0] = 0;
+  return s;
+}
+
+kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new, const uint16_t *v_new,
+                           const uint16_t *q, float softmax_scale, float *out, void *workspace,
+                           size_t workspace_bytes, int32_t splits, hipStream_t stream) {
+  kvq_status s = check_attention_args(cfg, cache, q, out, workspace, splits, softmax_scale);
+  if (s != KVQ_OK) return s;
+  if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new or v_new is null");
+  if (cache->n_tokens >= cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "cache is full (%d tokens)", cfg->max_tokens);
+  const int R = cfg->residual;
+  const int64_t n1 = cache->n_tokens + 1;
+  // one launch when the append needs no flush or queue pop and the residual
+  // is the chunked all-fp16 kind; otherwise the two calls in sequence
+  const bool fused = cfg->v_policy == KVQ_V_CHUNK && cache->nq_k == cache->nq_v && n1 - cache->nq_k < R;
+  if (!fused) {
+    const size_t need = workspace_for(cfg, splits == 0 ? kvq_auto_splits(cfg, n1) : splits);
+    if (workspace_bytes < need)
+      return fail(KVQ_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+    s = kvq_append_token(cfg, cache, k_new, v_new, stream);
+    if (s != KVQ_OK) return s;
+    return kvq_decode_attention(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
+  }
+  s = launch_attention(cfg, cache, n1, k_new, v_new, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
+  if (s != KVQ_OK) return s;
+  cache->n_tokens = n1;
   g_err[0] = 0;
   return KVQ_OK;
 }

@@ -573,15 +573,27 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) qf[h][i] = h2f(qp[i]) * a.qscale;
     }
+    if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
+      // fused step: store the new token into its ring slot
+      constexpr int CH = kHeadDim * 2 / 16;
+      const int which = tid / CH, ch = tid % CH;
+      const uint4 *src = reinterpret_cast<const uint4 *>((which ? a.v_new : a.k_new) + (int64_t)unit * kHeadDim);
+      uint4 *dst = reinterpret_cast<uint4 *>((which ? a.c.v_resid : a.c.k_resid) +
+                                             ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
+      dst[ch] = src[ch];
+    }
     for (int rs = wave; rs < rsteps; rs += kWaves) {
       const int64_t t = a.n_main + (int64_t)rs * TPS + tl;
       const bool valid = t < a.n;
       const int slot = (int)((valid ? t : a.n_main) % R);
+      const bool fresh = a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
+      const uint16_t *krow = fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + (int64_t)slot * kHeadDim;
+      const uint16_t *vrow = fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + (int64_t)slot * kHeadDim;
       float kf[CPL], vf[CPL];
 #pragma unroll
       for (int i = 0; i < CPL; i += 8) {
-        const uint4 kk = *reinterpret_cast<const uint4 *>(kr + (int64_t)slot * kHeadDim + i);
-        const uint4 vv = *reinterpret_cast<const uint4 *>(vr + (int64_t)slot * kHeadDim + i);
+        const uint4 kk = *reinterpret_cast<const uint4 *>(krow + i);
+        const uint4 vv = *reinterpret_cast<const uint4 *>(vrow + i);
         const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
         const uint32_t vw4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll

@@ -56,6 +56,11 @@ struct AttnArgs {
   int resid_main;        // 1: [n_main, n) is all-fp16 and the last split takes it
   int nparts;            // splits + tail_wg; 1 means the kernel writes out directly
   float qscale;          // softmax_scale * log2(e)
+  // Fused decode step: token n - 1 is read from k_new / v_new ([B*Hkv][128])
+  // instead of the residual ring, and the last split writes it into its ring
+  // slot.  Null when the token was appended beforehand.
+  const uint16_t *k_new;
+  const uint16_t *v_new;
 };
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s);

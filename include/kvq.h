@@ -163,6 +163,17 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                 void *workspace, size_t workspace_bytes, int32_t splits,
                                 hipStream_t stream);
 
+/* One decode step: kvq_append_token(k_new, v_new) followed by
+ * kvq_decode_attention(q) with the same results, but as a single kernel
+ * launch whenever the append needs no flush and the cache uses the chunked
+ * value residual: the attention kernel reads the new token from k_new/v_new
+ * and stores it into its residual slot.  Otherwise it runs the two calls in
+ * sequence.  Arguments and requirements are those of the two calls; on a
+ * validation failure nothing is enqueued and the cache is unchanged. */
+kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new,
+                           const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
+                           void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *kvq_status_string(kvq_status s);
 

@@ -124,6 +124,15 @@ def test_state_and_argument_errors_leave_counters_unchanged(lib):
     assert lib.kvq_decode_attention(P(c), P(s1), 1, 0.1, 1, 1, 1 << 30, 65, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_attention(P(c), P(s1), 1, float("inf"), 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_attention(P(c), P(s1), 1, 0.1, 1, 1, 16, 0, None) == kvq.KVQ_ERR_CAPACITY
+    # fused step: same checks as append + attention, nothing changes on failure
+    st = _fake_cache(started=1, n=100)
+    before = _snapshot(st)
+    assert lib.kvq_decode_step(P(c), P(st), None, 1, 1, 0.1, 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_step(P(c), P(st), 1, 1, None, 0.1, 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_step(P(c), P(st), 1, 1, 1, 0.1, 1, 1, 16, 0, None) == kvq.KVQ_ERR_CAPACITY
+    assert lib.kvq_decode_step(P(c), P(_fake_cache(1, 4224)), 1, 1, 1, 0.1, 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_CAPACITY
+    assert lib.kvq_decode_step(P(c), P(_fake_cache(0, 0)), 1, 1, 1, 0.1, 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_STATE
+    assert _snapshot(st) == before
     s0 = _fake_cache(started=1, n=0)
     assert lib.kvq_decode_attention(P(c), P(s0), 1, 0.1, 1, 1, 1 << 30, 0, None) == kvq.KVQ_ERR_STATE
     assert lib.kvq_status_string(kvq.KVQ_ERR_CAPACITY) == b"capacity exceeded"

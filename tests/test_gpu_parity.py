@@ -146,3 +146,34 @@ def test_prefill_leaves_inputs_untouched():
     cache.prefill(k, v)
     torch.cuda.synchronize()
     assert torch.equal(k, k0) and torch.equal(v, v0)
+
+
+@pytest.mark.parametrize("policy", [CHUNK, FIFO])
+def test_decode_step_matches_append_then_attention(policy):
+    """kvq_decode_step (fused when no flush is due) gives the same cache bytes
+    and bit-identical outputs as kvq_append_token + kvq_decode_attention, and
+    stays within the oracle tolerance across flushes."""
+    w = _w(130 + policy, 2, 4, 2, 190, 2, 32, 64, 80, policy)
+    print(f"case {w.name}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    cfg_a, fused = make_cache(2, 32, 64, 2, 4, 2, w.max_tokens, policy)
+    cfg_b, plain = make_cache(2, 32, 64, 2, 4, 2, w.max_tokens, policy)
+    ref = oracle.QuantizedKVCache(2, 32, 64, 2, 2, 128, policy)
+    fused.prefill(k, v)
+    plain.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    ws_a, ws_b = fused.workspace(), plain.workspace()
+    for i in range(w.steps):
+        q = qs[i].contiguous()
+        oa = fused.step(kn[i].contiguous(), vn[i].contiguous(), q, workspace=ws_a)
+        plain.append(kn[i].contiguous(), vn[i].contiguous())
+        ob = plain.attention(q, workspace=ws_b)
+        ref.append(host(kn[i]), host(vn[i]))
+        assert (fused.n_tokens, fused.nq_k, fused.nq_v) == (ref.n, ref.nq_k, ref.nq_v)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {i}"
+        if i % 16 == 15 or i == w.steps - 1:
+            assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
+    compare_all_buffers(fused, ref)
