@@ -203,7 +203,8 @@ struct Geo {
   static constexpr int SPG = GS / TPS;                   // wave steps per key group
   static constexpr int RS = kHeadDim + 4;                // padded reduction row (floats)
   static constexpr int RED = kWaves * TPS * RS + kParts * kHeadDim;
-  static constexpr int QP = kWaves * HPG * kHeadDim;
+  static constexpr int QPW = HPG * (kHeadDim + 8);                // per wave: q'[HPG][128], beta[HPG][8]
+  static constexpr int QP = kWaves * QPW;
   static constexpr int TAIL = HPG * kMaxTail + kParts * HPG * kHeadDim;
   static constexpr int WORK = RED > QP ? (RED > TAIL ? RED : TAIL) : (QP > TAIL ? QP : TAIL);
   static constexpr int RES = HPG * kHeadDim + 2 * HPG + 2 * kWaves * HPG;
@@ -358,8 +359,14 @@ struct StepBuf {
   uint32_t kz;       // their int16 zero-points
 };
 
+// Occupancy target: four waves per SIMD (at most 128 VGPRs) for the MHA
+// tilings, two for the grouped-query tiling that keeps 4 heads in registers.
+template <int HPG>
+constexpr int kWavesPerEU = HPG == 1 ? 4 : 2;
+
 template <int BITS, int GS, int HPG, int LPT>
-__global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
+void decode_attn_kernel(AttnArgs a) {
   using Gm = Geo<BITS, GS, HPG, LPT>;
   constexpr int CPL = Gm::CPL, TPS = Gm::TPS, PER = Gm::PER, WPL = Gm::WPL, W = Gm::W;
   constexpr int NVG = Gm::NVG, VGR = Gm::VGR, SPG = Gm::SPG;
@@ -398,18 +405,23 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
   const int wg1 = g0 + (g1 - g0) * (wave + 1) / kWaves;
   const int nsteps = (wg1 - wg0) * SPG;
 
-  // query (log2 units) for channels 2*lane, 2*lane+1, used to fold key scales
+  // query (log2 units, divided by the unpack scale) for channels 2*lane,
+  // 2*lane+1, used to fold key scales
   float qa[HPG], qb[HPG];
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
     const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * HPG + h)) * kHeadDim + 2 * lane;
-    qa[h] = h2f(qp[0]) * a.qscale;
-    qb[h] = h2f(qp[1]) * a.qscale;
+    qa[h] = h2f(qp[0]) * (a.qscale * INV_U);
+    qb[h] = h2f(qp[1]) * (a.qscale * INV_U);
   }
 
-  float *lds_qp = smem + wave * (HPG * kHeadDim);
+  // per-wave folded-query buffer: q'[h][128] then the slice biases beta[h][LPT]
+  float *lds_qp = smem + wave * Gm::QPW;
+  float *lds_beta = lds_qp + HPG * kHeadDim;
+  constexpr int FOLD = CPL / 2;   // fold lanes (two channels each) per lane slice
+  static_assert(FOLD <= 16 && (FOLD & (FOLD - 1)) == 0, "slice bias must reduce within a DPP row");
   float qf[HPG][CPL];
-  float beta[HPG];
+  float beta[HPG];   // zero-point bias of this lane's channel slice for the current key group
   float m[HPG], mthr[HPG], lsum[HPG], acc[HPG][CPL], bias[HPG][NVG];
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
@@ -478,14 +490,17 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
 
   auto process = [&](const Buf &bf, int s) {
     if (s % SPG == 0) {
-      // new key group: fold its per-channel scales into the query
+      // new key group: fold its per-channel scales into the query; each block
+      // of FOLD lanes holds one lane slice's channels and sums its share of
+      // the zero-point bias
       const float z0 = (float)(int16_t)(bf.kz & 0xffffu);
       const float z1 = (float)(int16_t)(bf.kz >> 16);
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
-        const float p0 = qa[h] * bf.ks.x, p1 = qb[h] * bf.ks.y;
-        beta[h] = wave_sum(fmaf(p0, z0, p1 * z1));
-        *reinterpret_cast<float2 *>(lds_qp + h * kHeadDim + 2 * lane) = make_float2(p0 * INV_U, p1 * INV_U);
+        const float p0 = qa[h] * bf.ks.x, p1 = qb[h] * bf.ks.y;   // q'/U
+        const float part = block_sum<FOLD>(fmaf(p0, z0, p1 * z1));
+        *reinterpret_cast<float2 *>(lds_qp + h * kHeadDim + 2 * lane) = make_float2(p0, p1);
+        if (lane % FOLD == 0) lds_beta[h * 8 + lane / FOLD] = part * U;
       }
       wave_sync();
 #pragma unroll
@@ -498,6 +513,7 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
           qf[h][i + 2] = v.z;
           qf[h][i + 3] = v.w;
         }
+        beta[h] = lds_beta[h * 8 + j];
       }
       wave_sync();
     }
@@ -520,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(AttnArgs a) {
     }
     float p[HPG];
 #pragma unroll
-    for (int h = 0; h < HPG; ++h) p[h] = soft(h, block_sum<LPT>(sc[h] + d1[h]) + beta[h]);
+    for (int h = 0; h < HPG; ++h) p[h] = soft(h, block_sum<LPT>((sc[h] + d1[h]) + beta[h]));
     // values
     float vz[NVG];
     vz[0] = (float)(int16_t)(bf.vz & 0xffffu);
