@@ -142,6 +142,67 @@ def cpu_baseline(w, sample, budget_s=12.0):
             "seconds_per_call_extrapolated": round(t_total / done * w.units, 3)}
 
 
+def prefill_bytes(w, L):
+    """Bytes a prefill of L tokens must move: fp16 K and V in, codes +
+    metadata + fp16 residual out."""
+    d, b, G, R = w.head_dim, w.bits, w.group, w.residual
+    nq = L - L % R
+    out = nq * d * b // 8 * 2 + (nq // G) * d * 6 + nq * (d // G) * 6 + (L - nq) * d * 2 * 2
+    return w.units * (L * d * 2 * 2 + out)
+
+
+def flush_bytes(w):
+    """Bytes one residual flush must move: R fp16 keys and values in, their
+    codes and metadata out (the append's own token write included)."""
+    d, b, G, R = w.head_dim, w.bits, w.group, w.residual
+    return w.units * (R * d * 2 * 2 + R * d * b // 8 * 2 + (R // G) * d * 6 + R * (d // G) * 6 + d * 2 * 2)
+
+
+def time_prefill_and_flush(w, dev, stream, reps=5):
+    """HIP-event timing of one prefill (layer-0 prompt) and of one append that
+    flushes the residual, on a scratch cache of the same shape."""
+    L = w.context
+    k, v = gen_prefill(w, 0, dev)
+    cap = ((L + 2 * w.residual) // w.residual) * w.residual
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, cap, w.v_policy)
+    c = kvq.KVCache(cfg, dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps + 1):
+        c.c.started, c.c.n_tokens, c.c.nq_k, c.c.nq_v = 0, 0, 0, 0
+        e0.record(stream)
+        c.prefill(k, v, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    pre_us = sorted(times[1:])[len(times[1:]) // 2]
+    # bring the residual to R - 1 tokens, then time the append that flushes
+    kn, vn = gen_new_tokens(w, 0, dev, steps=w.residual)
+    need = (w.residual - 1) - (c.n_tokens - c.nq_k)
+    for i in range(need):
+        c.append(kn[i], vn[i], stream.cuda_stream)
+    state = (c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes)
+    times = []
+    for _ in range(reps + 1):
+        c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes = state
+        e0.record(stream)
+        c.append(kn[-1], vn[-1], stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert c.flushes == state[3] + 1
+        times.append(e0.elapsed_time(e1) * 1e3)
+    fl_us = sorted(times[1:])[len(times[1:]) // 2]
+    pb, fb = prefill_bytes(w, L), flush_bytes(w)
+    del k, v, c
+    torch.cuda.empty_cache()
+    return {"prefill": {"us": round(pre_us, 1), "bytes": pb, "GB/s": round(pb / pre_us / 1e3, 1),
+                        "frac": round(pb / pre_us / 1e3 / HBM_PEAK_GBS, 4), "tokens": L},
+            "flush": {"us": round(fl_us, 2), "bytes": fb, "GB/s": round(fb / fl_us / 1e3, 1),
+                      "frac": round(fb / fl_us / 1e3 / HBM_PEAK_GBS, 4),
+                      "per_appended_token_us": round(fl_us / w.residual, 3)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +214,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
+    ap.add_argument("--no-side", action="store_true", help="skip the prefill and flush timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -226,6 +288,8 @@ def main():
     call_bytes = cb / calls
     achieved = call_bytes / (call_us * 1e-6) / 1e9
 
+    side = time_prefill_and_flush(w, dev, stream) if not args.no_side else None
+
     if args.copy_probe:
         # a plain elementwise kernel of known traffic: reads and writes 256 MiB
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -260,6 +324,8 @@ def main():
                      "kernel": "decode_attn_kernel (one launch per call)", "avg_call_us": round(call_us, 2),
                      "bytes_per_call": int(call_bytes)},
     }
+    if side is not None:
+        res.update(side)
     if not args.no_cpu:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         del caches, news, qs

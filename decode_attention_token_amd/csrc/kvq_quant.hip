@@ -22,6 +22,7 @@ __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_
 
 struct GroupParams {
   float s, z;
+  float r;   // RN(1 / s), for the fast quotient
 };
 
 // Scale and zero-point of one group from its minimum and maximum: S spreads
@@ -35,7 +36,7 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, float qm
   } else {
     s = (mn != 0.0f) ? fabsf(mn) : 1.0f;
   }
-  return {s, rintf(mn / s)};
+  return {s, rintf(mn / s), 1.0f / s};
 }
 
 __device__ __forceinline__ uint32_t code_of(float x, GroupParams p, float qmax) {
@@ -44,54 +45,115 @@ __device__ __forceinline__ uint32_t code_of(float x, GroupParams p, float qmax) 
   return static_cast<uint32_t>(q);
 }
 
-// One workgroup of 128 threads quantizes one key group (G tokens x 128
-// channels) of one unit.  Thread c reduces channel c over the G tokens; then
-// the threads pack token rows word by word from the shared parameters.
-template <int BITS>
-__global__ __launch_bounds__(128) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
+// Codes of N values of one group.  rint(x / s) with x / s correctly rounded
+// equals rint(x * r), r = RN(1/s), unless the quotient lies within 2^-21 |x/s|
+// of a half-integer (x * r is that close to the correctly rounded quotient).
+// The fast products are checked for that; if any lane of the wave meets such
+// a value, the whole chunk is redone with IEEE divisions (a rare, uniform
+// branch), so the codes stay exactly those of the correctly rounded map.
+template <int N>
+__device__ __forceinline__ void codes_of(const float *x, GroupParams p, float qmax, uint32_t *code) {
+  bool near = false;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float y = x[k] * p.r;
+    const float mid = floorf(y) + 0.5f;
+    near |= fabsf(y - mid) <= fmaxf(fabsf(y), 1.0f) * 0x1p-20f;
+    code[k] = static_cast<uint32_t>(fminf(fmaxf(rintf(y) - p.z, 0.0f), qmax));
+  }
+  if (__any(near)) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) code[k] = code_of(x[k], p, qmax);
+  }
+}
+
+// Unpacks 8 fp16 values (one 16-byte load) to fp32.
+__device__ __forceinline__ void load8(const uint16_t *p, float *x) {
+  const uint4 v = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f((uint16_t)(w[i] & 0xffffu));
+    x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+  }
+}
+
+// One workgroup of 256 threads quantizes one key group (GS tokens x 128
+// channels) of one unit.  Thread (pair, part) owns channels 2*pair, 2*pair+1
+// and a quarter of the group's tokens, held in registers: it reduces min/max
+// over its quarter (the quarters combine in LDS), codes its values into an LDS
+// byte tile, and the tile is packed into token rows word by word with
+// coalesced stores.
+template <int BITS, int GS>
+__global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
                                                             int64_t src_rows, int64_t src_row0,
                                                             int64_t dst_group0) {
   constexpr int PER = 32 / BITS;              // codes per word
   constexpr int W = kHeadDim / PER;           // words per token row
+  constexpr int TQ = GS / 4;                  // tokens per thread
   constexpr float QMAX = float((1 << BITS) - 1);
-  const int G = c.group;
   const int g = blockIdx.x;
   const int unit = blockIdx.y;
   const int tid = threadIdx.x;
-  __shared__ float s_s[kHeadDim];
-  __shared__ float s_z[kHeadDim];
+  const int pair = tid & 63, part = tid >> 6;
+  const int ch = 2 * pair;
+  __shared__ float s_mn[4][kHeadDim], s_mx[4][kHeadDim];
+  __shared__ uint8_t s_code[GS][kHeadDim];
 
-  const uint16_t *rows = src + ((int64_t)unit * src_rows + src_row0 + (int64_t)g * G) * kHeadDim;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int t = 0; t < G; ++t) {
-    const float x = h2f(rows[(int64_t)t * kHeadDim + tid]);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+  const uint16_t *rows = src + ((int64_t)unit * src_rows + src_row0 + (int64_t)g * GS + part * TQ) * kHeadDim + ch;
+  float xa[TQ], xb[TQ];
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(rows + (int64_t)t * kHeadDim);
+    xa[t] = h2f((uint16_t)(w & 0xffffu));
+    xb[t] = h2f((uint16_t)(w >> 16));
   }
-  const GroupParams p = group_params(mn, mx, QMAX);
-  const int64_t gidx = (int64_t)unit * (c.cap / G) + dst_group0 + g;
-  c.k_scale[gidx * kHeadDim + tid] = p.s;
-  c.k_zero[gidx * kHeadDim + tid] = static_cast<int16_t>(p.z);
-  s_s[tid] = p.s;
-  s_z[tid] = p.z;
+  float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < TQ; ++t) {
+    mn0 = fminf(mn0, xa[t]);
+    mx0 = fmaxf(mx0, xa[t]);
+    mn1 = fminf(mn1, xb[t]);
+    mx1 = fmaxf(mx1, xb[t]);
+  }
+  s_mn[part][ch] = mn0;
+  s_mn[part][ch + 1] = mn1;
+  s_mx[part][ch] = mx0;
+  s_mx[part][ch + 1] = mx1;
   __syncthreads();
-
-  uint32_t *dst = c.k_codes + ((int64_t)unit * c.cap + (dst_group0 + g) * (int64_t)G) * W;
-  for (int i = tid; i < G * W; i += blockDim.x) {
-    const int t = i / W;
-    const int w = i % W;
-    const uint16_t *r = rows + (int64_t)t * kHeadDim + w * PER;
+  mn0 = fminf(fminf(s_mn[0][ch], s_mn[1][ch]), fminf(s_mn[2][ch], s_mn[3][ch]));
+  mx0 = fmaxf(fmaxf(s_mx[0][ch], s_mx[1][ch]), fmaxf(s_mx[2][ch], s_mx[3][ch]));
+  mn1 = fminf(fminf(s_mn[0][ch + 1], s_mn[1][ch + 1]), fminf(s_mn[2][ch + 1], s_mn[3][ch + 1]));
+  mx1 = fmaxf(fmaxf(s_mx[0][ch + 1], s_mx[1][ch + 1]), fmaxf(s_mx[2][ch + 1], s_mx[3][ch + 1]));
+  const GroupParams p0 = group_params(mn0, mx0, QMAX);
+  const GroupParams p1 = group_params(mn1, mx1, QMAX);
+  if (part == 0) {
+    const int64_t gidx = ((int64_t)unit * (c.cap / GS) + dst_group0 + g) * kHeadDim + ch;
+    *reinterpret_cast<float2 *>(c.k_scale + gidx) = make_float2(p0.s, p1.s);
+    *reinterpret_cast<uint32_t *>(c.k_zero + gidx) =
+        (uint32_t)(uint16_t)(int16_t)p0.z | ((uint32_t)(uint16_t)(int16_t)p1.z << 16);
+  }
+  uint32_t ca[TQ], cb[TQ];
+  codes_of<TQ>(xa, p0, QMAX, ca);
+  codes_of<TQ>(xb, p1, QMAX, cb);
+#pragma unroll
+  for (int t = 0; t < TQ; ++t)
+    *reinterpret_cast<uint16_t *>(&s_code[part * TQ + t][ch]) = (uint16_t)(ca[t] | (cb[t] << 8));
+  __syncthreads();
+  uint32_t *dst = c.k_codes + ((int64_t)unit * c.cap + (dst_group0 + g) * (int64_t)GS) * W;
+  for (int i = tid; i < GS * W; i += blockDim.x) {
+    const int t = i / W, w = i % W;
+    const uint8_t *b = &s_code[t][w * PER];
     uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int ch = w * PER + k;
-      word |= code_of(h2f(r[k]), GroupParams{s_s[ch], s_z[ch]}, QMAX) << (k * BITS);
-    }
+    for (int k = 0; k < PER; ++k) word |= (uint32_t)b[k] << (k * BITS);
     dst[i] = word;
   }
 }
 
-// One thread quantizes one value group: G channels of one token row.
+// One thread quantizes one value group (G channels of one token row) in
+// chunks of 32 channels held in registers: a min/max pass, then a coding
+// pass over the same 16-byte loads (served by the cache).
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const uint16_t *__restrict__ src,
                                                               int64_t src_rows, int64_t src_row0, int count,
@@ -111,21 +173,40 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
 
   const uint16_t *x = src + ((int64_t)unit * src_rows + src_row0 + i) * kHeadDim + j * G;
   float mn = INFINITY, mx = -INFINITY;
-  for (int k = 0; k < G; ++k) {
-    const float v = h2f(x[k]);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+  for (int k0 = 0; k0 < G; k0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      mn = fminf(mn, v[k]);
+      mx = fmaxf(mx, v[k]);
+    }
   }
   const GroupParams p = group_params(mn, mx, QMAX);
   const int64_t row = (int64_t)unit * c.cap + dst_row0 + i;
   c.v_scale[row * NG + j] = p.s;
   c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
   uint32_t *dst = c.v_codes + row * W + j * (G / PER);
-  for (int w = 0; w < G / PER; ++w) {
-    uint32_t word = 0;
+  for (int k0 = 0; k0 < G; k0 += 32) {
+    float v[32];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) word |= code_of(h2f(x[w * PER + k]), p, QMAX) << (k * BITS);
-    dst[w] = word;
+    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+    uint32_t cd[32];
+    codes_of<32>(v, p, QMAX, cd);
+    uint32_t words[32 / PER];
+#pragma unroll
+    for (int w = 0; w < 32 / PER; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) word |= cd[w * PER + k] << (k * BITS);
+      words[w] = word;
+    }
+    if constexpr (BITS == 2) {
+      *reinterpret_cast<uint2 *>(dst + k0 / PER) = make_uint2(words[0], words[1]);
+    } else {
+      *reinterpret_cast<uint4 *>(dst + k0 / PER) = make_uint4(words[0], words[1], words[2], words[3]);
+    }
   }
 }
 
@@ -162,10 +243,19 @@ hipError_t launch_quantize_keys(const CacheView &c, int units, const uint16_t *s
                                 int64_t src_row0, int ngroups, int64_t dst_group0, hipStream_t s) {
   if (ngroups <= 0 || units <= 0) return hipSuccess;
   dim3 grid(ngroups, units);
-  if (c.bits == 2)
-    hipLaunchKernelGGL(quantize_keys_kernel<2>, grid, dim3(128), 0, s, c, src, src_rows, src_row0, dst_group0);
-  else
-    hipLaunchKernelGGL(quantize_keys_kernel<4>, grid, dim3(128), 0, s, c, src, src_rows, src_row0, dst_group0);
+#define KVQ_QK(B, G)                                                                                     \
+  hipLaunchKernelGGL((quantize_keys_kernel<B, G>), grid, dim3(256), 0, s, c, src, src_rows, src_row0, \
+                     dst_group0)
+  if (c.bits == 2) {
+    if (c.group == 32) KVQ_QK(2, 32);
+    else if (c.group == 64) KVQ_QK(2, 64);
+    else KVQ_QK(2, 128);
+  } else {
+    if (c.group == 32) KVQ_QK(4, 32);
+    else if (c.group == 64) KVQ_QK(4, 64);
+    else KVQ_QK(4, 128);
+  }
+#undef KVQ_QK
   return hipGetLastError();
 }
 
