@@ -38,6 +38,26 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
   byte accounting        pinned: the per-token byte table for Llama-2-7B
                          (524,288 / 262,144 / 131,072 / 65,536 bytes) and the
                          ~5 GB for 10k fp16 tokens in [HFQ] 1 and 3.2.
+  hybrid_is_symmetric    pinned: agrees with |mean| < 0.1 * std computed by
+                         numpy away from the threshold; zero-centred groups
+                         choose symmetric, offset groups asymmetric.
+  quantize_groups_symmetric / _hybrid
+                         pinned: on-grid exactness (x = s*k recovers S = s and
+                         the signed codes), |x - x_hat| <= S/2, asymmetric
+                         groups equal quantize_groups.
+  InnerQCache            pinned: sinks stay exact fp16, window holds
+                         min(R, n - sinks) tokens, prefill(L)+appends ==
+                         prefill(L+m), all-fp16 cache reduces to plain
+                         attention.
+
+Sources for the InnerQ-style variant:
+  [InnerQ] euno.news, "【论文】InnerQ：硬件感知免调优KV缓存量化用于大语言模型",
+           methodology 1 (groups along the inner / hidden dimension), 2 (per
+           group statistics min, max, mean, variance; symmetric quantization
+           when the group is centred on zero, asymmetric otherwise, one
+           shared scale per group), 4 (recent and attention-sink tokens kept
+           in fp16).
+  [HFQ] 2.1 defines symmetric quantization as a range symmetric about zero.
 """
 from __future__ import annotations
 
@@ -46,7 +66,8 @@ import numpy as np
 __all__ = [
     "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
     "attention", "kv_code_bytes_per_token", "attention_call_bytes", "flush_bytes",
-    "CHUNK", "FIFO",
+    "CHUNK", "FIFO", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
+    "InnerQCache", "innerq_attention_call_bytes",
 ]
 
 CHUNK = 0   # value residual flushed as a block of R tokens, like the keys ([HFQ] 3.1)
@@ -315,6 +336,204 @@ class QuantizedKVCache:
         ks = [(self.nq_k + i) % R for i in range(self.kr.shape[2])]
         vs = [(self.nq_v + i) % R for i in range(self.vr.shape[2])]
         return ks, vs
+
+
+# --------------------------------------------------------------------------- InnerQ-style
+def hybrid_is_symmetric(x):
+    """Per-group mode choice: symmetric when the group is centred on zero.
+
+    [InnerQ] methodology 2 picks symmetric quantization for zero-centred
+    groups from the group statistics.  Reading: centred means
+    |mean| < 0.1 * std with the population standard deviation, which is
+    exactly 101 * s1^2 < n * s2 for s1 = sum x, s2 = sum x^2.  Both sums run
+    in index order in float64, so any implementation taking the same steps
+    makes the same choice.  x: float16 [..., n]  ->  bool [...].
+    """
+    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    n = xf.shape[-1]
+    s1 = np.zeros(xf.shape[:-1], np.float64)
+    s2 = np.zeros(xf.shape[:-1], np.float64)
+    for i in range(n):
+        s1 = s1 + xf[..., i]
+        s2 = s2 + xf[..., i] * xf[..., i]
+    return 101.0 * (s1 * s1) < float(n) * s2
+
+
+def quantize_groups_symmetric(x, bits: int):
+    """Symmetric quantization about zero ([HFQ] 2.1): S = max|x| / (2^(b-1) - 1),
+    signed code k = clamp(rint(x / S), -(2^(b-1) - 1), 2^(b-1) - 1).
+
+    Storage: the code is kept offset-binary, u = k + 2^(b-1), and the group's
+    zero-point is recorded as Z = -2^(b-1), so S * (u + Z) = S * k and the
+    same dequantization serves both modes.  An all-zero group takes S = 1.
+    Returns (u uint8, S float32, Z int16).
+    """
+    xf = np.asarray(x, dtype=np.float16).astype(_F32)
+    half = 1 << (bits - 1)
+    qm = _F32(half - 1)
+    amax = np.abs(xf).max(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s_sym = (amax / qm).astype(_F32)
+    scale = np.where(amax > 0, s_sym, _F32(1.0)).astype(_F32)
+    k = np.clip(np.rint((xf / scale[..., None]).astype(_F32)), -qm, qm)
+    u = (k + _F32(half)).astype(np.uint8)
+    zero = np.full(scale.shape, -half, np.int16)
+    return u, scale, zero
+
+
+def quantize_groups_hybrid(x, bits: int):
+    """[InnerQ] methodology 2: per group, symmetric when centred on zero
+    (hybrid_is_symmetric), else the asymmetric map of quantize_groups."""
+    sym = hybrid_is_symmetric(x)
+    ca, sa, za = quantize_groups(x, bits)
+    cs, ss, zs = quantize_groups_symmetric(x, bits)
+    codes = np.where(sym[..., None], cs, ca).astype(np.uint8)
+    return codes, np.where(sym, ss, sa).astype(_F32), np.where(sym, zs, za).astype(np.int16)
+
+
+class InnerQCache:
+    """InnerQ-style cache: keys and values both grouped along the hidden
+    dimension (per token, groups of G channels, [InnerQ] methodology 1) with
+    the hybrid per-group mode; the first `sinks` tokens and the most recent
+    `window` tokens stay fp16 ([InnerQ] methodology 4).
+
+    Token t < sinks is a sink.  Later tokens enter a FIFO window; once a push
+    makes the window exceed `window` tokens, the oldest one is quantized and
+    appended to the quantized part [sinks, nq).
+    """
+
+    def __init__(self, bits, group, window, sinks, batch, kv_heads, head_dim):
+        if head_dim % group:
+            raise ValueError("head_dim must be a multiple of G")
+        if window <= 0 or sinks < 0:
+            raise ValueError("window must be positive and sinks non-negative")
+        self.bits, self.G, self.R, self.S = bits, group, window, sinks
+        self.B, self.H, self.d = batch, kv_heads, head_dim
+        B, H, d, G = batch, kv_heads, head_dim, group
+        self.sink_k = np.zeros((B, H, 0, d), np.float16)
+        self.sink_v = np.zeros((B, H, 0, d), np.float16)
+        self.qk = np.zeros((B, H, 0, d), np.uint8)
+        self.qk_s = np.zeros((B, H, 0, d // G), _F32)
+        self.qk_z = np.zeros((B, H, 0, d // G), np.int16)
+        self.qv = np.zeros((B, H, 0, d), np.uint8)
+        self.qv_s = np.zeros((B, H, 0, d // G), _F32)
+        self.qv_z = np.zeros((B, H, 0, d // G), np.int16)
+        self.rk = np.zeros((B, H, 0, d), np.float16)
+        self.rv = np.zeros((B, H, 0, d), np.float16)
+        self.n = 0
+        self.started = False
+
+    @property
+    def nq(self):
+        """End of the quantized part: tokens [sinks, nq) are quantized."""
+        return self.n if self.n <= self.S else self.S + self.qk.shape[2]
+
+    def _quantize_rows(self, rows):
+        B, H, m, d = rows.shape
+        G = self.G
+        c, s, z = quantize_groups_hybrid(rows.reshape(B, H, m, d // G, G), self.bits)
+        return c.reshape(B, H, m, d), s, z
+
+    def _push_quantized(self, k, v):
+        c, s, z = self._quantize_rows(k)
+        self.qk = np.concatenate([self.qk, c], axis=2)
+        self.qk_s = np.concatenate([self.qk_s, s], axis=2)
+        self.qk_z = np.concatenate([self.qk_z, z], axis=2)
+        c, s, z = self._quantize_rows(v)
+        self.qv = np.concatenate([self.qv, c], axis=2)
+        self.qv_s = np.concatenate([self.qv_s, s], axis=2)
+        self.qv_z = np.concatenate([self.qv_z, z], axis=2)
+
+    def prefill(self, k, v):
+        if self.started:
+            raise RuntimeError("prefill on a non-empty cache")
+        k = np.asarray(k, np.float16)
+        v = np.asarray(v, np.float16)
+        L = k.shape[2]
+        ns = min(L, self.S)
+        self.sink_k, self.sink_v = k[:, :, :ns].copy(), v[:, :, :ns].copy()
+        if L > self.S:
+            r = min(self.R, L - self.S)
+            self._push_quantized(k[:, :, self.S:L - r], v[:, :, self.S:L - r])
+            self.rk, self.rv = k[:, :, L - r:].copy(), v[:, :, L - r:].copy()
+        self.n = L
+        self.started = True
+
+    def append(self, k_new, v_new):
+        if not self.started:
+            raise RuntimeError("append before prefill")
+        k_new = np.asarray(k_new, np.float16)[:, :, None, :]
+        v_new = np.asarray(v_new, np.float16)[:, :, None, :]
+        if self.n < self.S:
+            self.sink_k = np.concatenate([self.sink_k, k_new], axis=2)
+            self.sink_v = np.concatenate([self.sink_v, v_new], axis=2)
+        else:
+            self.rk = np.concatenate([self.rk, k_new], axis=2)
+            self.rv = np.concatenate([self.rv, v_new], axis=2)
+            if self.rk.shape[2] > self.R:          # pop the oldest and quantize it
+                self._push_quantized(self.rk[:, :, :1], self.rv[:, :, :1])
+                self.rk, self.rv = self.rk[:, :, 1:], self.rv[:, :, 1:]
+        self.n += 1
+
+    def dequantized(self):
+        B, H, d, G = self.B, self.H, self.d, self.G
+        m = self.qk.shape[2]
+        kh = dequantize(self.qk.reshape(B, H, m, d // G, G), self.qk_s, self.qk_z).reshape(B, H, m, d)
+        vh = dequantize(self.qv.reshape(B, H, m, d // G, G), self.qv_s, self.qv_z).reshape(B, H, m, d)
+        K = np.concatenate([self.sink_k.astype(_F32), kh, self.rk.astype(_F32)], axis=2)
+        V = np.concatenate([self.sink_v.astype(_F32), vh, self.rv.astype(_F32)], axis=2)
+        return K, V
+
+    def buffers(self, max_tokens):
+        """Device layout: quantized token t (sinks <= t < nq) at row t of
+        k_codes/v_codes u32 [B,H,cap,d*b/32] and of k_scale/k_zero/v_scale/
+        v_zero [B,H,cap,d/G]; window token t at ring slot t mod R of
+        k_resid/v_resid f16 [B,H,R,d]; sink t at row t of k_sink/v_sink f16
+        [B,H,sinks,d]."""
+        B, H, d, G, R, b, S = self.B, self.H, self.d, self.G, self.R, self.bits, self.S
+        cap = max_tokens
+        W = d * b // 32
+        out = {
+            "k_codes": np.zeros((B, H, cap, W), np.uint32),
+            "k_scale": np.zeros((B, H, cap, d // G), _F32),
+            "k_zero": np.zeros((B, H, cap, d // G), np.int16),
+            "v_codes": np.zeros((B, H, cap, W), np.uint32),
+            "v_scale": np.zeros((B, H, cap, d // G), _F32),
+            "v_zero": np.zeros((B, H, cap, d // G), np.int16),
+            "k_resid": np.zeros((B, H, R, d), np.float16),
+            "v_resid": np.zeros((B, H, R, d), np.float16),
+            "k_sink": np.zeros((B, H, S, d), np.float16),
+            "v_sink": np.zeros((B, H, S, d), np.float16),
+        }
+        m = self.qk.shape[2]
+        rows = slice(S, S + m)
+        out["k_codes"][:, :, rows] = pack_rows(self.qk, b)
+        out["v_codes"][:, :, rows] = pack_rows(self.qv, b)
+        out["k_scale"][:, :, rows], out["k_zero"][:, :, rows] = self.qk_s, self.qk_z
+        out["v_scale"][:, :, rows], out["v_zero"][:, :, rows] = self.qv_s, self.qv_z
+        ns = self.sink_k.shape[2]
+        out["k_sink"][:, :, :ns], out["v_sink"][:, :, :ns] = self.sink_k, self.sink_v
+        nq = self.nq
+        for i in range(self.rk.shape[2]):
+            out["k_resid"][:, :, (nq + i) % R] = self.rk[:, :, i]
+            out["v_resid"][:, :, (nq + i) % R] = self.rv[:, :, i]
+        return out
+
+    def live_resid_slots(self):
+        nq = self.nq
+        slots = [(nq + i) % self.R for i in range(self.rk.shape[2])]
+        return slots, slots
+
+
+def innerq_attention_call_bytes(batch, q_heads, kv_heads, head_dim, bits, group, n, nq, sinks):
+    """Algorithmic bytes of one decode-attention call over an InnerQ-style
+    cache: per quantized token, key and value codes plus one fp32 scale and
+    int16 zero per group each; fp16 sinks and window; fp16 q, fp32 out."""
+    d, b, G = head_dim, bits, group
+    m = max(0, nq - sinks) if n > sinks else 0
+    fp16_tokens = n - m
+    per_unit = m * 2 * (d * b // 8 + (d // G) * 6) + fp16_tokens * d * 2 * 2
+    return batch * kv_heads * per_unit + batch * q_heads * d * (2 + 4)
 
 
 # --------------------------------------------------------------------------- attention
