@@ -38,16 +38,24 @@ METRIC = "decode-attn effective KV GB/s (% HBM peak) + tokens/s, Llama-2-7B shap
 
 def attn_bytes(w, n, nq_k, nq_v):
     """Algorithmic bytes of one decode-attention call (codes, fp32 scale + int16
-    zero per group, fp16 residual, fp16 q, fp32 out)."""
+    zero per group, fp16 residual / sinks / window, fp16 q, fp32 out)."""
     d, b, G = w.head_dim, w.bits, w.group
-    per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6 + nq_v * d * b // 8 + nq_v * (d // G) * 6
-                + ((n - nq_k) + (n - nq_v)) * d * 2)
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        m = nq_k - min(n, w.sinks)   # quantized tokens
+        per_unit = m * 2 * (d * b // 8 + (d // G) * 6) + (n - m) * d * 2 * 2
+    else:
+        per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6 + nq_v * d * b // 8 + nq_v * (d // G) * 6
+                    + ((n - nq_k) + (n - nq_v)) * d * 2)
     return w.batch * w.num_kv_heads * per_unit + w.batch * w.num_q_heads * d * 6
 
 
+def make_cfg(w, max_tokens):
+    return kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks)
+
+
 def build_caches(w, layers, max_tokens, dev):
-    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim, max_tokens, w.v_policy)
+    cfg = make_cfg(w, max_tokens)
     caches = []
     for layer in range(layers):
         k, v = gen_prefill(w, layer, dev)
@@ -64,29 +72,35 @@ def sample_units(w, count=512, seed=7):
     return [int(u) for u in np.random.default_rng(seed).permutation(w.units)[:count]]
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_llama2_7b_2bit_traffic.txt")
+# decode kernel, its source files and its committed counter summary per scheme
+KERNELS = {
+    0: ("decode_attn_kernel", ("kvq_attn.hip", "kvq_attn_common.h", "kvq_internal.h"),
+        "decode_attn_llama2_7b_2bit_traffic.txt"),
+    1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_internal.h"),
+        "innerq_attn_b4_h32_L131072_4bit_traffic.txt"),
+}
 
 
-def kernel_source_digest():
+def kernel_source_digest(scheme=0):
     import hashlib
     h = hashlib.sha256()
-    for name in ("kvq_attn.hip", "kvq_internal.h"):
+    for name in KERNELS[scheme][1]:
         with open(os.path.join(ROOT, "decode_attention_token_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
+def measured_traffic(w):
     """HBM bytes per launch of the decode kernel from the committed counter
     summary, or None when it is missing, for another workload, or taken on a
     different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", KERNELS[w.scheme][2])) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("kernel_source_digest") != kernel_source_digest() or kv.get("workload") != workload_name:
+    if kv.get("kernel_source_digest") != kernel_source_digest(w.scheme) or kv.get("workload") != w.name:
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -120,7 +134,10 @@ def cpu_baseline(w, sample, budget_s=12.0):
     unit_w = w.scaled(batch=1, num_kv_heads=1, num_q_heads=hpg)
     refs = []
     for k, v, kn, vn, q in sample:
-        ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+        else:
+            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
         ref.prefill(k, v)
         ref.append(kn, vn)
         refs.append((ref, q))
@@ -132,7 +149,8 @@ def cpu_baseline(w, sample, budget_s=12.0):
             oracle.attention(q, K, V, 1.0 / math.sqrt(w.head_dim))
             t_total += time.perf_counter() - t0
             done += 1
-            nbytes += attn_bytes(unit_w, ref.n, ref.nq_k, ref.nq_v)
+            nq = ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_k
+            nbytes += attn_bytes(unit_w, ref.n, nq, ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_v)
             if t_total >= budget_s:
                 break
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -144,17 +162,25 @@ def cpu_baseline(w, sample, budget_s=12.0):
 
 def prefill_bytes(w, L):
     """Bytes a prefill of L tokens must move: fp16 K and V in, codes +
-    metadata + fp16 residual out."""
+    metadata + fp16 residual (or sinks and window) out."""
     d, b, G, R = w.head_dim, w.bits, w.group, w.residual
-    nq = L - L % R
-    out = nq * d * b // 8 * 2 + (nq // G) * d * 6 + nq * (d // G) * 6 + (L - nq) * d * 2 * 2
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        m = max(0, L - w.sinks - R)
+        out = m * 2 * (d * b // 8 + (d // G) * 6) + (L - m) * d * 2 * 2
+    else:
+        nq = L - L % R
+        out = nq * d * b // 8 * 2 + (nq // G) * d * 6 + nq * (d // G) * 6 + (L - nq) * d * 2 * 2
     return w.units * (L * d * 2 * 2 + out)
 
 
 def flush_bytes(w):
-    """Bytes one residual flush must move: R fp16 keys and values in, their
-    codes and metadata out (the append's own token write included)."""
+    """Bytes one quantizing append must move (the append's own token write
+    included).  KIVI: R fp16 keys and values in, their codes and metadata
+    out.  InnerQ: the token leaving the window in, its codes and metadata
+    out."""
     d, b, G, R = w.head_dim, w.bits, w.group, w.residual
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        return w.units * (d * 2 * 2 + 2 * (d * b // 8 + (d // G) * 6) + d * 2 * 2)
     return w.units * (R * d * 2 * 2 + R * d * b // 8 * 2 + (R // G) * d * 6 + R * (d // G) * 6 + d * 2 * 2)
 
 
@@ -164,9 +190,7 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
     L = w.context
     k, v = gen_prefill(w, 0, dev)
     cap = ((L + 2 * w.residual) // w.residual) * w.residual
-    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim, cap, w.v_policy)
-    c = kvq.KVCache(cfg, dev)
+    c = kvq.KVCache(make_cfg(w, cap), dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
     for _ in range(reps + 1):
@@ -178,8 +202,9 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
         times.append(e0.elapsed_time(e1) * 1e3)
     pre_us = sorted(times[1:])[len(times[1:]) // 2]
     # bring the residual to R - 1 tokens, then time the append that flushes
+    # (InnerQ: the window is full after a long prefill, every append quantizes)
     kn, vn = gen_new_tokens(w, 0, dev, steps=w.residual)
-    need = (w.residual - 1) - (c.n_tokens - c.nq_k)
+    need = 0 if w.scheme == kvq.KVQ_SCHEME_INNERQ else (w.residual - 1) - (c.n_tokens - c.nq_k)
     for i in range(need):
         c.append(kn[i], vn[i], stream.cuda_stream)
     state = (c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes)
@@ -200,7 +225,7 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
                         "frac": round(pb / pre_us / 1e3 / HBM_PEAK_GBS, 4), "tokens": L},
             "flush": {"us": round(fl_us, 2), "bytes": fb, "GB/s": round(fb / fl_us / 1e3, 1),
                       "frac": round(fb / fl_us / 1e3 / HBM_PEAK_GBS, 4),
-                      "per_appended_token_us": round(fl_us / w.residual, 3)}}
+                      "per_appended_token_us": round(fl_us / (1 if w.scheme else w.residual), 3)}}
 
 
 def main():
@@ -318,10 +343,11 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": w.context,
                    "bits": w.bits, "group": w.group, "residual": w.residual, "layers": layers,
-                   "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo"},
+                   "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo",
+                   "scheme": "innerq" if w.scheme == kvq.KVQ_SCHEME_INNERQ else "kivi", "sinks": w.sinks},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "decode_attn_kernel (one launch per call)", "avg_call_us": round(call_us, 2),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
+                     "kernel": KERNELS[w.scheme][0], "avg_call_us": round(call_us, 2),
                      "bytes_per_call": int(call_bytes)},
     }
     if side is not None:

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_DEVICE, KVQ_ERR_UNSUPPORTED = range(6)
 KVQ_V_CHUNK, KVQ_V_FIFO = 0, 1
+KVQ_SCHEME_KIVI, KVQ_SCHEME_INNERQ = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
@@ -29,12 +30,13 @@ EXPORTED = [
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bits", "group", "residual", "batch", "num_q_heads", "num_kv_heads", "head_dim",
-        "max_tokens", "v_policy")]
+        "max_tokens", "v_policy", "scheme", "sink_tokens")]
 
 
 class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")]
+        "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid", "k_sink",
+        "v_sink")]
 
 
 class kvq_cache(ctypes.Structure):
@@ -42,6 +44,7 @@ class kvq_cache(ctypes.Structure):
         ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
         ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
+        ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
         ("n_tokens", ctypes.c_int64), ("nq_k", ctypes.c_int64), ("nq_v", ctypes.c_int64),
         ("started", ctypes.c_int32), ("flushes", ctypes.c_int32),
     ]
@@ -97,9 +100,17 @@ def _check(status: int):
 
 
 def make_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                v_policy=KVQ_V_CHUNK) -> kvq_config:
+                v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0) -> kvq_config:
     return kvq_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                      v_policy)
+                      v_policy, scheme, sink_tokens)
+
+
+def make_innerq_config(bits, group, window, sink_tokens, batch, num_q_heads, num_kv_heads, head_dim,
+                       max_tokens) -> kvq_config:
+    """InnerQ-style cache: hybrid groups of `group` channels per token for keys
+    and values, `sink_tokens` leading and `window` recent tokens in fp16."""
+    return make_config(bits, group, window, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
+                       KVQ_V_FIFO, KVQ_SCHEME_INNERQ, sink_tokens)
 
 
 def kvq_layout_bytes(cfg: kvq_config) -> kvq_layout:
@@ -139,18 +150,21 @@ class KVCache:
 
     _DT = {"k_codes": torch.int32, "k_scale": torch.float32, "k_zero": torch.int16,
            "v_codes": torch.int32, "v_scale": torch.float32, "v_zero": torch.int16,
-           "k_resid": torch.float16, "v_resid": torch.float16}
+           "k_resid": torch.float16, "v_resid": torch.float16, "k_sink": torch.float16,
+           "v_sink": torch.float16}
 
     def __init__(self, cfg: kvq_config, device="cuda"):
         self.cfg = cfg
         lay = kvq_layout_bytes(cfg)
-        B, H, d, cap, G, R = (cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.max_tokens,
-                              cfg.group, cfg.residual)
+        B, H, d, cap, G, R, S = (cfg.batch, cfg.num_kv_heads, cfg.head_dim, cfg.max_tokens,
+                                 cfg.group, cfg.residual, cfg.sink_tokens)
         W = d * cfg.bits // 32
-        shapes = {"k_codes": (B, H, cap, W), "k_scale": (B, H, cap // G, d),
-                  "k_zero": (B, H, cap // G, d), "v_codes": (B, H, cap, W),
-                  "v_scale": (B, H, cap, d // G), "v_zero": (B, H, cap, d // G),
-                  "k_resid": (B, H, R, d), "v_resid": (B, H, R, d)}
+        innerq = cfg.scheme == KVQ_SCHEME_INNERQ
+        kmeta = (B, H, cap, d // G) if innerq else (B, H, cap // G, d)
+        shapes = {"k_codes": (B, H, cap, W), "k_scale": kmeta, "k_zero": kmeta,
+                  "v_codes": (B, H, cap, W), "v_scale": (B, H, cap, d // G),
+                  "v_zero": (B, H, cap, d // G), "k_resid": (B, H, R, d), "v_resid": (B, H, R, d),
+                  "k_sink": (B, H, S, d), "v_sink": (B, H, S, d)}
         self.tensors = {}
         for name, shp in shapes.items():
             t = torch.zeros(shp, dtype=self._DT[name], device=device)
@@ -158,7 +172,7 @@ class KVCache:
             self.tensors[name] = t
         self.c = kvq_cache()
         for name, t in self.tensors.items():
-            setattr(self.c, name, t.data_ptr())
+            setattr(self.c, name, t.data_ptr() if t.numel() else None)
         # per-call marshalling state, built once
         self._cfg_ref = ctypes.byref(cfg)
         self._c_ref = ctypes.byref(self.c)

@@ -1,13 +1,14 @@
 // Host side of libkvq: argument validation, buffer layout, host counters and
 // stream-ordered kernel launches.  See include/kvq.h for the contract.
 //
-// Cache state machine (KIVI part of the juejin.cn page "大模型量化技术原理：
+// KIVI cache state machine (KIVI part of the juejin.cn page "大模型量化技术原理：
 // KIVI、IntactKV、KVQuant", how it works; pgsm.cn KV-cache quantization
 // article, 3.1): the key cache is split into a grouped part of nq_k tokens
 // (a multiple of G, here also of R) and an fp16 remainder of n - nq_k < R
 // tokens; a new key joins the remainder, and when the remainder holds R
 // tokens it is quantized, appended and emptied in the same call.  Values use
-// the same chunked rule, or a FIFO queue of the R most recent tokens.
+// the same chunked rule, or a FIFO queue of the R most recent tokens.  The
+// InnerQ-style state machine is described at innerq_prefill below.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,11 +31,16 @@ kvq_status fail(kvq_status s, const char *fmt, ...) {
   return s;
 }
 
+bool is_innerq(const kvq_config *c) { return c->scheme == KVQ_SCHEME_INNERQ; }
+
 kvq_status check_config(const kvq_config *c) {
   if (!c) return fail(KVQ_ERR_ARG, "config is null");
+  if (c->scheme != KVQ_SCHEME_KIVI && c->scheme != KVQ_SCHEME_INNERQ) return fail(KVQ_ERR_ARG, "unknown scheme");
+  const bool iq = is_innerq(c);
   if (c->bits != 2 && c->bits != 4) return fail(KVQ_ERR_ARG, "bits must be 2 or 4 (got %d)", c->bits);
   if (c->group <= 0) return fail(KVQ_ERR_ARG, "group must be positive");
-  if (c->residual <= 0 || c->residual % c->group)
+  if (c->residual <= 0) return fail(KVQ_ERR_ARG, "residual must be positive");
+  if (!iq && c->residual % c->group)
     return fail(KVQ_ERR_ARG, "residual (%d) must be a positive multiple of group (%d)", c->residual, c->group);
   if (c->head_dim <= 0 || c->head_dim % c->group)
     return fail(KVQ_ERR_ARG, "head_dim (%d) must be a multiple of group (%d)", c->head_dim, c->group);
@@ -42,10 +48,16 @@ kvq_status check_config(const kvq_config *c) {
   if (c->batch <= 0 || c->num_kv_heads <= 0 || c->num_q_heads <= 0)
     return fail(KVQ_ERR_ARG, "batch and head counts must be positive");
   if (c->num_q_heads % c->num_kv_heads) return fail(KVQ_ERR_ARG, "num_q_heads must be a multiple of num_kv_heads");
-  if (c->max_tokens <= 0 || c->max_tokens % c->residual)
+  if (c->max_tokens <= 0) return fail(KVQ_ERR_ARG, "max_tokens must be positive");
+  if (!iq && c->max_tokens % c->residual)
     return fail(KVQ_ERR_ARG, "max_tokens (%d) must be a positive multiple of residual (%d)", c->max_tokens,
                 c->residual);
   if (c->v_policy != KVQ_V_CHUNK && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "unknown v_policy");
+  if (c->sink_tokens < 0) return fail(KVQ_ERR_ARG, "sink_tokens must be non-negative");
+  if (iq && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "the InnerQ scheme keeps a FIFO window (v_policy 1)");
+  if (!iq && c->sink_tokens) return fail(KVQ_ERR_UNSUPPORTED, "sink tokens are implemented for the InnerQ scheme only");
+  if (c->sink_tokens > 512) return fail(KVQ_ERR_UNSUPPORTED, "more than 512 sink tokens is not implemented");
+  if (c->max_tokens > (1 << 25)) return fail(KVQ_ERR_UNSUPPORTED, "max_tokens above 2^25 is not implemented");
   if (c->head_dim != kvq::kHeadDim) return fail(KVQ_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
   if (c->group != 32 && c->group != 64 && c->group != 128)
     return fail(KVQ_ERR_UNSUPPORTED, "only group 32, 64 or 128 is implemented");
@@ -58,11 +70,12 @@ kvq_status check_config(const kvq_config *c) {
   return KVQ_OK;
 }
 
-kvq_status check_cache(const kvq_cache *k) {
+kvq_status check_cache(const kvq_config *c, const kvq_cache *k) {
   if (!k) return fail(KVQ_ERR_ARG, "cache is null");
   if (!k->k_codes || !k->k_scale || !k->k_zero || !k->v_codes || !k->v_scale || !k->v_zero || !k->k_resid ||
       !k->v_resid)
     return fail(KVQ_ERR_ARG, "a cache buffer pointer is null");
+  if (c->sink_tokens > 0 && (!k->k_sink || !k->v_sink)) return fail(KVQ_ERR_ARG, "a sink buffer pointer is null");
   return KVQ_OK;
 }
 
@@ -76,10 +89,13 @@ kvq::CacheView view_of(const kvq_config *c, const kvq_cache *k) {
   v.v_zero = k->v_zero;
   v.k_resid = k->k_resid;
   v.v_resid = k->v_resid;
+  v.k_sink = k->k_sink;
+  v.v_sink = k->v_sink;
   v.cap = c->max_tokens;
   v.bits = c->bits;
   v.group = c->group;
   v.residual = c->residual;
+  v.sinks = c->sink_tokens;
   return v;
 }
 
@@ -92,13 +108,13 @@ int64_t main_tokens(const kvq_config *c, const kvq_cache *k) {
   return (m / c->group) * c->group;
 }
 
-int32_t auto_splits_for(const kvq_config *c, int64_t n_main) {
+// Splits for `nq` quantized tokens per unit: aim for two 8-wave workgroups
+// per compute unit of a 256-CU part, but keep at least 512 tokens (KIVI:
+// sixteen key groups, two per wave) in every split.
+int32_t auto_splits_for(const kvq_config *c, int64_t nq) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
-  const int64_t groups = n_main / c->group;
-  // aim for two 8-wave workgroups per compute unit of a 256-CU part, but
-  // keep at least sixteen key groups (two per wave) in every split
   int64_t s = (512 + units - 1) / units;
-  const int64_t by_work = groups / 16;
+  const int64_t by_work = is_innerq(c) ? nq / 512 : nq / c->group / 16;
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;
   if (s > kvq::kMaxSplits) s = kvq::kMaxSplits;
@@ -109,6 +125,54 @@ int32_t auto_splits_for(const kvq_config *c, int64_t n_main) {
 // query head.
 size_t workspace_for(const kvq_config *c, int32_t splits) {
   return (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
+}
+
+// InnerQ-style state (euno.news InnerQ summary, methodology 4): tokens
+// t < sinks are kept fp16 in the sink rows; later tokens enter a FIFO window
+// of at most R fp16 tokens (ring slot t mod R) whose oldest token is
+// quantized into row nq once a push would make it exceed R; tokens
+// [sinks, nq) are quantized.  While n <= sinks, nq == n.
+kvq_status innerq_prefill(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k, const uint16_t *v,
+                          int64_t len, hipStream_t stream) {
+  const int R = cfg->residual, S = cfg->sink_tokens;
+  const int units = cfg->batch * cfg->num_kv_heads;
+  const kvq::CacheView cv = view_of(cfg, cache);
+  const int64_t ns = len < S ? len : S;
+  const int64_t r = len > S ? (len - S < R ? len - S : R) : 0;
+  const int64_t nq = len - r;
+  hipError_t e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, S, k, v, len, 0, (int)ns, 0, units, stream);
+  if (e != hipSuccess) return device_error(e, "copy sink tokens");
+  if (nq > ns) {
+    e = kvq::launch_innerq_quantize(cv, units, k, v, len, ns, (int)(nq - ns), ns, stream);
+    if (e != hipSuccess) return device_error(e, "quantize prompt");
+  }
+  e = kvq::launch_copy_rows(cv.k_resid, cv.v_resid, R, k, v, len, nq, (int)r, (int)(nq % R), units, stream);
+  if (e != hipSuccess) return device_error(e, "copy window tokens");
+  cache->n_tokens = len;
+  cache->nq_k = cache->nq_v = nq;
+  cache->started = 1;
+  cache->flushes = 0;
+  return KVQ_OK;
+}
+
+kvq_status innerq_append(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new, const uint16_t *v_new,
+                         hipStream_t stream) {
+  const int R = cfg->residual, S = cfg->sink_tokens;
+  const int units = cfg->batch * cfg->num_kv_heads;
+  const int64_t n = cache->n_tokens, nq = cache->nq_k;
+  const bool to_sink = n < S;
+  const bool pop = !to_sink && n - nq == R;
+  const hipError_t e = kvq::launch_innerq_append(view_of(cfg, cache), units, k_new, v_new, pop ? nq : -1, to_sink,
+                                                 (int)(to_sink ? n : n % R), stream);
+  if (e != hipSuccess) return device_error(e, "append");
+  cache->n_tokens = n + 1;
+  if (to_sink) {
+    cache->nq_k = cache->nq_v = n + 1;
+  } else if (pop) {
+    cache->nq_k = cache->nq_v = nq + 1;
+    cache->flushes += 1;
+  }
+  return KVQ_OK;
 }
 
 }  // namespace
@@ -125,22 +189,31 @@ kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out) {
   const size_t words = d * cfg->bits / 32;
   const size_t G = (size_t)cfg->group;
   out->k_codes = units * cap * words * 4;
-  out->k_scale = units * (cap / G) * d * 4;
-  out->k_zero = units * (cap / G) * d * 2;
+  if (is_innerq(cfg)) {
+    out->k_scale = units * cap * (d / G) * 4;
+    out->k_zero = units * cap * (d / G) * 2;
+  } else {
+    out->k_scale = units * (cap / G) * d * 4;
+    out->k_zero = units * (cap / G) * d * 2;
+  }
   out->v_codes = units * cap * words * 4;
   out->v_scale = units * cap * (d / G) * 4;
   out->v_zero = units * cap * (d / G) * 2;
   out->k_resid = units * (size_t)cfg->residual * d * 2;
   out->v_resid = out->k_resid;
+  out->k_sink = units * (size_t)cfg->sink_tokens * d * 2;
+  out->v_sink = out->k_sink;
   g_err[0] = 0;
   return KVQ_OK;
 }
 
 int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens) {
   if (check_config(cfg) != KVQ_OK || n_tokens < 0) return 0;
-  // the split kernel covers the whole key groups of the quantized part; an
-  // upper bound of n_tokens keeps this a pure function of the length
-  const int64_t nq = n_tokens - (n_tokens % cfg->residual);
+  // an upper bound of the quantized tokens keeps this a pure function of the
+  // length: KIVI covers whole key groups of the grouped part, InnerQ the
+  // tokens after the sinks
+  const int64_t nq = is_innerq(cfg) ? (n_tokens > cfg->sink_tokens ? n_tokens - cfg->sink_tokens : 0)
+                                    : n_tokens - (n_tokens % cfg->residual);
   return auto_splits_for(cfg, nq);
 }
 
@@ -154,12 +227,17 @@ kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache, const u
                                 int64_t len, hipStream_t stream) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
-  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
   if (cache->started) return fail(KVQ_ERR_STATE, "prefill on a cache that already holds tokens");
   if (len < 0) return fail(KVQ_ERR_ARG, "negative length");
   if (len > cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "len %lld exceeds max_tokens %d", (long long)len,
                                          cfg->max_tokens);
   if (len > 0 && (!k || !v)) return fail(KVQ_ERR_ARG, "k or v is null");
+  if (is_innerq(cfg)) {
+    s = innerq_prefill(cfg, cache, k, v, len, stream);
+    if (s == KVQ_OK) g_err[0] = 0;
+    return s;
+  }
   const int R = cfg->residual, G = cfg->group;
   const int units = cfg->batch * cfg->num_kv_heads;
   const int64_t nq_k = len - (len % R);
@@ -197,10 +275,15 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
                             const uint16_t *v_new, hipStream_t stream) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
-  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
   if (!cache->started) return fail(KVQ_ERR_STATE, "append before prefill");
   if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new or v_new is null");
   if (cache->n_tokens >= cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "cache is full (%d tokens)", cfg->max_tokens);
+  if (is_innerq(cfg)) {
+    s = innerq_append(cfg, cache, k_new, v_new, stream);
+    if (s == KVQ_OK) g_err[0] = 0;
+    return s;
+  }
   const int R = cfg->residual, G = cfg->group;
   const int units = cfg->batch * cfg->num_kv_heads;
   const kvq::CacheView cv = view_of(cfg, cache);
@@ -245,7 +328,7 @@ kvq_status check_attention_args(const kvq_config *cfg, const kvq_cache *cache, c
                                 void *workspace, int32_t splits, float softmax_scale) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
-  if ((s = check_cache(cache)) != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
   if (!cache->started) return fail(KVQ_ERR_STATE, "attention before prefill");
   if (!q || !out || !workspace) return fail(KVQ_ERR_ARG, "q, out or workspace is null");
   if (splits < 0 || splits > kvq::kMaxSplits) return fail(KVQ_ERR_ARG, "splits must be in [0, %d]", kvq::kMaxSplits);
@@ -255,9 +338,42 @@ kvq_status check_attention_args(const kvq_config *cfg, const kvq_cache *cache, c
 
 // Enqueues attention over a cache of n_tokens tokens; with k_new/v_new the
 // last token is taken from them and stored into its residual slot.
+kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                   float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                   int32_t splits, hipStream_t stream) {
+  const int64_t n = cache->n_tokens;
+  const int64_t first = n < cfg->sink_tokens ? n : cfg->sink_tokens;
+  if (splits == 0) splits = auto_splits_for(cfg, cache->nq_k - first);
+  const size_t need = workspace_for(cfg, splits);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  kvq::AttnArgs a;
+  a.c = view_of(cfg, cache);
+  a.q = q;
+  a.out = out;
+  a.partials = static_cast<float *>(workspace);
+  a.batch = cfg->batch;
+  a.hq = cfg->num_q_heads;
+  a.hkv = cfg->num_kv_heads;
+  a.n = n;
+  a.nq_k = a.nq_v = cache->nq_k;
+  a.n_main = cache->nq_k;
+  a.splits = splits;
+  a.tail_wg = 0;
+  a.resid_main = 1;
+  a.nparts = splits;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.k_new = a.v_new = nullptr;
+  const hipError_t e = kvq::launch_innerq_attention(a, stream);
+  if (e != hipSuccess) return device_error(e, "decode attention");
+  return KVQ_OK;
+}
+
 kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64_t n_tokens, const uint16_t *k_new,
                             const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
                             void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream) {
+  if (is_innerq(cfg))
+    return launch_innerq_attention(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
   const int64_t m = cache->nq_k < cache->nq_v ? cache->nq_k : cache->nq_v;
   const int64_t n_main = (m / cfg->group) * cfg->group;
   if (splits == 0) splits = auto_splits_for(cfg, n_main);
@@ -319,7 +435,8 @@ kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16
   const int64_t n1 = cache->n_tokens + 1;
   // one launch when the append needs no flush or queue pop and the residual
   // is the chunked all-fp16 kind; otherwise the two calls in sequence
-  const bool fused = cfg->v_policy == KVQ_V_CHUNK && cache->nq_k == cache->nq_v && n1 - cache->nq_k < R;
+  const bool fused = !is_innerq(cfg) && cfg->v_policy == KVQ_V_CHUNK && cache->nq_k == cache->nq_v &&
+                     n1 - cache->nq_k < R;
   if (!fused) {
     const size_t need = workspace_for(cfg, splits == 0 ? kvq_auto_splits(cfg, n1) : splits);
     if (workspace_bytes < need)

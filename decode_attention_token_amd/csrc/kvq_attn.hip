@@ -36,159 +36,12 @@
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
+#include "kvq_attn_common.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kWaves = 8;                         // waves per workgroup
-constexpr int kThreads = kWave * kWaves;
-constexpr int kParts = kThreads / 128;            // thread groups of 128 in the reductions
-constexpr float kMargin = 8.0f;    // log2 units: weights stay below 2^8 between rescales
 constexpr int kMaxTail = 512 + 127;  // residual <= 512, group <= 128
-
-typedef float f2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-
-// 2^x with the hardware instruction; arguments here are <= kMargin or -inf,
-// and results below the fp32 normal range only ever weight negligible terms.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ---------------------------------------------------------------- cross-lane
-// DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1] swap lanes xor 1 and
-// xor 2; row_half_mirror / row_mirror reverse 8- and 16-lane blocks, which
-// pairs equal-sum halves once the smaller blocks are reduced.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over aligned blocks of N lanes; every lane of a block gets the same bits.
-template <int N>
-__device__ __forceinline__ float block_sum(float v) {
-  if constexpr (N >= 2) v += dpp<0xB1>(v);
-  if constexpr (N >= 4) v += dpp<0x4E>(v);
-  if constexpr (N >= 8) v += dpp<0x141>(v);
-  if constexpr (N >= 16) v += dpp<0x140>(v);
-  static_assert(N <= 16, "block wider than a DPP row");
-  return v;
-}
-
-template <int N>
-__device__ __forceinline__ float block_max(float v) {
-  if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
-  if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
-  if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
-  if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
-  return v;
-}
-
-__device__ __forceinline__ float lane_of(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Whole-wave sum / max, returned uniformly to every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = block_sum<16>(v);
-  return (lane_of(v, 0) + lane_of(v, 16)) + (lane_of(v, 32) + lane_of(v, 48));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = block_max<16>(v);
-  return fmaxf(fmaxf(lane_of(v, 0), lane_of(v, 16)), fmaxf(lane_of(v, 32), lane_of(v, 48)));
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// ---------------------------------------------------------------- unpacking
-// One 32-bit code word -> floats equal to code * scale, in channel order.
-// 2-bit: a nibble 0b00cc read as an fp4 e2m1 number is exactly cc / 2, so the
-// word is masked into nibbles and two nibbles convert per instruction
-// (16 codes: 3 integer + 8 conversion instructions).
-// 4-bit: a byte 0b0000cccc read as an fp8 e4m3 number is exactly cccc * 2^-9
-// (subnormals 0..7, then the first binade), two bytes per instruction.
-template <int BITS>
-struct Unpack;
-
-template <>
-struct Unpack<2> {
-  static constexpr float scale = 0.5f;
-  __device__ static __forceinline__ void run(uint32_t w, float *out) {
-    const uint32_t m0 = w & 0x33333333u;          // nibble k: code 2k
-    const uint32_t m1 = (w >> 2) & 0x33333333u;   // nibble k: code 2k + 1
-    f2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m0, 1.0f, 0);
-    f2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m1, 1.0f, 0);
-    f2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m0, 1.0f, 1);
-    f2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m1, 1.0f, 1);
-    f2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m0, 1.0f, 2);
-    f2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m1, 1.0f, 2);
-    f2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m0, 1.0f, 3);
-    f2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(m1, 1.0f, 3);
-    out[0] = a0.x;  out[2] = a0.y;  out[1] = b0.x;  out[3] = b0.y;
-    out[4] = a1.x;  out[6] = a1.y;  out[5] = b1.x;  out[7] = b1.y;
-    out[8] = a2.x;  out[10] = a2.y; out[9] = b2.x;  out[11] = b2.y;
-    out[12] = a3.x; out[14] = a3.y; out[13] = b3.x; out[15] = b3.y;
-  }
-};
-
-template <>
-struct Unpack<4> {
-  static constexpr float scale = 1.0f / 512.0f;
-  __device__ static __forceinline__ void run(uint32_t w, float *out) {
-    const uint32_t m0 = w & 0x0F0F0F0Fu;          // byte k: code 2k
-    const uint32_t m1 = (w >> 4) & 0x0F0F0F0Fu;   // byte k: code 2k + 1
-    f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(m0, false);
-    f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(m0, true);
-    f2 c = __builtin_amdgcn_cvt_pk_f32_fp8(m1, false);
-    f2 d = __builtin_amdgcn_cvt_pk_f32_fp8(m1, true);
-    out[0] = a.x; out[2] = a.y; out[4] = b.x; out[6] = b.y;
-    out[1] = c.x; out[3] = c.y; out[5] = d.x; out[7] = d.y;
-  }
-};
-
-// Raw buffer loads: an SGPR resource per stream, a lane-constant VGPR byte
-// offset and a uniform SGPR byte offset per step, so no vector ALU work goes
-// into addressing; out-of-range offsets read zero instead of faulting.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kStream = 2;   // cache policy: non-temporal (the cache is read once per call)
-
-__device__ __forceinline__ Rsrc rsrc_of(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-template <int N>
-__device__ __forceinline__ void bload_words(Rsrc r, uint32_t voff, uint32_t soff, uint32_t *w) {
-  if constexpr (N == 4) {
-    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStream));
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if constexpr (N == 2) {
-    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream));
-    w[0] = v.x; w[1] = v.y;
-  } else {
-    static_assert(N == 1, "words per lane");
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t *w) {
-  if constexpr (N == 4) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if constexpr (N == 2) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    w[0] = v.x; w[1] = v.y;
-  } else {
-    static_assert(N == 1, "words per lane");
-    w[0] = *p;
-  }
-}
 
 // ---------------------------------------------------------------- geometry
 template <int BITS, int GS, int HPG, int LPT>
@@ -201,53 +54,13 @@ struct Geo {
   static constexpr int NVG = CPL >= GS ? CPL / GS : 1;   // value groups per lane
   static constexpr int VGR = kHeadDim / GS;              // value groups per row
   static constexpr int SPG = GS / TPS;                   // wave steps per key group
-  static constexpr int RS = kHeadDim + 4;                // padded reduction row (floats)
-  static constexpr int RED = kWaves * TPS * RS + kParts * kHeadDim;
+  static constexpr int RED = kRedFloats<LPT>;
   static constexpr int QPW = HPG * (kHeadDim + 8);                // per wave: q'[HPG][128], beta[HPG][8]
   static constexpr int QP = kWaves * QPW;
   static constexpr int TAIL = HPG * kMaxTail + kParts * HPG * kHeadDim;
   static constexpr int WORK = RED > QP ? (RED > TAIL ? RED : TAIL) : (QP > TAIL ? QP : TAIL);
-  static constexpr int RES = HPG * kHeadDim + 2 * HPG + 2 * kWaves * HPG;
-  static constexpr int SMEM = WORK + RES;                // floats
+  static constexpr int SMEM = WORK + kStageFloats<HPG>;  // floats
 };
-
-// Result staging shared by the main and tail paths: acc[HPG][128], (m, l)[HPG],
-// per-wave (m, l)[kWaves][HPG].
-struct Stage {
-  float *acc, *ml, *wml;
-};
-
-template <int HPG>
-__device__ __forceinline__ Stage stage_of(float *smem, int work) {
-  Stage s;
-  s.acc = smem + work;
-  s.ml = s.acc + HPG * kHeadDim;
-  s.wml = s.ml + 2 * HPG;
-  return s;
-}
-
-// Writes this part's result: the normalized output when the unit has one
-// part, else an unnormalized (acc, m, l) record for the merge kernel.
-template <int HPG>
-__device__ void finish_part(const AttnArgs &a, int unit, int part, const Stage &st) {
-  const int tid = threadIdx.x;
-  const int b = unit / a.hkv, hk = unit % a.hkv;
-  const int nparts = a.nparts;
-  if (nparts == 1) {
-    for (int i = tid; i < HPG * kHeadDim; i += blockDim.x) {
-      const int h = i / kHeadDim, c = i % kHeadDim;
-      const int64_t bh = (int64_t)b * a.hq + hk * HPG + h;
-      a.out[bh * kHeadDim + c] = st.acc[i] / st.ml[2 * h + 1];
-    }
-    return;
-  }
-  for (int i = tid; i < HPG * (kHeadDim + 2); i += blockDim.x) {
-    const int h = i / (kHeadDim + 2), c = i % (kHeadDim + 2);
-    const int64_t bh = (int64_t)b * a.hq + hk * HPG + h;
-    float *rec = a.partials + (bh * nparts + part) * kPartialStride;
-    rec[c] = c < kHeadDim ? st.acc[h * kHeadDim + c] : st.ml[2 * h + (c - kHeadDim)];
-  }
-}
 
 // ---------------------------------------------------------------- tail path
 // Tokens [n_main, n): keys and values may each be quantized or fp16 per token.
@@ -359,11 +172,6 @@ struct StepBuf {
   uint32_t kz;       // their int16 zero-points
 };
 
-// Occupancy target: four waves per SIMD (at most 128 VGPRs) for the MHA
-// tilings, two for the grouped-query tiling that keeps 4 heads in registers.
-template <int HPG>
-constexpr int kWavesPerEU = HPG == 1 ? 4 : 2;
-
 template <int BITS, int GS, int HPG, int LPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
 void decode_attn_kernel(AttnArgs a) {
@@ -422,21 +230,14 @@ void decode_attn_kernel(AttnArgs a) {
   static_assert(FOLD <= 16 && (FOLD & (FOLD - 1)) == 0, "slice bias must reduce within a DPP row");
   float qf[HPG][CPL];
   float beta[HPG];   // zero-point bias of this lane's channel slice for the current key group
-  float m[HPG], mthr[HPG], lsum[HPG], acc[HPG][CPL], bias[HPG][NVG];
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
-    m[h] = -INFINITY;
-    mthr[h] = -INFINITY;
-    lsum[h] = 0.0f;
     beta[h] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      acc[h][i] = 0.0f;
-      qf[h][i] = 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < NVG; ++k) bias[h][k] = 0.0f;
+    for (int i = 0; i < CPL; ++i) qf[h][i] = 0.0f;
   }
+  Online<HPG, CPL, NVG> o;
+  o.init();
 
   // per-unit buffer resources (uniform); lane-constant byte offsets
   const int64_t ngr_cap = cap / GS;
@@ -468,24 +269,6 @@ void decode_attn_kernel(AttnArgs a) {
     }
     bf.ks = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rks, kmeta_lane * 4, g * (kHeadDim * 4), 0));
     bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, kmeta_lane * 2, g * (kHeadDim * 2), 0);
-  };
-
-  // online softmax with a lazily raised, wave-uniform maximum; returns p
-  auto soft = [&](int h, float sv) -> float {
-    if (__any(sv > mthr[h])) {
-      const float mn = fmaxf(m[h], wave_max(sv));
-      const float f = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      mthr[h] = mn + kMargin;
-      lsum[h] *= f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[h][i] *= f;
-#pragma unroll
-      for (int k = 0; k < NVG; ++k) bias[h][k] *= f;
-    }
-    const float p = fast_exp2(sv - m[h]);
-    lsum[h] += p;
-    return p;
   };
 
   auto process = [&](const Buf &bf, int s) {
@@ -536,7 +319,7 @@ void decode_attn_kernel(AttnArgs a) {
     }
     float p[HPG];
 #pragma unroll
-    for (int h = 0; h < HPG; ++h) p[h] = soft(h, block_sum<LPT>((sc[h] + d1[h]) + beta[h]));
+    for (int h = 0; h < HPG; ++h) p[h] = o.weight(h, block_sum<LPT>((sc[h] + d1[h]) + beta[h]));
     // values
     float vz[NVG];
     vz[0] = (float)(int16_t)(bf.vz & 0xffffu);
@@ -544,7 +327,7 @@ void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < HPG; ++h) {
 #pragma unroll
-      for (int k = 0; k < NVG; ++k) bias[h][k] = fmaf(p[h] * bf.vs[k], vz[k], bias[h][k]);
+      for (int k = 0; k < NVG; ++k) o.bias[h][k] = fmaf(p[h] * bf.vs[k], vz[k], o.bias[h][k]);
     }
 #pragma unroll
     for (int w = 0; w < WPL; ++w) {
@@ -556,7 +339,7 @@ void decode_attn_kernel(AttnArgs a) {
       for (int h = 0; h < HPG; ++h) {
         const float wt = p[h] * bf.vs[k];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[h][w * PER + i] = fmaf(wt, vf[i], acc[h][w * PER + i]);
+        for (int i = 0; i < PER; ++i) o.acc[h][w * PER + i] = fmaf(wt, vf[i], o.acc[h][w * PER + i]);
       }
     }
   };
@@ -605,96 +388,11 @@ void decode_attn_kernel(AttnArgs a) {
       const bool fresh = a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
       const uint16_t *krow = fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + (int64_t)slot * kHeadDim;
       const uint16_t *vrow = fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + (int64_t)slot * kHeadDim;
-      float kf[CPL], vf[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; i += 8) {
-        const uint4 kk = *reinterpret_cast<const uint4 *>(krow + i);
-        const uint4 vv = *reinterpret_cast<const uint4 *>(vrow + i);
-        const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
-        const uint32_t vw4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[i + 2 * e] = h2f((uint16_t)(kw4[e] & 0xffffu));
-          kf[i + 2 * e + 1] = h2f((uint16_t)(kw4[e] >> 16));
-          vf[i + 2 * e] = h2f((uint16_t)(vw4[e] & 0xffffu));
-          vf[i + 2 * e + 1] = h2f((uint16_t)(vw4[e] >> 16));
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < HPG; ++h) {
-        float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CPL; i += 2) {
-          d0 = fmaf(qf[h][i], kf[i], d0);
-          d1 = fmaf(qf[h][i + 1], kf[i + 1], d1);
-        }
-        float sv = block_sum<LPT>(d0 + d1);
-        sv = valid ? sv : -INFINITY;
-        const float wt = soft(h, sv) * U;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) acc[h][i] = fmaf(wt, vf[i], acc[h][i]);
-      }
+      fp16_token<HPG, CPL, NVG, LPT>(o, qf, krow, vrow, valid, U);
     }
   }
 
-  // ---- combine the waves and the TPS token lanes of each wave
-  float lw[HPG];
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) lw[h] = wave_sum(lsum[h]) * (1.0f / LPT);
-  __syncthreads();   // every wave is done with its folded-query buffer
-  float *s_red = smem;                              // [kWaves*TPS][RS]
-  float *s_half = smem + kWaves * TPS * Gm::RS;     // [kParts][128]
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      st.wml[(wave * HPG + h) * 2] = m[h];
-      st.wml[(wave * HPG + h) * 2 + 1] = lw[h];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.wml[(w * HPG + h) * 2]);
-    const float fw = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - M);
-    float *row = s_red + (wave * TPS + tl) * Gm::RS + j * CPL;
-#pragma unroll
-    for (int i = 0; i < CPL; i += 4) {
-      const int k0 = (NVG > 1) ? (i / (CPL / NVG)) : 0;
-      float4 v;
-      v.x = fmaf(acc[h][i], INV_U, bias[h][k0]) * fw;
-      v.y = fmaf(acc[h][i + 1], INV_U, bias[h][k0]) * fw;
-      v.z = fmaf(acc[h][i + 2], INV_U, bias[h][k0]) * fw;
-      v.w = fmaf(acc[h][i + 3], INV_U, bias[h][k0]) * fw;
-      *reinterpret_cast<float4 *>(row + i) = v;
-    }
-    __syncthreads();
-    {
-      const int c = tid & (kHeadDim - 1), half = tid >> 7;
-      float sum = 0.0f;
-      for (int r = half; r < kWaves * TPS; r += kParts) sum += s_red[r * Gm::RS + c];
-      s_half[half * kHeadDim + c] = sum;
-    }
-    __syncthreads();
-    if (tid < kHeadDim) {
-      float t = 0.0f;
-#pragma unroll
-      for (int p = 0; p < kParts; ++p) t += s_half[p * kHeadDim + tid];
-      st.acc[h * kHeadDim + tid] = t;
-      if (tid == 0) {
-        float L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = st.wml[(w * HPG + h) * 2];
-          if (mw != -INFINITY) L = fmaf(exp2f(mw - M), st.wml[(w * HPG + h) * 2 + 1], L);
-        }
-        st.ml[2 * h] = M;
-        st.ml[2 * h + 1] = L;
-      }
-    }
-    __syncthreads();
-  }
+  combine_waves<HPG, LPT, NVG>(o, smem, st, wave, lane, INV_U);
   finish_part<HPG>(a, unit, split, st);
 }
 
@@ -749,11 +447,16 @@ hipError_t launch_by_group(const AttnArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
-  hipError_t e = (a.c.bits == 2) ? launch_by_group<2>(a, s) : launch_by_group<4>(a, s);
-  if (e != hipSuccess || a.nparts == 1) return e;
+hipError_t launch_merge(const AttnArgs &a, hipStream_t s) {
+  if (a.nparts == 1) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.hq), dim3(kHeadDim), 0, s, a.partials, a.out, a.nparts);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
+  hipError_t e = (a.c.bits == 2) ? launch_by_group<2>(a, s) : launch_by_group<4>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_merge(a, s);
 }
 
 }  // namespace kvq

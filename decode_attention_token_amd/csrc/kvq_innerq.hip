@@ -1,0 +1,401 @@
+// InnerQ-style cache for gfx950: quantizer, append and decode attention.
+//
+// Layout (euno.news, "【论文】InnerQ：硬件感知免调优KV缓存量化用于大语言模型",
+// methodology 1, 2 and 4): keys and values are both grouped per token along
+// the hidden dimension, G channels per group, each group with one shared
+// scale; a group whose values are centred on zero is quantized symmetrically,
+// any other asymmetrically; the first `sinks` tokens and the most recent
+// `residual` tokens (a FIFO window) stay fp16.
+//
+// Symmetric groups store the signed level k in [-(2^(b-1)-1), 2^(b-1)-1] as
+// the code k + 2^(b-1) with zero-point Z = -2^(b-1), so S * (code + Z) is the
+// dequantized value in both modes and the attention kernel needs no mode bit.
+//
+// Attention.  Grouping along the reduction dimension means a lane's channel
+// slice (32 or 16 channels) lies inside one key group, so a token's score is
+//     s_t = sum_g S_tg (sum_{c in g} q_c k_tc + Z_tg sum_{c in g} q_c)
+// and each lane multiplies its partial dot product by its group's scale once
+// (methodology 3: the scale is loaded once per group and reused for the
+// group's products).  Values follow the same per-(token, group) rule as the
+// KIVI value path.  The lane layout, load pipeline, online softmax and wave
+// combination are those of the KIVI kernel (kvq_attn.hip).
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "kvq_internal.h"
+#include "kvq_attn_common.h"
+#include "kvq_quant_common.h"
+
+namespace kvq {
+namespace {
+
+// ---------------------------------------------------------------- quantizer
+// Quantizes the G fp16 values at x (one group of one token row).  Mode:
+// symmetric when 101 * s1^2 < G * s2 with s1 = sum x and s2 = sum x^2 taken in
+// float64 in channel order (|mean| < std / 10, population std).  Symmetric:
+// S = max|x| / (2^(b-1) - 1) (1 for an all-zero group), Z = -2^(b-1), codes
+// clamp(rint(x / S) - Z, 1, 2^b - 1).  Asymmetric: the KIVI group map.
+template <int BITS>
+__device__ __forceinline__ void quantize_group_hybrid(const uint16_t *x, int G, uint32_t *codes, float *scale,
+                                                      int16_t *zero) {
+  constexpr int PER = 32 / BITS;
+  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr float QM = float((1 << (BITS - 1)) - 1);
+  constexpr float HALF = float(1 << (BITS - 1));
+  float mn = INFINITY, mx = -INFINITY, amax = 0.0f;
+  double s1 = 0.0, s2 = 0.0;
+  for (int k0 = 0; k0 < G; k0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      mn = fminf(mn, v[k]);
+      mx = fmaxf(mx, v[k]);
+      amax = fmaxf(amax, fabsf(v[k]));
+      const double xd = (double)v[k];
+      s1 += xd;
+      s2 += xd * xd;   // exact product of an fp16 value, so contraction is harmless
+    }
+  }
+  const bool sym = 101.0 * (s1 * s1) < (double)G * s2;
+  GroupParams p;
+  float lo;
+  if (sym) {
+    const float s = amax > 0.0f ? amax / QM : 1.0f;
+    p = {s, -HALF, 1.0f / s};
+    lo = 1.0f;
+  } else {
+    p = group_params(mn, mx, QMAX);
+    lo = 0.0f;
+  }
+  *scale = p.s;
+  *zero = static_cast<int16_t>(p.z);
+  for (int k0 = 0; k0 < G; k0 += 32) {
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+    uint32_t cd[32];
+    codes_of<32>(v, p, lo, QMAX, cd);
+    uint32_t words[32 / PER];
+#pragma unroll
+    for (int w = 0; w < 32 / PER; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) word |= cd[w * PER + k] << (k * BITS);
+      words[w] = word;
+    }
+    if constexpr (BITS == 2) {
+      *reinterpret_cast<uint2 *>(codes + k0 / PER) = make_uint2(words[0], words[1]);
+    } else {
+      *reinterpret_cast<uint4 *>(codes + k0 / PER) = make_uint4(words[0], words[1], words[2], words[3]);
+    }
+  }
+}
+
+// Destination of group j of token row `row` (absolute, unit * cap + t).
+template <int BITS>
+__device__ __forceinline__ void quantize_into(const CacheView &c, bool values, const uint16_t *x, int64_t row,
+                                              int j) {
+  constexpr int PER = 32 / BITS;
+  constexpr int W = kHeadDim / PER;
+  const int G = c.group, NG = kHeadDim / G;
+  uint32_t *codes = (values ? c.v_codes : c.k_codes) + row * W + j * (G / PER);
+  float *scale = (values ? c.v_scale : c.k_scale) + row * NG + j;
+  int16_t *zero = (values ? c.v_zero : c.k_zero) + row * NG + j;
+  quantize_group_hybrid<BITS>(x, G, codes, scale, zero);
+}
+
+// One thread per (tensor, unit, row, group): keys in the first half of the
+// grid, values in the second.  Source row src_row0 + i of [unit][src_rows]
+// [128] goes to cache row dst_row0 + i.
+template <int BITS>
+__global__ __launch_bounds__(256) void innerq_quantize_kernel(CacheView c, const uint16_t *__restrict__ ksrc,
+                                                              const uint16_t *__restrict__ vsrc, int64_t src_rows,
+                                                              int64_t src_row0, int count, int64_t dst_row0,
+                                                              int units) {
+  const int NG = kHeadDim / c.group;
+  const int64_t per = (int64_t)units * count * NG;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= 2 * per) return;
+  const bool values = idx >= per;
+  if (values) idx -= per;
+  const int j = (int)(idx % NG);
+  const int64_t r = idx / NG;
+  const int i = (int)(r % count);
+  const int unit = (int)(r / count);
+  const uint16_t *x = (values ? vsrc : ksrc) + ((int64_t)unit * src_rows + src_row0 + i) * kHeadDim + j * c.group;
+  quantize_into<BITS>(c, values, x, (int64_t)unit * c.cap + dst_row0 + i, j);
+}
+
+// One workgroup (one wave) per unit.  When pop_row >= 0 the window is full:
+// the oldest window token (ring slot pop_row mod R) is quantized into cache
+// row pop_row first.  Then the new key and value rows are written into row
+// `slot` of the sink rows (to_sink) or of the ring.
+template <int BITS>
+__global__ __launch_bounds__(64) void innerq_append_kernel(CacheView c, const uint16_t *__restrict__ k_new,
+                                                           const uint16_t *__restrict__ v_new, int64_t pop_row,
+                                                           int to_sink, int slot) {
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int R = c.residual, NG = kHeadDim / c.group;
+  if (pop_row >= 0) {
+    if (tid < 2 * NG) {
+      const bool values = tid >= NG;
+      const int j = tid % NG;
+      const uint16_t *ring = values ? c.v_resid : c.k_resid;
+      const uint16_t *x = ring + ((int64_t)unit * R + pop_row % R) * kHeadDim + j * c.group;
+      quantize_into<BITS>(c, values, x, (int64_t)unit * c.cap + pop_row, j);
+    }
+    __syncthreads();   // the popped slot is read before the new token overwrites it
+  }
+  constexpr int CH = kHeadDim * 2 / 16;   // 16-byte chunks per row
+  if (tid < 2 * CH) {
+    const bool values = tid >= CH;
+    const int ch = tid % CH;
+    const uint4 *src = reinterpret_cast<const uint4 *>((values ? v_new : k_new) + (int64_t)unit * kHeadDim);
+    uint16_t *base = to_sink ? (values ? c.v_sink : c.k_sink) + ((int64_t)unit * c.sinks + slot) * kHeadDim
+                             : (values ? c.v_resid : c.k_resid) + ((int64_t)unit * R + slot) * kHeadDim;
+    reinterpret_cast<uint4 *>(base)[ch] = src[ch];
+  }
+}
+
+// ---------------------------------------------------------------- attention
+template <int WPL>
+struct IqBuf {
+  uint32_t kw[WPL];
+  uint32_t vw[WPL];
+  float ks, vs;       // this lane's key / value group scales
+  uint32_t kz, vz;    // their int16 zero-points (low half)
+};
+
+// One workgroup of 8 waves per (split, unit).  The quantized tokens
+// [t0, nq) (t0 = number of sink tokens present) are cut into steps of TPS
+// tokens; each split takes a contiguous range of steps and each wave a
+// contiguous sub-range.  Lanes of a token past nq score -inf.  The last split
+// also takes the fp16 tokens: the sinks and the window [nq, n).
+template <int BITS, int GS, int HPG, int LPT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
+void innerq_attn_kernel(AttnArgs a) {
+  constexpr int CPL = kHeadDim / LPT, TPS = kWave / LPT, PER = 32 / BITS, WPL = CPL / PER;
+  constexpr int W = kHeadDim / PER;
+  constexpr int NG = kHeadDim / GS;
+  constexpr float U = Unpack<BITS>::scale;
+  constexpr float INV_U = 1.0f / U;
+  static_assert(CPL <= GS, "a lane's channel slice must lie inside one group");
+  static_assert(WPL >= 1, "lane slice must hold whole words");
+  using Buf = IqBuf<WPL>;
+
+  __shared__ __attribute__((aligned(16))) float smem[kRedFloats<LPT> + kStageFloats<HPG>];
+  const Stage st = stage_of<HPG>(smem, kRedFloats<LPT>);
+
+  const int units = a.batch * a.hkv;
+  const int split = blockIdx.x / units;
+  const int unit = blockIdx.x % units;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane % LPT, tl = lane / LPT;
+  const int b = unit / a.hkv, hk = unit % a.hkv;
+  const int64_t cap = a.c.cap;
+  const int S = a.c.sinks;
+  const int64_t nsink = a.n < S ? a.n : S;   // sink tokens present
+  const int64_t t0 = nsink;                  // first quantized token
+  const int64_t nq = a.nq_k;                 // end of the quantized tokens
+  const int tsteps = (int)((nq - t0 + TPS - 1) / TPS);
+  const int s0 = (int)((int64_t)tsteps * split / a.splits);
+  const int s1 = (int)((int64_t)tsteps * (split + 1) / a.splits);
+  const int ws0 = s0 + (s1 - s0) * wave / kWaves;
+  const int ws1 = s0 + (s1 - s0) * (wave + 1) / kWaves;
+  const int nsteps = ws1 - ws0;
+
+  // query slice of this lane, in log2 units and divided by the unpack scale,
+  // and its plain sum (the zero-point term of the lane's group)
+  float qf[HPG][CPL], qsum[HPG];
+#pragma unroll
+  for (int h = 0; h < HPG; ++h) {
+    const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * HPG + h)) * kHeadDim + j * CPL;
+    qsum[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float qv = h2f(qp[i]) * a.qscale;
+      qsum[h] += qv;
+      qf[h][i] = qv * INV_U;
+    }
+  }
+  Online<HPG, CPL, 1> o;
+  o.init();
+
+  // per-unit buffer resources; the step's token offset goes into the vector
+  // offset so the hardware range check turns reads past the capacity into
+  // zeros (those lanes are masked)
+  const Rsrc rkc = rsrc_of(a.c.k_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
+  const Rsrc rvc = rsrc_of(a.c.v_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
+  const Rsrc rks = rsrc_of(a.c.k_scale + (int64_t)unit * cap * NG, (uint32_t)(cap * NG * 4));
+  const Rsrc rkz = rsrc_of(a.c.k_zero + (int64_t)unit * cap * NG, (uint32_t)(cap * NG * 2));
+  const Rsrc rvs = rsrc_of(a.c.v_scale + (int64_t)unit * cap * NG, (uint32_t)(cap * NG * 4));
+  const Rsrc rvz = rsrc_of(a.c.v_zero + (int64_t)unit * cap * NG, (uint32_t)(cap * NG * 2));
+  const uint32_t code_lane = (uint32_t)(tl * W + j * WPL) * 4u;
+  const uint32_t meta_lane = (uint32_t)(tl * NG + (j * CPL) / GS);
+
+  auto load = [&](Buf &bf, int s) {
+    s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
+    const uint32_t tb = (uint32_t)(t0 + (int64_t)(ws0 + s) * TPS);   // first token of the step
+    const uint32_t vc = code_lane + tb * (W * 4);
+    const uint32_t vm = meta_lane + tb * NG;
+    bload_words<WPL>(rkc, vc, 0, bf.kw);
+    bload_words<WPL>(rvc, vc, 0, bf.vw);
+    bf.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, vm * 4, 0, kStream));
+    bf.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, vm * 4, 0, kStream));
+    bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, vm * 2, 0, kStream);
+    bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, vm * 2, 0, kStream);
+  };
+
+  auto process = [&](const Buf &bf, int s) {
+    const bool valid = t0 + (int64_t)(ws0 + s) * TPS + tl < nq;
+    const float kz = (float)(int16_t)(bf.kz & 0xffffu);
+    const float vz = (float)(int16_t)(bf.vz & 0xffffu);
+    float sc[HPG], d1[HPG];
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) sc[h] = d1[h] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WPL; ++w) {
+      float kf[PER];
+      Unpack<BITS>::run(bf.kw[w], kf);
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) {
+#pragma unroll
+        for (int i = 0; i < PER; i += 2) {
+          sc[h] = fmaf(qf[h][w * PER + i], kf[i], sc[h]);
+          d1[h] = fmaf(qf[h][w * PER + i + 1], kf[i + 1], d1[h]);
+        }
+      }
+    }
+    float p[HPG];
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      const float sv = block_sum<LPT>(bf.ks * fmaf(kz, qsum[h], sc[h] + d1[h]));
+      p[h] = o.weight(h, valid ? sv : -INFINITY);
+    }
+    const float vs = valid ? bf.vs : 0.0f;   // rows past nq may hold any bits
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) o.bias[h][0] = fmaf(p[h] * vs, vz, o.bias[h][0]);
+#pragma unroll
+    for (int w = 0; w < WPL; ++w) {
+      float vf[PER];
+      Unpack<BITS>::run(bf.vw[w], vf);
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) {
+        const float wt = p[h] * vs;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o.acc[h][w * PER + i] = fmaf(wt, vf[i], o.acc[h][w * PER + i]);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    Buf A, B, C;
+    load(A, 0);
+    load(B, 1);
+    for (int s = 0; s < nsteps; s += 3) {
+      load(C, s + 2);
+      process(A, s);
+      load(A, s + 3);
+      if (s + 1 < nsteps) process(B, s + 1);
+      load(B, s + 4);
+      if (s + 2 < nsteps) process(C, s + 2);
+    }
+  }
+
+  // fp16 tokens: sinks [0, nsink) from the sink rows, then the window
+  // [nq, n) from ring slots t mod R
+  if (split == a.splits - 1) {
+    const int R = a.c.residual;
+    const int nf = (int)(nsink + (a.n - nq));
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) qf[h][i] *= U;   // back to q * qscale
+    }
+    for (int rs = wave; rs * TPS < nf; rs += kWaves) {
+      const int i = rs * TPS + tl;
+      const bool valid = i < nf;
+      const int ii = valid ? i : 0;
+      const uint16_t *krow, *vrow;
+      if (ii < nsink) {
+        const int64_t off = ((int64_t)unit * S + ii) * kHeadDim + j * CPL;
+        krow = a.c.k_sink + off;
+        vrow = a.c.v_sink + off;
+      } else {
+        const int64_t off = ((int64_t)unit * R + (nq + (ii - nsink)) % R) * kHeadDim + j * CPL;
+        krow = a.c.k_resid + off;
+        vrow = a.c.v_resid + off;
+      }
+      fp16_token<HPG, CPL, 1, LPT>(o, qf, krow, vrow, valid, U);
+    }
+  }
+
+  combine_waves<HPG, LPT, 1>(o, smem, st, wave, lane, INV_U);
+  finish_part<HPG>(a, unit, split, st);
+}
+
+template <int BITS, int GS, int HPG>
+hipError_t launch_iq_kernel(const AttnArgs &a, hipStream_t s) {
+  constexpr int LPT = (HPG == 4) ? 8 : 4;
+  hipLaunchKernelGGL((innerq_attn_kernel<BITS, GS, HPG, LPT>), dim3(a.batch * a.hkv * a.nparts), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int GS>
+hipError_t launch_iq_by_heads(const AttnArgs &a, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: return launch_iq_kernel<BITS, GS, 1>(a, s);
+    case 2: return launch_iq_kernel<BITS, GS, 2>(a, s);
+    case 4: return launch_iq_kernel<BITS, GS, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BITS>
+hipError_t launch_iq_by_group(const AttnArgs &a, hipStream_t s) {
+  switch (a.c.group) {
+    case 32: return launch_iq_by_heads<BITS, 32>(a, s);
+    case 64: return launch_iq_by_heads<BITS, 64>(a, s);
+    case 128: return launch_iq_by_heads<BITS, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_innerq_quantize(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
+                                  int64_t src_rows, int64_t src_row0, int count, int64_t dst_row0, hipStream_t s) {
+  if (count <= 0 || units <= 0) return hipSuccess;
+  const int64_t total = 2 * (int64_t)units * count * (kHeadDim / c.group);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (c.bits == 2)
+    hipLaunchKernelGGL(innerq_quantize_kernel<2>, dim3(blocks), dim3(256), 0, s, c, ksrc, vsrc, src_rows, src_row0,
+                       count, dst_row0, units);
+  else
+    hipLaunchKernelGGL(innerq_quantize_kernel<4>, dim3(blocks), dim3(256), 0, s, c, ksrc, vsrc, src_rows, src_row0,
+                       count, dst_row0, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_innerq_append(const CacheView &c, int units, const uint16_t *k_new, const uint16_t *v_new,
+                                int64_t pop_row, bool to_sink, int slot, hipStream_t s) {
+  if (c.bits == 2)
+    hipLaunchKernelGGL(innerq_append_kernel<2>, dim3(units), dim3(64), 0, s, c, k_new, v_new, pop_row,
+                       to_sink ? 1 : 0, slot);
+  else
+    hipLaunchKernelGGL(innerq_append_kernel<4>, dim3(units), dim3(64), 0, s, c, k_new, v_new, pop_row,
+                       to_sink ? 1 : 0, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_innerq_attention(const AttnArgs &a, hipStream_t s) {
+  hipError_t e = (a.c.bits == 2) ? launch_iq_by_group<2>(a, s) : launch_iq_by_group<4>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_merge(a, s);
+}
+
+}  // namespace kvq

@@ -20,8 +20,11 @@ struct CacheView {
   int16_t *v_zero;
   uint16_t *k_resid;
   uint16_t *v_resid;
+  uint16_t *k_sink;   // InnerQ-style layout: fp16 sink rows [unit][sinks][128]
+  uint16_t *v_sink;
   int64_t cap;      // max_tokens
   int bits, group, residual;
+  int sinks;        // sink tokens kept fp16 (InnerQ-style layout; 0 otherwise)
 };
 
 // Quantize `ngroups` key groups per unit.  Source rows: src + (unit * src_rows
@@ -42,6 +45,26 @@ hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t 
 hipError_t launch_copy_to_residual(const CacheView &c, int units, const uint16_t *ksrc,
                                    const uint16_t *vsrc, int64_t src_rows, int64_t row0,
                                    int count, int slot0, bool keys, bool values, hipStream_t s);
+
+// Copy rows [row0, row0 + count) of ksrc / vsrc ([unit][src_rows][128] fp16)
+// into rows (slot0 + i) mod dst_rows of kdst / vdst ([unit][dst_rows][128]);
+// a null destination is skipped.
+hipError_t launch_copy_rows(uint16_t *kdst, uint16_t *vdst, int dst_rows, const uint16_t *ksrc,
+                            const uint16_t *vsrc, int64_t src_rows, int64_t row0, int count, int slot0,
+                            int units, hipStream_t s);
+
+// InnerQ-style layout: quantize `count` token rows per unit, keys from ksrc
+// and values from vsrc (row src_row0 + i of [unit][src_rows][128]), into
+// cache rows dst_row0 + i, hybrid groups of G channels.
+hipError_t launch_innerq_quantize(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
+                                  int64_t src_rows, int64_t src_row0, int count, int64_t dst_row0,
+                                  hipStream_t s);
+
+// InnerQ-style append: if pop_row >= 0, quantize ring slot pop_row mod R into
+// cache row pop_row; then store k_new / v_new ([unit][128]) into row `slot`
+// of the sink rows (to_sink) or of the ring.
+hipError_t launch_innerq_append(const CacheView &c, int units, const uint16_t *k_new, const uint16_t *v_new,
+                                int64_t pop_row, bool to_sink, int slot, hipStream_t s);
 
 struct AttnArgs {
   CacheView c;
@@ -64,5 +87,13 @@ struct AttnArgs {
 };
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s);
+
+// InnerQ-style attention: quantized tokens [min(n, sinks), nq_k) split over
+// `splits` workgroups per unit, fp16 sinks and window in the last split;
+// nparts == splits.
+hipError_t launch_innerq_attention(const AttnArgs &a, hipStream_t s);
+
+// Second launch that merges the part records when nparts > 1 (no-op else).
+hipError_t launch_merge(const AttnArgs &a, hipStream_t s);
 
 }  // namespace kvq

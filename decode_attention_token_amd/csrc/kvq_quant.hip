@@ -14,69 +14,10 @@
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
+#include "kvq_quant_common.h"
 
 namespace kvq {
 namespace {
-
-__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-
-struct GroupParams {
-  float s, z;
-  float r;   // RN(1 / s), for the fast quotient
-};
-
-// Scale and zero-point of one group from its minimum and maximum: S spreads
-// the range over the 2^b - 1 steps and Z = rint(min / S), which maps the
-// minimum to code 0.  A constant group takes S = |min| (1 for an all-zero
-// group) and so reconstructs exactly.
-__device__ __forceinline__ GroupParams group_params(float mn, float mx, float qmax) {
-  float s;
-  if (mx > mn) {
-    s = (mx - mn) / qmax;
-  } else {
-    s = (mn != 0.0f) ? fabsf(mn) : 1.0f;
-  }
-  return {s, rintf(mn / s), 1.0f / s};
-}
-
-__device__ __forceinline__ uint32_t code_of(float x, GroupParams p, float qmax) {
-  float q = rintf(x / p.s) - p.z;
-  q = fminf(fmaxf(q, 0.0f), qmax);
-  return static_cast<uint32_t>(q);
-}
-
-// Codes of N values of one group.  rint(x / s) with x / s correctly rounded
-// equals rint(x * r), r = RN(1/s), unless the quotient lies within 2^-21 |x/s|
-// of a half-integer (x * r is that close to the correctly rounded quotient).
-// The fast products are checked for that; if any lane of the wave meets such
-// a value, the whole chunk is redone with IEEE divisions (a rare, uniform
-// branch), so the codes stay exactly those of the correctly rounded map.
-template <int N>
-__device__ __forceinline__ void codes_of(const float *x, GroupParams p, float qmax, uint32_t *code) {
-  bool near = false;
-#pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const float y = x[k] * p.r;
-    const float mid = floorf(y) + 0.5f;
-    near |= fabsf(y - mid) <= fmaxf(fabsf(y), 1.0f) * 0x1p-20f;
-    code[k] = static_cast<uint32_t>(fminf(fmaxf(rintf(y) - p.z, 0.0f), qmax));
-  }
-  if (__any(near)) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) code[k] = code_of(x[k], p, qmax);
-  }
-}
-
-// Unpacks 8 fp16 values (one 16-byte load) to fp32.
-__device__ __forceinline__ void load8(const uint16_t *p, float *x) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = h2f((uint16_t)(w[i] & 0xffffu));
-    x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
-  }
-}
 
 // One workgroup of 256 threads quantizes one key group (GS tokens x 128
 // channels) of one unit.  Thread (pair, part) owns channels 2*pair, 2*pair+1
@@ -134,8 +75,8 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
         (uint32_t)(uint16_t)(int16_t)p0.z | ((uint32_t)(uint16_t)(int16_t)p1.z << 16);
   }
   uint32_t ca[TQ], cb[TQ];
-  codes_of<TQ>(xa, p0, QMAX, ca);
-  codes_of<TQ>(xb, p1, QMAX, cb);
+  codes_of<TQ>(xa, p0, 0.0f, QMAX, ca);
+  codes_of<TQ>(xb, p1, 0.0f, QMAX, cb);
 #pragma unroll
   for (int t = 0; t < TQ; ++t)
     *reinterpret_cast<uint16_t *>(&s_code[part * TQ + t][ch]) = (uint16_t)(ca[t] | (cb[t] << 8));
@@ -193,7 +134,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
 #pragma unroll
     for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
     uint32_t cd[32];
-    codes_of<32>(v, p, QMAX, cd);
+    codes_of<32>(v, p, 0.0f, QMAX, cd);
     uint32_t words[32 / PER];
 #pragma unroll
     for (int w = 0; w < 32 / PER; ++w) {
@@ -210,8 +151,9 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   }
 }
 
-// Copies fp16 rows into the residual rings, 16 bytes per thread; the second
-// half of the grid (when both are given) copies the value rows.
+// Copies fp16 rows into ring-indexed destination rows (the residual rings or
+// the sink rows), 16 bytes per thread; the second half of the grid (when both
+// destinations are given) copies the value rows.
 __global__ __launch_bounds__(256) void copy_rows_kernel(uint16_t *__restrict__ kring, uint16_t *__restrict__ vring,
                                                         int ring_rows, const uint16_t *__restrict__ ksrc,
                                                         const uint16_t *__restrict__ vsrc, int64_t src_rows,
@@ -273,16 +215,23 @@ hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t 
   return hipGetLastError();
 }
 
+hipError_t launch_copy_rows(uint16_t *kdst, uint16_t *vdst, int dst_rows, const uint16_t *ksrc,
+                            const uint16_t *vsrc, int64_t src_rows, int64_t row0, int count, int slot0,
+                            int units, hipStream_t s) {
+  if (count <= 0 || units <= 0) return hipSuccess;
+  if (kdst == nullptr && vdst == nullptr) return hipSuccess;
+  const int64_t total = (int64_t)units * count * (kHeadDim * 2 / 16) * ((kdst && vdst) ? 2 : 1);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, kdst, vdst, dst_rows, ksrc, vsrc, src_rows,
+                     row0, count, slot0, units);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_to_residual(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
                                    int64_t src_rows, int64_t row0, int count, int slot0, bool keys, bool values,
                                    hipStream_t s) {
-  if (count <= 0 || units <= 0) return hipSuccess;
-  if (!keys && !values) return hipSuccess;
-  const int64_t total = (int64_t)units * count * (kHeadDim * 2 / 16) * ((keys && values) ? 2 : 1);
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, s, keys ? c.k_resid : nullptr,
-                     values ? c.v_resid : nullptr, c.residual, ksrc, vsrc, src_rows, row0, count, slot0, units);
-  return hipGetLastError();
+  return launch_copy_rows(keys ? c.k_resid : nullptr, values ? c.v_resid : nullptr, c.residual, ksrc, vsrc,
+                          src_rows, row0, count, slot0, units, s);
 }
 
 }  // namespace kvq

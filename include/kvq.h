@@ -1,6 +1,7 @@
 /*
- * kvq.h - C ABI of libkvq: KIVI-style 2/4-bit quantized KV cache and decode
- * attention over it, for AMD Instinct MI355X (gfx950).
+ * kvq.h - C ABI of libkvq: 2/4-bit quantized KV caches (KIVI-style and
+ * InnerQ-style) and decode attention over them, for AMD Instinct MI355X
+ * (gfx950).
  *
  * Method sources (web pages, cited by title and section):
  *   [KIVI] juejin.cn, "大模型量化技术原理：KIVI、IntactKV、KVQuant", KIVI part:
@@ -10,9 +11,14 @@
  *          once it holds R tokens with R % G == 0, value queue, prefill keeps
  *          only the quantized cache).
  *   [HFQ]  pgsm.cn news 20017, KV-cache quantization article: 2.1 affine map
- *          X_Q = round(X / S) - Z, 2.2 keys per channel / values per token,
- *          3.1 fp16 residual cache batch-quantized when full, 4.1 knobs
- *          nbits, group_size, residual_length.
+ *          X_Q = round(X / S) - Z, symmetric vs asymmetric ranges, 2.2 keys
+ *          per channel / values per token, 3.1 fp16 residual cache
+ *          batch-quantized when full, 4.1 knobs nbits, group_size,
+ *          residual_length.
+ *   [InnerQ] euno.news, "【论文】InnerQ：硬件感知免调优KV缓存量化用于大语言模型",
+ *          methodology 1 (groups along the hidden dimension), 2 (per-group
+ *          symmetric or asymmetric mode from the group statistics, one shared
+ *          scale per group), 4 (recent and sink tokens kept fp16).
  *
  * Conventions
  *   - fp16 tensors are passed as uint16_t bit patterns; every pointer named
@@ -27,12 +33,14 @@
  *     nothing and leaves kvq_cache unchanged; kvq_last_error() explains why.
  *     A failed kernel launch returns KVQ_ERR_DEVICE; counters are then
  *     undefined and the cache must be rebuilt.
- *   - Only head_dim == 128, bits in {2, 4}, G in {32, 64, 128} and a query to
- *     key head ratio in {1, 2, 4} are implemented; other valid shapes return
+ *   - Only head_dim == 128, bits in {2, 4}, G in {32, 64, 128}, a query to
+ *     key head ratio in {1, 2, 4}, residual <= 512, sink_tokens <= 512 and
+ *     max_tokens <= 2^25 are implemented; other valid shapes return
  *     KVQ_ERR_UNSUPPORTED.
  *
- * Device layout of one layer's cache (U = batch * num_kv_heads units, unit
- * u = b * num_kv_heads + h; cap = max_tokens; W = head_dim * bits / 32):
+ * Device layout of one layer's KVQ_SCHEME_KIVI cache (U = batch *
+ * num_kv_heads units, unit u = b * num_kv_heads + h; cap = max_tokens;
+ * W = head_dim * bits / 32):
  *   k_codes u32 [U][cap][W]        token-major rows; channel c's code sits at
  *                                  bits [(c*bits) % 32, +bits) of word
  *                                  (c*bits) / 32 of the token's row
@@ -44,6 +52,16 @@
  *   k_resid, v_resid f16 [U][R][head_dim]  fp16 residual ring, token t in
  *                                  slot t mod R
  *   Dequantized value of a code: S * (code + Z) (inverse of [HFQ] 2.1).
+ *
+ * Device layout of a KVQ_SCHEME_INNERQ cache: k_codes, v_codes as above;
+ *   k_scale, v_scale f32 [U][cap][head_dim/G]  per (token, group of G channels)
+ *   k_zero, v_zero   i16 [U][cap][head_dim/G]
+ *   k_resid, v_resid f16 [U][R][head_dim]  recent-token window, token t in
+ *                                  slot t mod R
+ *   k_sink, v_sink   f16 [U][sink_tokens][head_dim]  token t < sink_tokens
+ *   Quantized tokens are those in [sink_tokens, nq); a symmetric group stores
+ *   the signed level k as code k + 2^(bits-1) with Z = -2^(bits-1), so
+ *   S * (code + Z) dequantizes both modes.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -71,11 +89,26 @@ typedef enum {
  * quantized and appended ([KIVI] how it works, value queue). */
 typedef enum { KVQ_V_CHUNK = 0, KVQ_V_FIFO = 1 } kvq_v_policy;
 
+/* Quantization scheme.
+ * KVQ_SCHEME_KIVI: keys per channel over groups of G tokens, values per token
+ *   over groups of G channels, asymmetric ([KIVI], [HFQ] 2.2); fp16 residual
+ *   of fewer than R tokens (or the R most recent values, KVQ_V_FIFO).
+ * KVQ_SCHEME_INNERQ: keys and values both per token over groups of G channels
+ *   ([InnerQ] methodology 1); each group symmetric when it is centred on zero,
+ *   read as |mean| < std / 10 with the population std, else asymmetric
+ *   ([InnerQ] methodology 2); the first sink_tokens tokens and the R most
+ *   recent tokens stay fp16 ([InnerQ] methodology 4), the recent ones as a
+ *   FIFO window whose oldest token is quantized when a push makes it exceed
+ *   R.  Requires v_policy == KVQ_V_FIFO. */
+typedef enum { KVQ_SCHEME_KIVI = 0, KVQ_SCHEME_INNERQ = 1 } kvq_scheme;
+
 /* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
- * plus the attention shape.  Constraints: bits in {2,4}; residual > 0 and
- * residual % group == 0 ([KIVI] how it works); head_dim % group == 0;
- * group * bits % 32 == 0; num_q_heads % num_kv_heads == 0;
- * max_tokens > 0 and max_tokens % residual == 0. */
+ * plus the attention shape and the scheme.  Constraints: bits in {2,4};
+ * head_dim % group == 0; group * bits % 32 == 0; num_q_heads % num_kv_heads
+ * == 0; residual > 0; max_tokens > 0.  KVQ_SCHEME_KIVI also needs residual %
+ * group == 0 ([KIVI] how it works), max_tokens % residual == 0 and
+ * sink_tokens == 0; KVQ_SCHEME_INNERQ needs sink_tokens >= 0 and v_policy ==
+ * KVQ_V_FIFO. */
 typedef struct {
   int32_t bits;
   int32_t group;        /* G */
@@ -86,17 +119,23 @@ typedef struct {
   int32_t head_dim;
   int32_t max_tokens;   /* capacity per unit, prompt plus generated tokens */
   int32_t v_policy;     /* kvq_v_policy */
+  int32_t scheme;       /* kvq_scheme */
+  int32_t sink_tokens;  /* KVQ_SCHEME_INNERQ: leading tokens kept fp16 */
 } kvq_config;
 
-/* Byte sizes of the eight caller-allocated device buffers of one cache. */
+/* Byte sizes of the caller-allocated device buffers of one cache (k_sink and
+ * v_sink are 0 unless sink_tokens > 0). */
 typedef struct {
-  size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid;
+  size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, k_sink, v_sink;
 } kvq_layout;
 
 /* One layer's cache: caller-owned device buffers (sized by kvq_layout_bytes)
  * and host counters.  Zero-initialize the struct, set the pointers, and leave
- * the counters to the library.  n_tokens = tokens cached; nq_k / nq_v = tokens
- * in the quantized key / value part; started = prefill has run. */
+ * the counters to the library.  n_tokens = tokens cached; nq_k / nq_v = end of
+ * the quantized key / value tokens (KIVI: [0, nq); InnerQ: [sink_tokens, nq)
+ * with nq_k == nq_v, and nq == n_tokens while n_tokens <= sink_tokens);
+ * started = prefill has run.  k_sink / v_sink may be null when sink_tokens
+ * is 0. */
 typedef struct {
   uint32_t *k_codes;
   float *k_scale;
@@ -106,11 +145,14 @@ typedef struct {
   int16_t *v_zero;
   uint16_t *k_resid;
   uint16_t *v_resid;
+  uint16_t *k_sink;
+  uint16_t *v_sink;
   int64_t n_tokens;
   int64_t nq_k;
   int64_t nq_v;
   int32_t started;
-  int32_t flushes;      /* key-residual flushes performed since prefill */
+  int32_t flushes;      /* KIVI: key-residual flushes since prefill; InnerQ:
+                           appends that quantized a token leaving the window */
 } kvq_cache;
 
 /* Validates cfg and fills *out with the buffer sizes.  Host only. */
@@ -130,20 +172,26 @@ size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t spli
 /* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
  * device [batch][num_kv_heads][len][head_dim], read only (the full-precision
  * tensors stay valid for the caller, as the page's prefill paragraph
- * requires).  The first len - (len mod R) tokens are quantized, keys per
- * channel over groups of G tokens and values per token over groups of G
+ * requires).  KIVI: the first len - (len mod R) tokens are quantized, keys
+ * per channel over groups of G tokens and values per token over groups of G
  * channels; the last len mod R tokens go to the residual ring.  With
- * KVQ_V_FIFO the last min(len, R) values stay fp16 instead.  Needs a cache
- * with started == 0 and len <= max_tokens; len == 0 is allowed. */
+ * KVQ_V_FIFO the last min(len, R) values stay fp16 instead.  InnerQ: tokens
+ * t < sink_tokens go to the sink rows, the last min(R, len - sink_tokens)
+ * to the window, the rest are quantized.  Needs a cache with started == 0
+ * and len <= max_tokens; len == 0 is allowed. */
 kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache,
                                 const uint16_t *k, const uint16_t *v, int64_t len,
                                 hipStream_t stream);
 
 /* One decode step's new key and value, fp16 device [batch][num_kv_heads]
- * [head_dim], written to residual slot n mod R; n += 1.  When the key
+ * [head_dim]; n += 1.  KIVI: written to residual slot n mod R; when the key
  * residual reaches R tokens it is quantized and appended to the grouped part
  * in the same call (eager flush, [KIVI] how it works; [HFQ] 3.1); values
- * follow the cache's kvq_v_policy.  Needs started and n < max_tokens. */
+ * follow the cache's kvq_v_policy.  InnerQ: token n < sink_tokens goes to
+ * sink row n; otherwise, when the window already holds R tokens its oldest
+ * token (ring slot nq mod R) is quantized into row nq first, and the new
+ * token takes ring slot n mod R; one kernel launch.  Needs started and
+ * n < max_tokens. */
 kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
                             const uint16_t *k_new, const uint16_t *v_new,
                             hipStream_t stream);
@@ -165,10 +213,10 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
 
 /* One decode step: kvq_append_token(k_new, v_new) followed by
  * kvq_decode_attention(q) with the same results, but as a single kernel
- * launch whenever the append needs no flush and the cache uses the chunked
+ * launch whenever a KIVI append needs no flush and the cache uses the chunked
  * value residual: the attention kernel reads the new token from k_new/v_new
- * and stores it into its residual slot.  Otherwise it runs the two calls in
- * sequence.  Arguments and requirements are those of the two calls; on a
+ * and stores it into its residual slot.  Otherwise (and always for InnerQ)
+ * it runs the two calls in sequence.  Arguments and requirements are those of the two calls; on a
  * validation failure nothing is enqueued and the cache is unchanged. */
 kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,

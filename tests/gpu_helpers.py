@@ -22,6 +22,45 @@ def make_cache(bits, G, R, B, Hq, Hkv, cap, policy=kvq.KVQ_V_CHUNK, d=128):
     return cfg, kvq.KVCache(cfg, "cuda")
 
 
+def make_innerq_cache(bits, G, R, S, B, Hq, Hkv, cap, d=128):
+    cfg = kvq.make_innerq_config(bits, G, R, S, B, Hq, Hkv, d, cap)
+    return cfg, kvq.KVCache(cfg, "cuda")
+
+
+def compare_innerq_unit(cache, ref, b, h, rb=None, rh=None):
+    """Bit-exact comparison of one unit's live bytes of an InnerQ-style cache:
+    quantized rows [sinks, nq), the sink rows present and the window slots."""
+    rb = b if rb is None else rb
+    rh = h if rh is None else rh
+    bufs = ref.buffers(cache.cfg.max_tokens)
+    assert (cache.n_tokens, cache.nq_k, cache.nq_v) == (ref.n, ref.nq, ref.nq)
+    T = cache.tensors
+    rows = np.s_[ref.S:ref.nq] if ref.n > ref.S else np.s_[0:0]
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        got = host(T[name][b, h][rows])
+        if name.endswith("codes"):
+            got = got.view(np.uint32)
+        want = bufs[name][rb, rh][rows]
+        if not np.array_equal(got, want):
+            bad = np.argwhere(got != want)
+            raise AssertionError(f"{name} unit ({b},{h}) differs at {bad[:5].tolist()} ({len(bad)} entries)")
+    ns = min(ref.n, ref.S)
+    for name in ("k_sink", "v_sink"):
+        got = host(T[name][b, h][:ns]).view(np.uint16)
+        assert np.array_equal(got, bufs[name][rb, rh][:ns].view(np.uint16)), name
+    slots, _ = ref.live_resid_slots()
+    for name in ("k_resid", "v_resid"):
+        if slots:
+            got = host(T[name][b, h][slots]).view(np.uint16)
+            assert np.array_equal(got, bufs[name][rb, rh][slots].view(np.uint16)), name
+
+
+def compare_innerq_buffers(cache, ref):
+    for b in range(ref.B):
+        for h in range(ref.H):
+            compare_innerq_unit(cache, ref, b, h)
+
+
 def compare_unit_buffers(cache, ref, b, h, rb=None, rh=None):
     """Bit-exact comparison of one unit's live cache bytes.
 

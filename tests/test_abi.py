@@ -43,6 +43,56 @@ def cfg(**kw):
     return kvq.make_config(**base)
 
 
+def iq_cfg(**kw):
+    base = dict(bits=4, group=64, residual=32, batch=4, num_q_heads=32, num_kv_heads=32,
+                head_dim=128, max_tokens=1000, v_policy=kvq.KVQ_V_FIFO, scheme=kvq.KVQ_SCHEME_INNERQ,
+                sink_tokens=4)
+    base.update(kw)
+    return kvq.make_config(**base)
+
+
+_STRUCT_PROBE = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "kvq.h"
+#define F(T, m) printf(#T "." #m " %zu %zu\n", offsetof(T, m), sizeof(((T *)0)->m));
+int main(void) {
+  printf("kvq_config %zu\nkvq_layout %zu\nkvq_cache %zu\n", sizeof(kvq_config), sizeof(kvq_layout),
+         sizeof(kvq_cache));
+  F(kvq_config, scheme) F(kvq_config, sink_tokens) F(kvq_layout, k_sink) F(kvq_layout, v_sink)
+  F(kvq_cache, k_sink) F(kvq_cache, v_sink) F(kvq_cache, n_tokens) F(kvq_cache, flushes)
+  return 0;
+}
+"""
+
+
+def test_ctypes_structs_match_the_c_header(tmp_path):
+    """Compiles a probe against include/kvq.h with the host C compiler and
+    compares struct sizes and field offsets with the binding's ctypes view."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "probe.c"
+    src.write_text(_STRUCT_PROBE)
+    exe = tmp_path / "probe"
+    subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in filter(None, out):
+        parts = line.split()
+        got[parts[0]] = tuple(int(x) for x in parts[1:])
+    T = {"kvq_config": kvq.kvq_config, "kvq_layout": kvq.kvq_layout, "kvq_cache": kvq.kvq_cache}
+    for name, ty in T.items():
+        assert got[name] == (ctypes.sizeof(ty),), name
+    for key, (off, size) in ((k, v) for k, v in got.items() if "." in k):
+        tname, field = key.split(".")
+        desc = getattr(T[tname], field)
+        assert (desc.offset, desc.size) == (off, size), key
+
+
 def test_layout_bytes_follow_the_documented_layout(lib):
     c = cfg()
     lay = kvq.kvq_layout_bytes(c)
@@ -56,6 +106,63 @@ def test_layout_bytes_follow_the_documented_layout(lib):
     assert lay.k_resid == lay.v_resid == units * R * d * 2
     lay4 = kvq.kvq_layout_bytes(cfg(bits=4, group=64))
     assert lay4.k_codes == units * cap * (d * 4 // 32) * 4
+
+
+def test_innerq_layout_bytes(lib):
+    c = iq_cfg()
+    lay = kvq.kvq_layout_bytes(c)
+    units, cap, d, G, R, S = 4 * 32, 1000, 128, 64, 32, 4
+    assert lay.k_codes == lay.v_codes == units * cap * (d * 4 // 32) * 4
+    assert lay.k_scale == lay.v_scale == units * cap * (d // G) * 4
+    assert lay.k_zero == lay.v_zero == units * cap * (d // G) * 2
+    assert lay.k_resid == lay.v_resid == units * R * d * 2
+    assert lay.k_sink == lay.v_sink == units * S * d * 2
+    assert kvq.kvq_layout_bytes(cfg()).k_sink == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(v_policy=kvq.KVQ_V_CHUNK), kvq.KVQ_ERR_ARG),
+    (dict(sink_tokens=-1), kvq.KVQ_ERR_ARG),
+    (dict(residual=0), kvq.KVQ_ERR_ARG),
+    (dict(scheme=2), kvq.KVQ_ERR_ARG),
+    (dict(group=48), kvq.KVQ_ERR_ARG),
+    (dict(sink_tokens=513), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(max_tokens=(1 << 25) + 1), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(residual=513), kvq.KVQ_ERR_UNSUPPORTED),
+])
+def test_invalid_innerq_configs_are_rejected(lib, bad, status):
+    c = iq_cfg(**bad)
+    out = kvq.kvq_layout()
+    assert lib.kvq_layout_bytes(ctypes.byref(c), ctypes.byref(out)) == status
+    assert lib.kvq_last_error().decode() != ""
+
+
+def test_innerq_relaxes_the_kivi_multiples(lib):
+    # window not a multiple of G, capacity not a multiple of the window
+    for kw in (dict(residual=20), dict(max_tokens=1001), dict(sink_tokens=0), dict(bits=2, group=32)):
+        out = kvq.kvq_layout()
+        assert lib.kvq_layout_bytes(ctypes.byref(iq_cfg(**kw)), ctypes.byref(out)) == kvq.KVQ_OK, kw
+    # sinks are an InnerQ feature here
+    out = kvq.kvq_layout()
+    assert lib.kvq_layout_bytes(ctypes.byref(cfg(sink_tokens=4)), ctypes.byref(out)) == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_innerq_null_sink_buffers_are_rejected(lib):
+    c = iq_cfg()
+    cache = _fake_cache()
+    assert lib.kvq_quantize_prefill(ctypes.byref(c), ctypes.byref(cache), 1, 1, 10, None) == kvq.KVQ_ERR_ARG
+    assert "sink" in lib.kvq_last_error().decode()
+    assert cache.started == 0
+
+
+def test_innerq_split_sizing_is_monotone(lib):
+    c = iq_cfg(max_tokens=200000)
+    prev = 0
+    for n in list(range(0, 5000, 37)) + [131072, 199999]:
+        cur = kvq.kvq_auto_splits(c, n)
+        assert 1 <= cur <= 64 and cur >= prev
+        prev = cur
+    assert kvq.kvq_auto_splits(c, 131072) == 4   # 128 units: two 8-wave workgroups per CU
 
 
 @pytest.mark.parametrize("bad,status", [

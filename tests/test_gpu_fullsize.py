@@ -10,7 +10,7 @@ import torch
 import decode_attention_token_amd as kvq
 import oracle
 from workloads import GQA_LONG, LLAMA7B_2BIT, LLAMA7B_4BIT, LONG_4BIT, gen_new_tokens, gen_prefill, gen_queries
-from gpu_helpers import ATOL, compare_unit_buffers, host
+from gpu_helpers import ATOL, compare_innerq_unit, compare_unit_buffers, host
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def test_fullsize_sampled_parity(w):
     kn, vn = gen_new_tokens(w, 0, "cuda", steps=1)
     q = gen_queries(w, 0, "cuda", steps=1)[0].contiguous()
     cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim, w.max_tokens, w.v_policy)
+                          w.head_dim, w.max_tokens, w.v_policy, w.scheme, w.sinks)
     cache = kvq.KVCache(cfg, "cuda")
     cache.prefill(k, v)
     cache.append(kn[0].contiguous(), vn[0].contiguous())
@@ -40,10 +40,16 @@ def test_fullsize_sampled_parity(w):
     worst = 0.0
     for u in _sample_units(w):
         b, h = divmod(u, w.num_kv_heads)
-        ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+        else:
+            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
         ref.prefill(host(k[b:b + 1, h:h + 1]), host(v[b:b + 1, h:h + 1]))
         ref.append(host(kn[0][b:b + 1, h:h + 1]), host(vn[0][b:b + 1, h:h + 1]))
-        compare_unit_buffers(cache, ref, b, h, 0, 0)
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            compare_innerq_unit(cache, ref, b, h, 0, 0)
+        else:
+            compare_unit_buffers(cache, ref, b, h, 0, 0)
         K, V = ref.dequantized()
         qh = host(q[b:b + 1, h * hpg:(h + 1) * hpg])
         want = oracle.attention(qh, K, V, scale)

@@ -46,6 +46,8 @@ class Workload:
     steps: int            # decode steps the workload runs
     layers: int           # distinct layer caches the workload cycles through
     v_policy: int = 0     # 0 chunked residual, 1 FIFO value queue
+    scheme: int = 0       # 0 KIVI-style, 1 InnerQ-style (R is then the recent window)
+    sinks: int = 0        # InnerQ-style: leading tokens kept fp16
 
     @property
     def units(self) -> int:
@@ -64,7 +66,9 @@ class Workload:
 
 # The five workloads: a tiny one the oracle finishes in well under a second,
 # the Llama-2-7B-layer-shaped 2-bit decode, a 4-bit variant, a grouped-query
-# long-context case and a long-context 4-bit case.
+# long-context case and a long-context 4-bit InnerQ-style case (groups of 64
+# channels per token for keys and values, 4 sink and 32 recent fp16 tokens,
+# as in the euno.news InnerQ summary, methodology 1 and 4).
 TINY = Workload("tiny-b1-h1-L256-2bit-G32-R32", 1, 1, 1, 1, 128, 256, 2, 32, 32, 4, 10.0, 1, 1)
 LLAMA7B_2BIT = Workload("llama2-7b-layer-b16-h32-L4096-2bit-G32-R128", 2, 16, 32, 32, 128, 4096,
                         2, 32, 128, 3, 8.0, 64, 32)
@@ -72,8 +76,8 @@ LLAMA7B_4BIT = Workload("b64-h32-L8192-4bit-G64-R128", 3, 64, 32, 32, 128, 8192,
                         3, 8.0, 128, 1)
 GQA_LONG = Workload("gqa-b8-q32-kv8-L32768-2bit-G32-R128", 4, 8, 32, 8, 128, 32768, 2, 32, 128,
                     4, 10.0, 1, 8)
-LONG_4BIT = Workload("b4-h32-L131072-4bit-G64-R128", 5, 4, 32, 32, 128, 131072, 4, 64, 128,
-                     4, 10.0, 1, 1)
+LONG_4BIT = Workload("innerq-b4-h32-L131072-4bit-G64-S4-W32", 5, 4, 32, 32, 128, 131072, 4, 64, 32,
+                     4, 10.0, 1, 1, v_policy=1, scheme=1, sinks=4)
 
 WORKLOADS = {w.config_id: w for w in (TINY, LLAMA7B_2BIT, LLAMA7B_4BIT, GQA_LONG, LONG_4BIT)}
 
