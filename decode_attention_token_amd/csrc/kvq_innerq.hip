@@ -160,19 +160,23 @@ __global__ __launch_bounds__(64) void innerq_append_kernel(CacheView c, const ui
 }
 
 // ---------------------------------------------------------------- attention
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
 template <int WPL>
 struct IqBuf {
   uint32_t kw[WPL];
   uint32_t vw[WPL];
   float ks, vs;       // this lane's key / value group scales
-  uint32_t kz, vz;    // their int16 zero-points (low half)
+  ushort2_t z;        // their int16 zero-points (x keys, y values), one register
 };
 
 // One workgroup of 8 waves per (split, unit).  The quantized tokens
-// [t0, nq) (t0 = number of sink tokens present) are cut into steps of TPS
-// tokens; each split takes a contiguous range of steps and each wave a
-// contiguous sub-range.  Lanes of a token past nq score -inf.  The last split
-// also takes the fp16 tokens: the sinks and the window [nq, n).
+// [t0, nq) (t0 = number of sink tokens present) are covered by steps of TPS
+// tokens that start on multiples of TPS, so every step's metadata read is a
+// whole aligned run of cache lines; each split takes a contiguous range of
+// steps and each wave a contiguous sub-range.  Lanes of a token outside
+// [t0, nq) score -inf.  The last split also takes the fp16 tokens: the sinks
+// and the window [nq, n).
 template <int BITS, int GS, int HPG, int LPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
 void innerq_attn_kernel(AttnArgs a) {
@@ -200,7 +204,8 @@ void innerq_attn_kernel(AttnArgs a) {
   const int64_t nsink = a.n < S ? a.n : S;   // sink tokens present
   const int64_t t0 = nsink;                  // first quantized token
   const int64_t nq = a.nq_k;                 // end of the quantized tokens
-  const int tsteps = (int)((nq - t0 + TPS - 1) / TPS);
+  const int64_t tb0 = t0 - t0 % TPS;         // first step start, aligned
+  const int tsteps = nq > t0 ? (int)((nq - tb0 + TPS - 1) / TPS) : 0;
   const int s0 = (int)((int64_t)tsteps * split / a.splits);
   const int s1 = (int)((int64_t)tsteps * (split + 1) / a.splits);
   const int ws0 = s0 + (s1 - s0) * wave / kWaves;
@@ -238,21 +243,24 @@ void innerq_attn_kernel(AttnArgs a) {
 
   auto load = [&](Buf &bf, int s) {
     s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
-    const uint32_t tb = (uint32_t)(t0 + (int64_t)(ws0 + s) * TPS);   // first token of the step
+    const uint32_t tb = (uint32_t)(tb0 + (int64_t)(ws0 + s) * TPS);   // first token of the step
     const uint32_t vc = code_lane + tb * (W * 4);
     const uint32_t vm = meta_lane + tb * NG;
     bload_words<WPL>(rkc, vc, 0, bf.kw);
     bload_words<WPL>(rvc, vc, 0, bf.vw);
     bf.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, vm * 4, 0, kStream));
     bf.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, vm * 4, 0, kStream));
-    bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, vm * 2, 0, kStream);
-    bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, vm * 2, 0, kStream);
+    // a step's zero-points fill half a cache line; the next step reads the
+    // other half, so these loads keep the default caching
+    bf.z.x = __builtin_amdgcn_raw_buffer_load_b16(rkz, vm * 2, 0, 0);
+    bf.z.y = __builtin_amdgcn_raw_buffer_load_b16(rvz, vm * 2, 0, 0);
   };
 
   auto process = [&](const Buf &bf, int s) {
-    const bool valid = t0 + (int64_t)(ws0 + s) * TPS + tl < nq;
-    const float kz = (float)(int16_t)(bf.kz & 0xffffu);
-    const float vz = (float)(int16_t)(bf.vz & 0xffffu);
+    const int64_t tok = tb0 + (int64_t)(ws0 + s) * TPS + tl;
+    const bool valid = tok >= t0 && tok < nq;   // rows outside may hold any bits
+    const float kz = (float)(int16_t)bf.z.x;
+    const float vz = (float)(int16_t)bf.z.y;
     float sc[HPG], d1[HPG];
 #pragma unroll
     for (int h = 0; h < HPG; ++h) sc[h] = d1[h] = 0.0f;
@@ -275,7 +283,7 @@ void innerq_attn_kernel(AttnArgs a) {
       const float sv = block_sum<LPT>(bf.ks * fmaf(kz, qsum[h], sc[h] + d1[h]));
       p[h] = o.weight(h, valid ? sv : -INFINITY);
     }
-    const float vs = valid ? bf.vs : 0.0f;   // rows past nq may hold any bits
+    const float vs = valid ? bf.vs : 0.0f;
 #pragma unroll
     for (int h = 0; h < HPG; ++h) o.bias[h][0] = fmaf(p[h] * vs, vz, o.bias[h][0]);
 #pragma unroll
