@@ -346,8 +346,13 @@ void decode_attn_kernel(AttnArgs a) {
 
   if (nsteps > 0) {
     Buf A, B, C;
+    // the two prologue batches must be issued in order: the compiler's wait
+    // counts are merged over the loop entry, and interleaved prologue loads
+    // would make every step wait for the step after it as well
     load(A, 0);
+    asm volatile("" ::: "memory");
     load(B, 1);
+    asm volatile("" ::: "memory");
     for (int s = 0; s < nsteps; s += 3) {
       load(C, s + 2);
       process(A, s);

@@ -71,6 +71,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_of(v, 0), lane_of(v, 16)), fmaxf(lane_of(v, 32), lane_of(v, 48)));
 }
 
+// A wave-uniform value moved to a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -230,8 +235,8 @@ struct Online {
     if (__any(sv > mthr[h])) {
       const float mn = fmaxf(m[h], wave_max(sv));
       const float f = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      mthr[h] = mn + kMargin;
+      m[h] = uniform(mn);   // wave-uniform: kept in scalar registers
+      mthr[h] = uniform(mn + kMargin);
       lsum[h] *= f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[h][i] *= f;

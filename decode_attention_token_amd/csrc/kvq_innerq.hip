@@ -160,14 +160,12 @@ __global__ __launch_bounds__(64) void innerq_append_kernel(CacheView c, const ui
 }
 
 // ---------------------------------------------------------------- attention
-typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
-
 template <int WPL>
 struct IqBuf {
   uint32_t kw[WPL];
   uint32_t vw[WPL];
   float ks, vs;       // this lane's key / value group scales
-  ushort2_t z;        // their int16 zero-points (x keys, y values), one register
+  uint32_t kz, vz;    // their int16 zero-points (low half)
 };
 
 // One workgroup of 8 waves per (split, unit).  The quantized tokens
@@ -206,6 +204,7 @@ void innerq_attn_kernel(AttnArgs a) {
   const int64_t nq = a.nq_k;                 // end of the quantized tokens
   const int64_t tb0 = t0 - t0 % TPS;         // first step start, aligned
   const int tsteps = nq > t0 ? (int)((nq - tb0 + TPS - 1) / TPS) : 0;
+  const int t0i = (int)t0, tb0i = (int)tb0, nqi = (int)nq;
   const int s0 = (int)((int64_t)tsteps * split / a.splits);
   const int s1 = (int)((int64_t)tsteps * (split + 1) / a.splits);
   const int ws0 = s0 + (s1 - s0) * wave / kWaves;
@@ -252,15 +251,15 @@ void innerq_attn_kernel(AttnArgs a) {
     bf.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, vm * 4, 0, kStream));
     // a step's zero-points fill half a cache line; the next step reads the
     // other half, so these loads keep the default caching
-    bf.z.x = __builtin_amdgcn_raw_buffer_load_b16(rkz, vm * 2, 0, 0);
-    bf.z.y = __builtin_amdgcn_raw_buffer_load_b16(rvz, vm * 2, 0, 0);
+    bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, vm * 2, 0, 0);
+    bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, vm * 2, 0, 0);
   };
 
   auto process = [&](const Buf &bf, int s) {
-    const int64_t tok = tb0 + (int64_t)(ws0 + s) * TPS + tl;
-    const bool valid = tok >= t0 && tok < nq;   // rows outside may hold any bits
-    const float kz = (float)(int16_t)bf.z.x;
-    const float vz = (float)(int16_t)bf.z.y;
+    const int tok = tb0i + (ws0 + s) * TPS + tl;   // token indices fit 32 bits (capacity <= 2^25)
+    const bool valid = tok >= t0i && tok < nqi;  // rows outside may hold any bits
+    const float kz = (float)(int16_t)(bf.kz & 0xffffu);
+    const float vz = (float)(int16_t)(bf.vz & 0xffffu);
     float sc[HPG], d1[HPG];
 #pragma unroll
     for (int h = 0; h < HPG; ++h) sc[h] = d1[h] = 0.0f;
@@ -301,8 +300,13 @@ void innerq_attn_kernel(AttnArgs a) {
 
   if (nsteps > 0) {
     Buf A, B, C;
+    // the two prologue batches must be issued in order: the compiler's wait
+    // counts are merged over the loop entry, and interleaved prologue loads
+    // would make every step wait for the step after it as well
     load(A, 0);
+    asm volatile("" ::: "memory");
     load(B, 1);
+    asm volatile("" ::: "memory");
     for (int s = 0; s < nsteps; s += 3) {
       load(C, s + 2);
       process(A, s);
