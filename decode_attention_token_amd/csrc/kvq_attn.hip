@@ -54,7 +54,7 @@ struct Geo {
   static constexpr int NVG = CPL >= GS ? CPL / GS : 1;   // value groups per lane
   static constexpr int VGR = kHeadDim / GS;              // value groups per row
   static constexpr int SPG = GS / TPS;                   // wave steps per key group
-  static constexpr int RED = kRedFloats<LPT>;
+  static constexpr int RED = kRedFloats<HPG>;
   static constexpr int QPW = HPG * (kHeadDim + 8);                // per wave: q'[HPG][128], beta[HPG][8]
   static constexpr int QP = kWaves * QPW;
   static constexpr int TAIL = HPG * kMaxTail + kParts * HPG * kHeadDim;
@@ -354,6 +354,7 @@ void decode_attn_kernel(AttnArgs a) {
     load(B, 1);
     asm volatile("" ::: "memory");
     for (int s = 0; s < nsteps; s += 3) {
+      progress_priority(nsteps - s, nsteps);
       load(C, s + 2);
       process(A, s);
       load(A, s + 3);

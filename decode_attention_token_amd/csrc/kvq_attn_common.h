@@ -71,6 +71,19 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_of(v, 0), lane_of(v, 16)), fmaxf(lane_of(v, 32), lane_of(v, 48)));
 }
 
+// Issue priority from progress: the SIMD arbiter favours the oldest waves,
+// so with equal shares of work the younger waves (and the second workgroup
+// on a compute unit) would finish well after the older ones.  A wave with
+// more of its steps left gets a higher priority, so all waves finish close
+// together.  `left` and `total` are wave-uniform step counts.
+__device__ __forceinline__ void progress_priority(int left, int total) {
+  const int band = (4 * left) / (total + 1);
+  if (band >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (band == 2) __builtin_amdgcn_s_setprio(2);
+  else if (band == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // A wave-uniform value moved to a scalar register.
 __device__ __forceinline__ float uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
@@ -197,10 +210,10 @@ __device__ void finish_part(const AttnArgs &a, int unit, int part, const Stage &
 template <int HPG>
 constexpr int kWavesPerEU = HPG == 1 ? 4 : 2;
 
-// Floats of the LDS area combine_waves uses: one padded row per token lane
-// group of every wave, then kParts partial rows.
-template <int LPT>
-constexpr int kRedFloats = kWaves * (kWave / LPT) * (kHeadDim + 4) + kParts * kHeadDim;
+// Floats of the LDS area combine_waves uses: one row of 128 channel sums per
+// wave and query head.
+template <int HPG>
+constexpr int kRedFloats = kWaves * HPG * kHeadDim;
 
 // Floats of the Stage area after the work area.
 template <int HPG>
@@ -289,73 +302,79 @@ __device__ __forceinline__ void fp16_token(Online<HPG, CPL, NVG> &o, const float
   }
 }
 
+// Sum over the TPS = 64 / LPT token lanes that share channel slice j (lanes
+// tl * LPT + j): rotates within 16-lane rows, then the row swaps of gfx950
+// (odd/even rows, then the two 32-lane halves).  Every lane gets the total
+// of its slice.
+template <int LPT>
+__device__ __forceinline__ float sum_token_lanes(float v) {
+  static_assert(LPT == 4 || LPT == 8, "token lanes per row");
+  if constexpr (LPT == 4) v += dpp<0x128>(v);   // row_ror:8
+  v += dpp<LPT == 4 ? 0x124 : 0x128>(v);        // row_ror:4 (LPT 4) or row_ror:8 (LPT 8)
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Combines the waves of a workgroup and the token lanes of each wave into
 // st.acc[h][128] (unnormalized, relative to the workgroup maximum) and
 // st.ml[h] = (max, sum).  o.acc holds sums of weight * code * U per channel
-// and o.bias the zero-point terms per value group; inv_u = 1 / U.  Ends with
-// a barrier; smem must hold kRedFloats<LPT> floats before the Stage area.
+// and o.bias the zero-point terms per value group; inv_u = 1 / U.  Each wave
+// first sums over its token lanes in registers and stores one row per head;
+// after one barrier, thread (h, c) merges the waves' rows with their
+// 2^(m_w - M) factors.  Ends with a barrier; smem must hold
+// kRedFloats<HPG> floats before the Stage area.
 template <int HPG, int LPT, int NVG>
 __device__ __forceinline__ void combine_waves(const Online<HPG, kHeadDim / LPT, NVG> &o, float *smem,
                                               const Stage &st, int wave, int lane, float inv_u) {
-  constexpr int CPL = kHeadDim / LPT, TPS = kWave / LPT, RS = kHeadDim + 4;
-  const int tid = threadIdx.x, j = lane % LPT, tl = lane / LPT;
-  float lw[HPG];
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) lw[h] = wave_sum(o.lsum[h]) * (1.0f / LPT);
-  __syncthreads();   // every wave is done with the work area
-  float *s_red = smem;                        // [kWaves*TPS][RS]
-  float *s_half = smem + kWaves * TPS * RS;   // [kParts][128]
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      st.wml[(wave * HPG + h) * 2] = o.m[h];
-      st.wml[(wave * HPG + h) * 2 + 1] = lw[h];
-    }
-  }
-  __syncthreads();
+  constexpr int CPL = kHeadDim / LPT;
+  const int tid = threadIdx.x, j = lane % LPT;
+  float *rows = smem;   // [kWaves][HPG][128]
+  __syncthreads();      // every wave is done with the work area
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
-    float M = -INFINITY;
+    const float lw = wave_sum(o.lsum[h]) * (1.0f / LPT);
+    float bsum[NVG];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.wml[(w * HPG + h) * 2]);
-    const float fw = (o.m[h] == -INFINITY) ? 0.0f : exp2f(o.m[h] - M);
-    float *row = s_red + (wave * TPS + tl) * RS + j * CPL;
+    for (int k = 0; k < NVG; ++k) bsum[k] = sum_token_lanes<LPT>(o.bias[h][k]);
+    float *row = rows + (wave * HPG + h) * kHeadDim + j * CPL;
 #pragma unroll
     for (int i = 0; i < CPL; i += 4) {
       const int k0 = (NVG > 1) ? (i / (CPL / NVG)) : 0;
       float4 v;
-      v.x = fmaf(o.acc[h][i], inv_u, o.bias[h][k0]) * fw;
-      v.y = fmaf(o.acc[h][i + 1], inv_u, o.bias[h][k0]) * fw;
-      v.z = fmaf(o.acc[h][i + 2], inv_u, o.bias[h][k0]) * fw;
-      v.w = fmaf(o.acc[h][i + 3], inv_u, o.bias[h][k0]) * fw;
-      *reinterpret_cast<float4 *>(row + i) = v;
+      v.x = fmaf(sum_token_lanes<LPT>(o.acc[h][i]), inv_u, bsum[k0]);
+      v.y = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 1]), inv_u, bsum[k0]);
+      v.z = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 2]), inv_u, bsum[k0]);
+      v.w = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 3]), inv_u, bsum[k0]);
+      if (lane < LPT) *reinterpret_cast<float4 *>(row + i) = v;
     }
-    __syncthreads();
-    {
-      const int c = tid & (kHeadDim - 1), half = tid >> 7;
-      float sum = 0.0f;
-      for (int r = half; r < kWaves * TPS; r += kParts) sum += s_red[r * RS + c];
-      s_half[half * kHeadDim + c] = sum;
+    if (lane == 0) {
+      st.wml[(wave * HPG + h) * 2] = o.m[h];
+      st.wml[(wave * HPG + h) * 2 + 1] = lw;
     }
-    __syncthreads();
-    if (tid < kHeadDim) {
-      float t = 0.0f;
-#pragma unroll
-      for (int p = 0; p < kParts; ++p) t += s_half[p * kHeadDim + tid];
-      st.acc[h * kHeadDim + tid] = t;
-      if (tid == 0) {
-        float L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = st.wml[(w * HPG + h) * 2];
-          if (mw != -INFINITY) L = fmaf(exp2f(mw - M), st.wml[(w * HPG + h) * 2 + 1], L);
-        }
-        st.ml[2 * h] = M;
-        st.ml[2 * h + 1] = L;
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  for (int i = tid; i < HPG * kHeadDim; i += blockDim.x) {
+    const int h = i / kHeadDim, c = i % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.wml[(w * HPG + h) * 2]);
+    float acc = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = st.wml[(w * HPG + h) * 2];
+      const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      L = fmaf(f, st.wml[(w * HPG + h) * 2 + 1], L);
+      acc = fmaf(f, rows[(w * HPG + h) * kHeadDim + c], acc);
+    }
+    st.acc[i] = acc;
+    if (c == 0) {
+      st.ml[2 * h] = M;
+      st.ml[2 * h + 1] = L;
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace

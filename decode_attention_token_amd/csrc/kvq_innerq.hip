@@ -187,8 +187,8 @@ void innerq_attn_kernel(AttnArgs a) {
   static_assert(WPL >= 1, "lane slice must hold whole words");
   using Buf = IqBuf<WPL>;
 
-  __shared__ __attribute__((aligned(16))) float smem[kRedFloats<LPT> + kStageFloats<HPG>];
-  const Stage st = stage_of<HPG>(smem, kRedFloats<LPT>);
+  __shared__ __attribute__((aligned(16))) float smem[kRedFloats<HPG> + kStageFloats<HPG>];
+  const Stage st = stage_of<HPG>(smem, kRedFloats<HPG>);
 
   const int units = a.batch * a.hkv;
   const int split = blockIdx.x / units;
@@ -308,6 +308,7 @@ void innerq_attn_kernel(AttnArgs a) {
     load(B, 1);
     asm volatile("" ::: "memory");
     for (int s = 0; s < nsteps; s += 3) {
+      progress_priority(nsteps - s, nsteps);
       load(C, s + 2);
       process(A, s);
       load(A, s + 3);
