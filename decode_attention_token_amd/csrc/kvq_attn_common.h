@@ -210,10 +210,10 @@ __device__ void finish_part(const AttnArgs &a, int unit, int part, const Stage &
 template <int HPG>
 constexpr int kWavesPerEU = HPG == 1 ? 4 : 2;
 
-// Floats of the LDS area combine_waves uses: one row of 128 channel sums per
-// wave and query head.
+// Floats of the LDS area combine_waves uses: per wave and query head, one
+// row of 128 channel sums for each of the wave's four 16-lane rows.
 template <int HPG>
-constexpr int kRedFloats = kWaves * HPG * kHeadDim;
+constexpr int kRedFloats = kWaves * HPG * 4 * kHeadDim;
 
 // Floats of the Stage area after the work area.
 template <int HPG>
@@ -302,52 +302,46 @@ __device__ __forceinline__ void fp16_token(Online<HPG, CPL, NVG> &o, const float
   }
 }
 
-// Sum over the TPS = 64 / LPT token lanes that share channel slice j (lanes
-// tl * LPT + j): rotates within 16-lane rows, then the row swaps of gfx950
-// (odd/even rows, then the two 32-lane halves).  Every lane gets the total
-// of its slice.
+// Sum over the token lanes of one 16-lane row that share channel slice j
+// (lanes tl * LPT + j): rotates by 8 (and 4) within the row.  Every lane of
+// the row gets its slice's row total.
 template <int LPT>
-__device__ __forceinline__ float sum_token_lanes(float v) {
+__device__ __forceinline__ float sum_row_token_lanes(float v) {
   static_assert(LPT == 4 || LPT == 8, "token lanes per row");
-  if constexpr (LPT == 4) v += dpp<0x128>(v);   // row_ror:8
-  v += dpp<LPT == 4 ? 0x124 : 0x128>(v);        // row_ror:4 (LPT 4) or row_ror:8 (LPT 8)
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  v += dpp<0x128>(v);                       // row_ror:8
+  if constexpr (LPT == 4) v += dpp<0x124>(v);   // row_ror:4
+  return v;
 }
 
 // Combines the waves of a workgroup and the token lanes of each wave into
 // st.acc[h][128] (unnormalized, relative to the workgroup maximum) and
 // st.ml[h] = (max, sum).  o.acc holds sums of weight * code * U per channel
 // and o.bias the zero-point terms per value group; inv_u = 1 / U.  Each wave
-// first sums over its token lanes in registers and stores one row per head;
-// after one barrier, thread (h, c) merges the waves' rows with their
-// 2^(m_w - M) factors.  Ends with a barrier; smem must hold
-// kRedFloats<HPG> floats before the Stage area.
+// sums over the token lanes of each 16-lane row in registers and stores four
+// rows per head; after one barrier, four threads per channel merge the
+// waves' rows with their 2^(m_w - M) factors and sum with a quad swap.  Ends
+// with a barrier; smem must hold kRedFloats<HPG> floats before the Stage area.
 template <int HPG, int LPT, int NVG>
 __device__ __forceinline__ void combine_waves(const Online<HPG, kHeadDim / LPT, NVG> &o, float *smem,
                                               const Stage &st, int wave, int lane, float inv_u) {
   constexpr int CPL = kHeadDim / LPT;
   const int tid = threadIdx.x, j = lane % LPT;
-  float *rows = smem;   // [kWaves][HPG][128]
+  float *rows = smem;   // [kWaves][HPG][4][128]
   __syncthreads();      // every wave is done with the work area
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
     const float lw = wave_sum(o.lsum[h]) * (1.0f / LPT);
-    float bsum[NVG];
-#pragma unroll
-    for (int k = 0; k < NVG; ++k) bsum[k] = sum_token_lanes<LPT>(o.bias[h][k]);
-    float *row = rows + (wave * HPG + h) * kHeadDim + j * CPL;
+    float *row = rows + ((wave * HPG + h) * 4 + lane / 16) * kHeadDim + j * CPL;
 #pragma unroll
     for (int i = 0; i < CPL; i += 4) {
       const int k0 = (NVG > 1) ? (i / (CPL / NVG)) : 0;
+      const float b = o.bias[h][k0];
       float4 v;
-      v.x = fmaf(sum_token_lanes<LPT>(o.acc[h][i]), inv_u, bsum[k0]);
-      v.y = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 1]), inv_u, bsum[k0]);
-      v.z = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 2]), inv_u, bsum[k0]);
-      v.w = fmaf(sum_token_lanes<LPT>(o.acc[h][i + 3]), inv_u, bsum[k0]);
-      if (lane < LPT) *reinterpret_cast<float4 *>(row + i) = v;
+      v.x = sum_row_token_lanes<LPT>(fmaf(o.acc[h][i], inv_u, b));
+      v.y = sum_row_token_lanes<LPT>(fmaf(o.acc[h][i + 1], inv_u, b));
+      v.z = sum_row_token_lanes<LPT>(fmaf(o.acc[h][i + 2], inv_u, b));
+      v.w = sum_row_token_lanes<LPT>(fmaf(o.acc[h][i + 3], inv_u, b));
+      if (lane % 16 < LPT) *reinterpret_cast<float4 *>(row + i) = v;
     }
     if (lane == 0) {
       st.wml[(wave * HPG + h) * 2] = o.m[h];
@@ -355,8 +349,9 @@ __device__ __forceinline__ void combine_waves(const Online<HPG, kHeadDim / LPT, 
     }
   }
   __syncthreads();
-  for (int i = tid; i < HPG * kHeadDim; i += blockDim.x) {
-    const int h = i / kHeadDim, c = i % kHeadDim;
+  static_assert((HPG * kHeadDim * 4) % kThreads == 0, "whole merge passes");
+  for (int i = tid; i < HPG * kHeadDim * 4; i += kThreads) {
+    const int r = i % 4, c = (i / 4) % kHeadDim, h = i / (4 * kHeadDim);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.wml[(w * HPG + h) * 2]);
@@ -364,14 +359,17 @@ __device__ __forceinline__ void combine_waves(const Online<HPG, kHeadDim / LPT, 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = st.wml[(w * HPG + h) * 2];
-      const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
       L = fmaf(f, st.wml[(w * HPG + h) * 2 + 1], L);
-      acc = fmaf(f, rows[(w * HPG + h) * kHeadDim + c], acc);
+      acc = fmaf(f, rows[((w * HPG + h) * 4 + r) * kHeadDim + c], acc);
     }
-    st.acc[i] = acc;
-    if (c == 0) {
-      st.ml[2 * h] = M;
-      st.ml[2 * h + 1] = L;
+    acc = block_sum<4>(acc);   // the four rows of channel c sit in one quad
+    if (r == 0) {
+      st.acc[h * kHeadDim + c] = acc;
+      if (c == 0) {
+        st.ml[2 * h] = M;
+        st.ml[2 * h + 1] = L;
+      }
     }
   }
   __syncthreads();
