@@ -45,6 +45,10 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                          pinned: on-grid exactness (x = s*k recovers S = s and
                          the signed codes), |x - x_hat| <= S/2, asymmetric
                          groups equal quantize_groups.
+  KiviSinkCache          pinned: sinks stay exact fp16, the tokens after them
+                         match a plain cache fed the same stream, prefill(L)
+                         + appends == prefill(L+m) across the sink boundary,
+                         all-fp16 reduces to plain attention.
   InnerQCache            pinned: sinks stay exact fp16, window holds
                          min(R, n - sinks) tokens, prefill(L)+appends ==
                          prefill(L+m), all-fp16 cache reduces to plain
@@ -67,7 +71,7 @@ __all__ = [
     "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
     "attention", "kv_code_bytes_per_token", "attention_call_bytes", "flush_bytes",
     "CHUNK", "FIFO", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
-    "InnerQCache", "innerq_attention_call_bytes",
+    "InnerQCache", "innerq_attention_call_bytes", "KiviSinkCache",
 ]
 
 CHUNK = 0   # value residual flushed as a block of R tokens, like the keys ([HFQ] 3.1)
@@ -336,6 +340,83 @@ class QuantizedKVCache:
         ks = [(self.nq_k + i) % R for i in range(self.kr.shape[2])]
         vs = [(self.nq_v + i) % R for i in range(self.vr.shape[2])]
         return ks, vs
+
+
+# --------------------------------------------------------------------------- KIVI with sinks
+class KiviSinkCache:
+    """KIVI-style cache whose first `sinks` tokens stay fp16 for the life of
+    the cache (attention-sink-aware quantization: the juejin.cn KIVI/IntactKV/
+    KVQuant page, KVQuant part, section 五 -- models put large attention on
+    the first tokens, so their quantization error matters most).
+
+    The KIVI state machine of QuantizedKVCache runs unchanged on the token
+    stream after the sinks: token t >= sinks is token t - sinks of the inner
+    cache.  Counters are reported for the whole stream: n, and nq_k / nq_v =
+    end of the quantized key / value tokens, i.e. sinks + the inner counts
+    (== n while n <= sinks).
+    """
+
+    def __init__(self, bits, group, residual, sinks, batch, kv_heads, head_dim, v_policy=CHUNK):
+        if sinks < 0:
+            raise ValueError("sinks must be non-negative")
+        self.S = sinks
+        self.inner = QuantizedKVCache(bits, group, residual, batch, kv_heads, head_dim, v_policy)
+        self.bits, self.G, self.R = bits, group, residual
+        self.B, self.H, self.d = batch, kv_heads, head_dim
+        self.sink_k = np.zeros((batch, kv_heads, 0, head_dim), np.float16)
+        self.sink_v = np.zeros((batch, kv_heads, 0, head_dim), np.float16)
+
+    @property
+    def n(self):
+        return self.sink_k.shape[2] + self.inner.n
+
+    @property
+    def nq_k(self):
+        return self.n if self.n <= self.S else self.S + self.inner.nq_k
+
+    @property
+    def nq_v(self):
+        return self.n if self.n <= self.S else self.S + self.inner.nq_v
+
+    @property
+    def flushes(self):
+        return self.inner.flushes
+
+    def prefill(self, k, v):
+        k = np.asarray(k, np.float16)
+        v = np.asarray(v, np.float16)
+        ns = min(k.shape[2], self.S)
+        self.inner.prefill(k[:, :, ns:], v[:, :, ns:])
+        self.sink_k, self.sink_v = k[:, :, :ns].copy(), v[:, :, :ns].copy()
+
+    def append(self, k_new, v_new):
+        if not self.inner.started:
+            raise RuntimeError("append before prefill")
+        if self.n < self.S:
+            self.sink_k = np.concatenate([self.sink_k, np.asarray(k_new, np.float16)[:, :, None]], axis=2)
+            self.sink_v = np.concatenate([self.sink_v, np.asarray(v_new, np.float16)[:, :, None]], axis=2)
+        else:
+            self.inner.append(k_new, v_new)
+
+    def dequantized(self):
+        K, V = self.inner.dequantized()
+        return (np.concatenate([self.sink_k.astype(_F32), K], axis=2),
+                np.concatenate([self.sink_v.astype(_F32), V], axis=2))
+
+    def buffers(self, max_tokens):
+        """Device layout: the inner cache's buffers (token t >= sinks at row /
+        ring slot of inner token t - sinks) plus k_sink / v_sink f16
+        [B,H,sinks,d] holding sink t at row t."""
+        out = self.inner.buffers(max_tokens)
+        ks = np.zeros((self.B, self.H, self.S, self.d), np.float16)
+        vs = np.zeros_like(ks)
+        ns = self.sink_k.shape[2]
+        ks[:, :, :ns], vs[:, :, :ns] = self.sink_k, self.sink_v
+        out["k_sink"], out["v_sink"] = ks, vs
+        return out
+
+    def live_resid_slots(self):
+        return self.inner.live_resid_slots()
 
 
 # --------------------------------------------------------------------------- InnerQ-style
