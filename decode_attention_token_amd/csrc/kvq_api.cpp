@@ -55,7 +55,6 @@ kvq_status check_config(const kvq_config *c) {
   if (c->v_policy != KVQ_V_CHUNK && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "unknown v_policy");
   if (c->sink_tokens < 0) return fail(KVQ_ERR_ARG, "sink_tokens must be non-negative");
   if (iq && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "the InnerQ scheme keeps a FIFO window (v_policy 1)");
-  if (!iq && c->sink_tokens) return fail(KVQ_ERR_UNSUPPORTED, "sink tokens are implemented for the InnerQ scheme only");
   if (c->sink_tokens > 512) return fail(KVQ_ERR_UNSUPPORTED, "more than 512 sink tokens is not implemented");
   if (c->max_tokens > (1 << 25)) return fail(KVQ_ERR_UNSUPPORTED, "max_tokens above 2^25 is not implemented");
   if (c->head_dim != kvq::kHeadDim) return fail(KVQ_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
@@ -240,31 +239,37 @@ kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache, const u
   }
   const int R = cfg->residual, G = cfg->group;
   const int units = cfg->batch * cfg->num_kv_heads;
-  const int64_t nq_k = len - (len % R);
-  const int64_t nq_v = (cfg->v_policy == KVQ_V_CHUNK) ? nq_k : (len > R ? len - R : 0);
   const kvq::CacheView cv = view_of(cfg, cache);
-  hipError_t e;
+  // sink tokens [0, ns) stay fp16; the KIVI rules apply to the L tokens after
+  // them (row and ring indices count from the first token after the sinks)
+  const int64_t ns = len < cfg->sink_tokens ? len : cfg->sink_tokens;
+  const int64_t L = len - ns;
+  const int64_t nq_k = L - (L % R);
+  const int64_t nq_v = (cfg->v_policy == KVQ_V_CHUNK) ? nq_k : (L > R ? L - R : 0);
+  hipError_t e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, cfg->sink_tokens, k, v, len, 0, (int)ns, 0, units,
+                                       stream);
+  if (e != hipSuccess) return device_error(e, "copy sink tokens");
   if (nq_k > 0) {
-    e = kvq::launch_quantize_keys(cv, units, k, len, 0, (int)(nq_k / G), 0, stream);
+    e = kvq::launch_quantize_keys(cv, units, k, len, ns, (int)(nq_k / G), 0, stream);
     if (e != hipSuccess) return device_error(e, "quantize keys");
   }
   if (nq_v > 0) {
-    e = kvq::launch_quantize_values(cv, units, v, len, 0, (int)nq_v, 0, stream);
+    e = kvq::launch_quantize_values(cv, units, v, len, ns, (int)nq_v, 0, stream);
     if (e != hipSuccess) return device_error(e, "quantize values");
   }
-  if (len > nq_k) {
-    e = kvq::launch_copy_to_residual(cv, units, k, nullptr, len, nq_k, (int)(len - nq_k), (int)(nq_k % R), true,
+  if (L > nq_k) {
+    e = kvq::launch_copy_to_residual(cv, units, k, nullptr, len, ns + nq_k, (int)(L - nq_k), (int)(nq_k % R), true,
                                      false, stream);
     if (e != hipSuccess) return device_error(e, "copy key residual");
   }
-  if (len > nq_v) {
-    e = kvq::launch_copy_to_residual(cv, units, nullptr, v, len, nq_v, (int)(len - nq_v), (int)(nq_v % R), false,
+  if (L > nq_v) {
+    e = kvq::launch_copy_to_residual(cv, units, nullptr, v, len, ns + nq_v, (int)(L - nq_v), (int)(nq_v % R), false,
                                      true, stream);
     if (e != hipSuccess) return device_error(e, "copy value residual");
   }
   cache->n_tokens = len;
-  cache->nq_k = nq_k;
-  cache->nq_v = nq_v;
+  cache->nq_k = ns + nq_k;
+  cache->nq_v = ns + nq_v;
   cache->started = 1;
   cache->flushes = 0;
   g_err[0] = 0;
@@ -287,9 +292,20 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
   const int R = cfg->residual, G = cfg->group;
   const int units = cfg->batch * cfg->num_kv_heads;
   const kvq::CacheView cv = view_of(cfg, cache);
-  int64_t n = cache->n_tokens, nq_k = cache->nq_k, nq_v = cache->nq_v;
-  int32_t flushes = cache->flushes;
+  const int S = cfg->sink_tokens;
   hipError_t e;
+  if (cache->n_tokens < S) {
+    // still filling the sink tokens
+    e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, S, k_new, v_new, 1, 0, 1, (int)cache->n_tokens, units, stream);
+    if (e != hipSuccess) return device_error(e, "append sink token");
+    cache->n_tokens += 1;
+    cache->nq_k = cache->nq_v = cache->n_tokens;
+    g_err[0] = 0;
+    return KVQ_OK;
+  }
+  // counters of the token stream after the sinks
+  int64_t n = cache->n_tokens - S, nq_k = cache->nq_k - S, nq_v = cache->nq_v - S;
+  int32_t flushes = cache->flushes;
   // FIFO: the value queue would exceed R, so quantize its oldest entry before
   // its ring slot (the same slot the new token takes) is overwritten
   if (cfg->v_policy == KVQ_V_FIFO && (n + 1) - nq_v > R) {
@@ -312,9 +328,9 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
     if (e != hipSuccess) return device_error(e, "flush values");
     nq_v += R;
   }
-  cache->n_tokens = n;
-  cache->nq_k = nq_k;
-  cache->nq_v = nq_v;
+  cache->n_tokens = S + n;
+  cache->nq_k = S + nq_k;
+  cache->nq_v = S + nq_v;
   cache->flushes = flushes;
   g_err[0] = 0;
   return KVQ_OK;
@@ -364,6 +380,7 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.nparts = splits;
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.k_new = a.v_new = nullptr;
+  a.nsink = 0;   // the InnerQ kernel derives its sinks from n and the config
   const hipError_t e = kvq::launch_innerq_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
   return KVQ_OK;
@@ -374,7 +391,12 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
                             void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream) {
   if (is_innerq(cfg))
     return launch_innerq_attention(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
-  const int64_t m = cache->nq_k < cache->nq_v ? cache->nq_k : cache->nq_v;
+  // sink tokens [0, ns) are fp16; everything else is indexed from the first
+  // token after them
+  const int64_t ns = n_tokens < cfg->sink_tokens ? n_tokens : cfg->sink_tokens;
+  const int64_t nq_k = cache->nq_k - ns, nq_v = cache->nq_v - ns;
+  n_tokens -= ns;
+  const int64_t m = nq_k < nq_v ? nq_k : nq_v;
   const int64_t n_main = (m / cfg->group) * cfg->group;
   if (splits == 0) splits = auto_splits_for(cfg, n_main);
   const size_t need = workspace_for(cfg, splits);
@@ -389,16 +411,18 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;
   a.n = n_tokens;
-  a.nq_k = cache->nq_k;
-  a.nq_v = cache->nq_v;
+  a.nq_k = nq_k;
+  a.nq_v = nq_v;
   a.n_main = n_main;
+  a.nsink = (int)ns;
   // tokens [n_main, n): all fp16 (chunked residual) -> the last split takes
-  // them; keys quantized but values fp16 (FIFO queue) -> a tail workgroup
+  // them; keys quantized but values fp16 (FIFO queue) -> a tail workgroup.
+  // The sink tokens always go to the last split.
   const bool has_rest = n_tokens > n_main;
-  const bool all_fp16 = cache->nq_k == n_main && cache->nq_v == n_main;
+  const bool all_fp16 = nq_k == n_main && nq_v == n_main;
   a.resid_main = (has_rest && all_fp16) ? 1 : 0;
   a.tail_wg = (has_rest && !all_fp16) ? 1 : 0;
-  a.splits = n_main > 0 ? splits : a.resid_main;
+  a.splits = n_main > 0 ? splits : ((a.resid_main || ns > 0) ? 1 : 0);
   a.nparts = a.splits + a.tail_wg;
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.k_new = k_new;
@@ -435,8 +459,8 @@ kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16
   const int64_t n1 = cache->n_tokens + 1;
   // one launch when the append needs no flush or queue pop and the residual
   // is the chunked all-fp16 kind; otherwise the two calls in sequence
-  const bool fused = !is_innerq(cfg) && cfg->v_policy == KVQ_V_CHUNK && cache->nq_k == cache->nq_v &&
-                     n1 - cache->nq_k < R;
+  const bool fused = !is_innerq(cfg) && cfg->v_policy == KVQ_V_CHUNK && cache->n_tokens >= cfg->sink_tokens &&
+                     cache->nq_k == cache->nq_v && n1 - cache->nq_k < R;
   if (!fused) {
     const size_t need = workspace_for(cfg, splits == 0 ? kvq_auto_splits(cfg, n1) : splits);
     if (workspace_bytes < need)

@@ -364,12 +364,13 @@ void decode_attn_kernel(AttnArgs a) {
     }
   }
 
-  // fp16 residual tokens [n_main, n), all keys and values fp16: same lane
-  // layout, plain query, weights p * U so the final 1/U scaling applies
-  if (a.resid_main && split == a.splits - 1) {
-    const int R = a.c.residual;
-    const int rcount = (int)(a.n - a.n_main);
-    const int rsteps = (rcount + TPS - 1) / TPS;
+  // fp16 tokens, in the last split: the sink tokens (rows of k_sink) and,
+  // with the chunked residual, tokens [n_main, n) from the ring.  Same lane
+  // layout, plain query, weights p * U so the final 1/U scaling applies.
+  const int rcount = a.resid_main ? (int)(a.n - a.n_main) : 0;
+  const int nf = a.nsink + rcount;
+  if (nf > 0 && split == a.splits - 1) {
+    const int R = a.c.residual, S = a.c.sinks;
     const uint16_t *kr = a.c.k_resid + (int64_t)unit * R * kHeadDim + j * CPL;
     const uint16_t *vr = a.c.v_resid + (int64_t)unit * R * kHeadDim + j * CPL;
 #pragma unroll
@@ -378,7 +379,7 @@ void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) qf[h][i] = h2f(qp[i]) * a.qscale;
     }
-    if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
+    if (rcount > 0 && a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
       // fused step: store the new token into its ring slot
       constexpr int CH = kHeadDim * 2 / 16;
       const int which = tid / CH, ch = tid % CH;
@@ -387,13 +388,22 @@ void decode_attn_kernel(AttnArgs a) {
                                              ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
       dst[ch] = src[ch];
     }
-    for (int rs = wave; rs < rsteps; rs += kWaves) {
-      const int64_t t = a.n_main + (int64_t)rs * TPS + tl;
-      const bool valid = t < a.n;
-      const int slot = (int)((valid ? t : a.n_main) % R);
-      const bool fresh = a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
-      const uint16_t *krow = fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + (int64_t)slot * kHeadDim;
-      const uint16_t *vrow = fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + (int64_t)slot * kHeadDim;
+    for (int rs = wave; rs * TPS < nf; rs += kWaves) {
+      const int i = rs * TPS + tl;
+      const bool valid = i < nf;
+      const int ii = valid ? i : 0;
+      const uint16_t *krow, *vrow;
+      if (ii < a.nsink) {
+        const int64_t off = ((int64_t)unit * S + ii) * kHeadDim + j * CPL;
+        krow = a.c.k_sink + off;
+        vrow = a.c.v_sink + off;
+      } else {
+        const int64_t t = a.n_main + (ii - a.nsink);
+        const bool fresh = a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
+        const int64_t slot = t % R;
+        krow = fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + slot * kHeadDim;
+        vrow = fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + slot * kHeadDim;
+      }
       fp16_token<HPG, CPL, NVG, LPT>(o, qf, krow, vrow, valid, U);
     }
   }

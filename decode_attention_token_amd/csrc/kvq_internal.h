@@ -78,6 +78,8 @@ struct AttnArgs {
   int tail_wg;           // 1: an extra workgroup per unit runs the mixed tail [n_main, n)
   int resid_main;        // 1: [n_main, n) is all-fp16 and the last split takes it
   int nparts;            // splits + tail_wg; 1 means the kernel writes out directly
+  int nsink;             // KIVI: fp16 sink tokens present (rows of c.k_sink); counters above
+                         // then count the tokens after them
   float qscale;          // softmax_scale * log2(e)
   // Fused decode step: token n - 1 is read from k_new / v_new ([B*Hkv][128])
   // instead of the residual ring, and the last split writes it into its ring

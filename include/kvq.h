@@ -15,6 +15,8 @@
  *          per channel / values per token, 3.1 fp16 residual cache
  *          batch-quantized when full, 4.1 knobs nbits, group_size,
  *          residual_length.
+ *   [KVQ]  the same juejin.cn page, KVQuant part, section 五 (attention-sink
+ *          aware quantization: the first tokens stay fp16).
  *   [InnerQ] euno.news, "【论文】InnerQ：硬件感知免调优KV缓存量化用于大语言模型",
  *          methodology 1 (groups along the hidden dimension), 2 (per-group
  *          symmetric or asymmetric mode from the group statistics, one shared
@@ -52,6 +54,10 @@
  *   k_resid, v_resid f16 [U][R][head_dim]  fp16 residual ring, token t in
  *                                  slot t mod R
  *   Dequantized value of a code: S * (code + Z) (inverse of [HFQ] 2.1).
+ *   With sink_tokens = S > 0 ([KVQ]): tokens t < S are kept fp16 in
+ *   k_sink, v_sink f16 [U][S][head_dim] (row t), and the rules above apply to
+ *   the tokens after them: token t >= S is token t - S of the rows, groups
+ *   and ring slots above.
  *
  * Device layout of a KVQ_SCHEME_INNERQ cache: k_codes, v_codes as above;
  *   k_scale, v_scale f32 [U][cap][head_dim/G]  per (token, group of G channels)
@@ -92,7 +98,8 @@ typedef enum { KVQ_V_CHUNK = 0, KVQ_V_FIFO = 1 } kvq_v_policy;
 /* Quantization scheme.
  * KVQ_SCHEME_KIVI: keys per channel over groups of G tokens, values per token
  *   over groups of G channels, asymmetric ([KIVI], [HFQ] 2.2); fp16 residual
- *   of fewer than R tokens (or the R most recent values, KVQ_V_FIFO).
+ *   of fewer than R tokens (or the R most recent values, KVQ_V_FIFO); the
+ *   first sink_tokens tokens optionally kept fp16 ([KVQ]).
  * KVQ_SCHEME_INNERQ: keys and values both per token over groups of G channels
  *   ([InnerQ] methodology 1); each group symmetric when it is centred on zero,
  *   read as |mean| < std / 10 with the population std, else asymmetric
@@ -105,10 +112,9 @@ typedef enum { KVQ_SCHEME_KIVI = 0, KVQ_SCHEME_INNERQ = 1 } kvq_scheme;
 /* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
  * plus the attention shape and the scheme.  Constraints: bits in {2,4};
  * head_dim % group == 0; group * bits % 32 == 0; num_q_heads % num_kv_heads
- * == 0; residual > 0; max_tokens > 0.  KVQ_SCHEME_KIVI also needs residual %
- * group == 0 ([KIVI] how it works), max_tokens % residual == 0 and
- * sink_tokens == 0; KVQ_SCHEME_INNERQ needs sink_tokens >= 0 and v_policy ==
- * KVQ_V_FIFO. */
+ * == 0; residual > 0; max_tokens > 0; sink_tokens >= 0.  KVQ_SCHEME_KIVI
+ * also needs residual % group == 0 ([KIVI] how it works) and max_tokens %
+ * residual == 0; KVQ_SCHEME_INNERQ needs v_policy == KVQ_V_FIFO. */
 typedef struct {
   int32_t bits;
   int32_t group;        /* G */
@@ -120,7 +126,7 @@ typedef struct {
   int32_t max_tokens;   /* capacity per unit, prompt plus generated tokens */
   int32_t v_policy;     /* kvq_v_policy */
   int32_t scheme;       /* kvq_scheme */
-  int32_t sink_tokens;  /* KVQ_SCHEME_INNERQ: leading tokens kept fp16 */
+  int32_t sink_tokens;  /* leading tokens kept fp16 (both schemes; 0 = none) */
 } kvq_config;
 
 /* Byte sizes of the caller-allocated device buffers of one cache (k_sink and
@@ -132,8 +138,8 @@ typedef struct {
 /* One layer's cache: caller-owned device buffers (sized by kvq_layout_bytes)
  * and host counters.  Zero-initialize the struct, set the pointers, and leave
  * the counters to the library.  n_tokens = tokens cached; nq_k / nq_v = end of
- * the quantized key / value tokens (KIVI: [0, nq); InnerQ: [sink_tokens, nq)
- * with nq_k == nq_v, and nq == n_tokens while n_tokens <= sink_tokens);
+ * the quantized key / value tokens, which are [sink_tokens, nq) (InnerQ:
+ * nq_k == nq_v), with nq == n_tokens while n_tokens <= sink_tokens;
  * started = prefill has run.  k_sink / v_sink may be null when sink_tokens
  * is 0. */
 typedef struct {
@@ -172,23 +178,24 @@ size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t spli
 /* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
  * device [batch][num_kv_heads][len][head_dim], read only (the full-precision
  * tensors stay valid for the caller, as the page's prefill paragraph
- * requires).  KIVI: the first len - (len mod R) tokens are quantized, keys
- * per channel over groups of G tokens and values per token over groups of G
- * channels; the last len mod R tokens go to the residual ring.  With
- * KVQ_V_FIFO the last min(len, R) values stay fp16 instead.  InnerQ: tokens
- * t < sink_tokens go to the sink rows, the last min(R, len - sink_tokens)
- * to the window, the rest are quantized.  Needs a cache with started == 0
- * and len <= max_tokens; len == 0 is allowed. */
+ * requires).  Tokens t < sink_tokens go to the sink rows.  KIVI, on the
+ * L = len - sinks tokens after them: the first L - (L mod R) are quantized,
+ * keys per channel over groups of G tokens and values per token over groups
+ * of G channels; the last L mod R go to the residual ring.  With KVQ_V_FIFO
+ * the last min(L, R) values stay fp16 instead.  InnerQ: the last
+ * min(R, len - sink_tokens) go to the window, the rest are quantized.  Needs
+ * a cache with started == 0 and len <= max_tokens; len == 0 is allowed. */
 kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache,
                                 const uint16_t *k, const uint16_t *v, int64_t len,
                                 hipStream_t stream);
 
 /* One decode step's new key and value, fp16 device [batch][num_kv_heads]
- * [head_dim]; n += 1.  KIVI: written to residual slot n mod R; when the key
+ * [head_dim]; n += 1.  Token n < sink_tokens goes to sink row n.  KIVI,
+ * otherwise: written to residual slot (n - sinks) mod R; when the key
  * residual reaches R tokens it is quantized and appended to the grouped part
  * in the same call (eager flush, [KIVI] how it works; [HFQ] 3.1); values
- * follow the cache's kvq_v_policy.  InnerQ: token n < sink_tokens goes to
- * sink row n; otherwise, when the window already holds R tokens its oldest
+ * follow the cache's kvq_v_policy.  InnerQ, otherwise: when the window
+ * already holds R tokens its oldest
  * token (ring slot nq mod R) is quantized into row nq first, and the new
  * token takes ring slot n mod R; one kernel launch.  Needs started and
  * n < max_tokens. */
@@ -213,8 +220,9 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
 
 /* One decode step: kvq_append_token(k_new, v_new) followed by
  * kvq_decode_attention(q) with the same results, but as a single kernel
- * launch whenever a KIVI append needs no flush and the cache uses the chunked
- * value residual: the attention kernel reads the new token from k_new/v_new
+ * launch whenever a KIVI append needs no flush, the new token is not a sink
+ * and the cache uses the chunked value residual: the attention kernel reads
+ * the new token from k_new/v_new
  * and stores it into its residual slot.  Otherwise (and always for InnerQ)
  * it runs the two calls in sequence.  Arguments and requirements are those of the two calls; on a
  * validation failure nothing is enqueued and the cache is unchanged. */

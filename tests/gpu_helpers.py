@@ -97,6 +97,31 @@ def compare_unit_buffers(cache, ref, b, h, rb=None, rh=None):
             assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), name
 
 
+def compare_sink_unit(cache, ref, b, h):
+    """Bit-exact comparison of one unit of a KIVI cache with sink tokens
+    (oracle.KiviSinkCache): the inner rows and ring slots, and the sink rows."""
+    inner = ref.inner
+    bufs = ref.buffers(cache.cfg.max_tokens)
+    assert (cache.n_tokens, cache.nq_k, cache.nq_v) == (ref.n, ref.nq_k, ref.nq_v)
+    T = cache.tensors
+    G = ref.G
+    for name, sl in (("k_codes", np.s_[:inner.nq_k]), ("k_scale", np.s_[:inner.nq_k // G]),
+                     ("k_zero", np.s_[:inner.nq_k // G]), ("v_codes", np.s_[:inner.nq_v]),
+                     ("v_scale", np.s_[:inner.nq_v]), ("v_zero", np.s_[:inner.nq_v])):
+        got = host(T[name][b, h][sl])
+        if name.endswith("codes"):
+            got = got.view(np.uint32)
+        assert np.array_equal(got, bufs[name][b, h][sl]), name
+    ns = min(ref.n, ref.S)
+    for name in ("k_sink", "v_sink"):
+        assert np.array_equal(host(T[name][b, h][:ns]).view(np.uint16), bufs[name][b, h][:ns].view(np.uint16)), name
+    ks, vs = ref.live_resid_slots()
+    for name, slots in (("k_resid", ks), ("v_resid", vs)):
+        if slots:
+            got = host(T[name][b, h][slots]).view(np.uint16)
+            assert np.array_equal(got, bufs[name][b, h][slots].view(np.uint16)), name
+
+
 def compare_all_buffers(cache, ref):
     for b in range(ref.B):
         for h in range(ref.H):

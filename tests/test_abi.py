@@ -142,9 +142,11 @@ def test_innerq_relaxes_the_kivi_multiples(lib):
     for kw in (dict(residual=20), dict(max_tokens=1001), dict(sink_tokens=0), dict(bits=2, group=32)):
         out = kvq.kvq_layout()
         assert lib.kvq_layout_bytes(ctypes.byref(iq_cfg(**kw)), ctypes.byref(out)) == kvq.KVQ_OK, kw
-    # sinks are an InnerQ feature here
+    # the KIVI scheme takes sinks too, and sizes their buffers
     out = kvq.kvq_layout()
-    assert lib.kvq_layout_bytes(ctypes.byref(cfg(sink_tokens=4)), ctypes.byref(out)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_layout_bytes(ctypes.byref(cfg(sink_tokens=4)), ctypes.byref(out)) == kvq.KVQ_OK
+    assert out.k_sink == out.v_sink == 16 * 32 * 4 * 128 * 2
+    assert lib.kvq_layout_bytes(ctypes.byref(cfg(sink_tokens=513)), ctypes.byref(out)) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_innerq_null_sink_buffers_are_rejected(lib):

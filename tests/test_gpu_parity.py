@@ -177,3 +177,71 @@ def test_decode_step_matches_append_then_attention(policy):
         if i % 16 == 15 or i == w.steps - 1:
             assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
     compare_all_buffers(fused, ref)
+
+
+# KIVI with fp16 sink tokens: (workload, sinks, steps at which attention is checked)
+SINK_CASES = [
+    (_w(140, 2, 4, 4, 300, 2, 32, 64, 70), 4, [1, 20, 21, 70]),            # flush at step 20
+    (_w(141, 2, 4, 2, 129, 4, 32, 64, 65, FIFO), 4, [1, 64, 65]),          # GQA 2, FIFO values
+    (_w(142, 1, 8, 2, 2, 2, 64, 128, 140), 8, [1, 6, 7, 8, 140]),          # L < sinks, GQA 4
+    (_w(143, 1, 2, 2, 3, 4, 64, 64, 5), 8, [1, 5]),                       # only sinks
+]
+
+
+@pytest.mark.parametrize("w,S,checks", SINK_CASES, ids=[c[0].name for c in SINK_CASES])
+def test_kivi_sink_tokens_parity(w, S, checks):
+    from gpu_helpers import compare_sink_unit
+    print(f"case {w.name} sinks {S}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads, 128,
+                          w.max_tokens + w.residual, w.v_policy, kvq.KVQ_SCHEME_KIVI, S)
+    cache = kvq.KVCache(cfg, "cuda")
+    ref = oracle.KiviSinkCache(w.bits, w.group, w.residual, S, w.batch, w.num_kv_heads, 128, w.v_policy)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    scale = 1.0 / math.sqrt(128)
+    ws = cache.workspace()
+    for step in range(1, w.steps + 1):
+        cache.append(kn[step - 1].contiguous(), vn[step - 1].contiguous())
+        ref.append(host(kn[step - 1]), host(vn[step - 1]))
+        assert (cache.n_tokens, cache.nq_k, cache.nq_v) == (ref.n, ref.nq_k, ref.nq_v)
+        if step in checks:
+            q = qs[step - 1].contiguous()
+            out = cache.attention(q, scale, workspace=ws)
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                for h in range(w.num_kv_heads):
+                    compare_sink_unit(cache, ref, b, h)
+            err = max_err(out, oracle_attention(ref, host(q), scale))
+            print(f"  step {step}: n={ref.n} nq_k={ref.nq_k} nq_v={ref.nq_v} err={err:.2e}", flush=True)
+            assert err <= ATOL
+
+
+def test_kivi_sink_decode_step_matches_append_then_attention():
+    from gpu_helpers import compare_sink_unit
+    w = _w(144, 2, 4, 2, 2, 2, 32, 64, 80)
+    S = 4
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    k, v = gen_prefill(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    mk = lambda: kvq.KVCache(kvq.make_config(2, 32, 64, 2, 4, 2, 128, 192, CHUNK, kvq.KVQ_SCHEME_KIVI, S), "cuda")
+    fused, plain = mk(), mk()
+    ref = oracle.KiviSinkCache(2, 32, 64, S, 2, 2, 128)
+    fused.prefill(k, v)
+    plain.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    wa, wb = fused.workspace(), plain.workspace()
+    for i in range(w.steps):
+        q = qs[i].contiguous()
+        oa = fused.step(kn[i].contiguous(), vn[i].contiguous(), q, workspace=wa)
+        plain.append(kn[i].contiguous(), vn[i].contiguous())
+        ob = plain.attention(q, workspace=wb)
+        ref.append(host(kn[i]), host(vn[i]))
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), i
+    assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
+    for b in range(2):
+        for h in range(2):
+            compare_sink_unit(fused, ref, b, h)
