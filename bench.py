@@ -44,8 +44,10 @@ def attn_bytes(w, n, nq_k, nq_v):
         m = nq_k - min(n, w.sinks)   # quantized tokens
         per_unit = m * 2 * (d * b // 8 + (d // G) * 6) + (n - m) * d * 2 * 2
     else:
-        per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6 + nq_v * d * b // 8 + nq_v * (d // G) * 6
-                    + ((n - nq_k) + (n - nq_v)) * d * 2)
+        ns = min(n, w.sinks)            # fp16 sink tokens; nq_k / nq_v count them
+        qk, qv = nq_k - ns, nq_v - ns   # quantized key / value tokens
+        per_unit = (qk * d * b // 8 + (qk // G) * d * 6 + qv * d * b // 8 + qv * (d // G) * 6
+                    + ((n - qk) + (n - qv)) * d * 2)
     return w.batch * w.num_kv_heads * per_unit + w.batch * w.num_q_heads * d * 6
 
 
@@ -240,6 +242,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
     ap.add_argument("--no-side", action="store_true", help="skip the prefill and flush timings")
+    ap.add_argument("--v-policy", choices=("chunk", "fifo"), default=None,
+                    help="override the workload's value-residual policy (KIVI scheme)")
+    ap.add_argument("--sinks", type=int, default=None, help="override the workload's fp16 sink tokens")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -251,6 +256,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     w = WORKLOADS[args.workload]
+    if args.v_policy is not None:
+        w = w.scaled(v_policy=0 if args.v_policy == "chunk" else 1)
+    if args.sinks is not None:
+        w = w.scaled(sinks=args.sinks)
     steps = w.steps if args.steps is None else args.steps
     layers = w.layers if args.layers is None else args.layers
     dev = torch.device("cuda:0")

@@ -25,6 +25,11 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                          lattice exactly), code(min) == 0, code(max) in
                          {2^b-2, 2^b-1}, monotone codes, |x - x_hat| <= S/2 + eps,
                          nearest-level brute force, constant groups exact.
+  quantize_groups(f16_scale=True)
+                         pinned: S is the smallest fp16 >= the fp32 scale
+                         (neighbour enumeration), on-grid lattices with fp16
+                         scales recovered exactly, nearest-level brute force,
+                         |x - x_hat| <= S/2, packed words decode to S and Z.
   dequantize             pinned with quantize_groups (round trip).
   pack_rows/unpack_rows  pinned: literal words from the layout definition,
                          brute-force enumeration of all codes in a word.
@@ -70,18 +75,30 @@ import numpy as np
 __all__ = [
     "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
     "attention", "kv_code_bytes_per_token", "attention_call_bytes", "flush_bytes",
-    "CHUNK", "FIFO", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
+    "CHUNK", "FIFO", "META_F32", "META_F16", "round_up_to_fp16", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
     "InnerQCache", "innerq_attention_call_bytes", "KiviSinkCache",
 ]
 
 CHUNK = 0   # value residual flushed as a block of R tokens, like the keys ([HFQ] 3.1)
 FIFO = 1    # value residual kept as a queue of the R most recent tokens ([KIVI] 工作原理)
 
+META_F32 = 0   # group metadata: fp32 scale + int16 zero-point (6 bytes)
+META_F16 = 1   # group metadata: fp16 scale rounded up + int16 zero-point in one 32-bit word
+
 _F32 = np.float32
 
 
 # --------------------------------------------------------------------------- quantizer
-def quantize_groups(x, bits: int):
+def round_up_to_fp16(s):
+    """Smallest fp16 value >= s, returned as float32 (s positive float32)."""
+    s = np.asarray(s, _F32)
+    h = s.astype(np.float16)                       # round to nearest even
+    low = h.astype(_F32) < s
+    h = np.where(low, np.nextafter(h, np.float16(np.inf)), h)
+    return h.astype(_F32)
+
+
+def quantize_groups(x, bits: int, f16_scale: bool = False):
     """Asymmetric affine quantization of each group along the last axis.
 
     [HFQ] 2.1 writes the quantizer as X_Q = round(X / S) - Z with scale S and
@@ -93,6 +110,10 @@ def quantize_groups(x, bits: int):
                so it reconstructs exactly
       Z      = rint(min / S)                 (integer, stored as int16)
       code_i = clamp(rint(x_i / S) - Z, 0, 2^b - 1)
+
+    With f16_scale (compressed metadata) S is replaced by the smallest fp16
+    value >= S before Z and the codes are computed, so it stores exactly in
+    fp16 and the group's range still fits the 2^b levels.
 
     x: float16 array, groups along the last axis.
     Returns (codes uint8 same shape, S float32 [...], Z int16 [...]).
@@ -108,6 +129,8 @@ def quantize_groups(x, bits: int):
         s_range = (span / qmax).astype(_F32)
     s_const = np.where(mn != 0, np.abs(mn), _F32(1.0)).astype(_F32)
     scale = np.where(mx > mn, s_range, s_const).astype(_F32)
+    if f16_scale:
+        scale = round_up_to_fp16(scale)
     zero = np.rint((mn / scale).astype(_F32)).astype(_F32)
     q = np.rint((xf / scale[..., None]).astype(_F32)).astype(_F32) - zero[..., None]
     codes = np.clip(q, _F32(0), qmax).astype(np.uint8)
@@ -174,9 +197,12 @@ class QuantizedKVCache:
     plus the residual; it never changes the fp16 inputs.
     """
 
-    def __init__(self, bits, group, residual, batch, kv_heads, head_dim, v_policy=CHUNK):
+    def __init__(self, bits, group, residual, batch, kv_heads, head_dim, v_policy=CHUNK, meta=META_F32):
         if bits not in (2, 4):
             raise ValueError("bits must be 2 or 4")
+        if meta not in (META_F32, META_F16):
+            raise ValueError("unknown metadata format")
+        self.meta = meta
         if residual <= 0 or residual % group:
             raise ValueError("R must be a positive multiple of G")
         if head_dim % group:
@@ -213,7 +239,7 @@ class QuantizedKVCache:
         G = self.G
         assert m % G == 0
         grp = k.reshape(B, H, m // G, G, d).transpose(0, 1, 2, 4, 3)   # [.., g, c, t]
-        codes, s, z = quantize_groups(grp, self.bits)
+        codes, s, z = quantize_groups(grp, self.bits, self.meta == META_F16)
         codes = codes.transpose(0, 1, 2, 4, 3).reshape(B, H, m, d)
         return codes, s, z                                            # s,z [.., g, c]
 
@@ -222,7 +248,7 @@ class QuantizedKVCache:
         B, H, m, d = v.shape
         G = self.G
         grp = v.reshape(B, H, m, d // G, G)
-        codes, s, z = quantize_groups(grp, self.bits)
+        codes, s, z = quantize_groups(grp, self.bits, self.meta == META_F16)
         return codes.reshape(B, H, m, d), s, z                        # s,z [.., t, j]
 
     def _append_keys(self, k):
@@ -307,6 +333,8 @@ class QuantizedKVCache:
         v_zero  i16 [B,H,cap,d/G]
         k_resid, v_resid f16 [B,H,R,d] token t at slot t mod R (live slots only;
                                        the others hold whatever was there)
+        With META_F16, k_scale / v_scale hold u32 words (fp16 S | Z << 16) of
+        the same shapes and k_zero / v_zero are empty.
         """
         B, H, d, G, R, b = self.B, self.H, self.d, self.G, self.R, self.bits
         cap = max_tokens
@@ -332,6 +360,13 @@ class QuantizedKVCache:
             out["k_resid"][:, :, (nqk + i) % R] = self.kr[:, :, i]
         for i in range(self.vr.shape[2]):
             out["v_resid"][:, :, (nqv + i) % R] = self.vr[:, :, i]
+        if self.meta == META_F16:
+            # one 32-bit word per group: fp16 bits of S in the low half, Z in the high half
+            for t in ("k", "v"):
+                sc, zr = out[t + "_scale"], out[t + "_zero"]
+                bits16 = sc.astype(np.float16).view(np.uint16).astype(np.uint32)
+                out[t + "_scale"] = bits16 | (zr.view(np.uint16).astype(np.uint32) << np.uint32(16))
+                out[t + "_zero"] = np.zeros(zr.shape[:2] + (0,) + zr.shape[3:], np.int16)
         return out
 
     def live_resid_slots(self):
@@ -356,11 +391,11 @@ class KiviSinkCache:
     (== n while n <= sinks).
     """
 
-    def __init__(self, bits, group, residual, sinks, batch, kv_heads, head_dim, v_policy=CHUNK):
+    def __init__(self, bits, group, residual, sinks, batch, kv_heads, head_dim, v_policy=CHUNK, meta=META_F32):
         if sinks < 0:
             raise ValueError("sinks must be non-negative")
         self.S = sinks
-        self.inner = QuantizedKVCache(bits, group, residual, batch, kv_heads, head_dim, v_policy)
+        self.inner = QuantizedKVCache(bits, group, residual, batch, kv_heads, head_dim, v_policy, meta)
         self.bits, self.G, self.R = bits, group, residual
         self.B, self.H, self.d = batch, kv_heads, head_dim
         self.sink_k = np.zeros((batch, kv_heads, 0, head_dim), np.float16)
@@ -648,17 +683,18 @@ def kv_code_bytes_per_token(layers, kv_heads, head_dim, bits):
     return layers * 2 * kv_heads * head_dim * bits // 8
 
 
-def attention_call_bytes(batch, q_heads, kv_heads, head_dim, bits, group, n, nq_k, nq_v):
+def attention_call_bytes(batch, q_heads, kv_heads, head_dim, bits, group, n, nq_k, nq_v, meta=META_F32):
     """Algorithmic bytes one decode-attention call must move.
 
-    Per unit: key codes + key metadata (fp32 scale + int16 zero per
-    (group, channel)) + value codes + value metadata (per (token, channel
-    group)) + the fp16 residual keys and values; plus the fp16 query and the
-    fp32 output of every query head.
+    Per unit: key codes + key metadata (scale + int16 zero per (group,
+    channel): 6 bytes, or 4 with META_F16) + value codes + value metadata (per
+    (token, channel group)) + the fp16 residual keys and values; plus the
+    fp16 query and the fp32 output of every query head.
     """
     d, b, G = head_dim, bits, group
-    per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * 6
-                + nq_v * d * b // 8 + nq_v * (d // G) * 6
+    mb = 6 if meta == META_F32 else 4
+    per_unit = (nq_k * d * b // 8 + (nq_k // G) * d * mb
+                + nq_v * d * b // 8 + nq_v * (d // G) * mb
                 + ((n - nq_k) + (n - nq_v)) * d * 2)
     return batch * kv_heads * per_unit + batch * q_heads * d * (2 + 4)
 
