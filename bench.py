@@ -46,14 +46,15 @@ def attn_bytes(w, n, nq_k, nq_v):
     else:
         ns = min(n, w.sinks)            # fp16 sink tokens; nq_k / nq_v count them
         qk, qv = nq_k - ns, nq_v - ns   # quantized key / value tokens
-        per_unit = (qk * d * b // 8 + (qk // G) * d * 6 + qv * d * b // 8 + qv * (d // G) * 6
+        mb = 4 if w.meta else 6         # metadata bytes per group
+        per_unit = (qk * d * b // 8 + (qk // G) * d * mb + qv * d * b // 8 + qv * (d // G) * mb
                     + ((n - qk) + (n - qv)) * d * 2)
     return w.batch * w.num_kv_heads * per_unit + w.batch * w.num_q_heads * d * 6
 
 
 def make_cfg(w, max_tokens):
     return kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks)
+                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks, w.meta)
 
 
 def build_caches(w, layers, max_tokens, dev):
@@ -138,8 +139,10 @@ def cpu_baseline(w, sample, budget_s=12.0):
     for k, v, kn, vn, q in sample:
         if w.scheme == kvq.KVQ_SCHEME_INNERQ:
             ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+        elif w.sinks:
+            ref = oracle.KiviSinkCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, w.v_policy, w.meta)
         else:
-            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy, w.meta)
         ref.prefill(k, v)
         ref.append(kn, vn)
         refs.append((ref, q))
@@ -170,8 +173,10 @@ def prefill_bytes(w, L):
         m = max(0, L - w.sinks - R)
         out = m * 2 * (d * b // 8 + (d // G) * 6) + (L - m) * d * 2 * 2
     else:
-        nq = L - L % R
-        out = nq * d * b // 8 * 2 + (nq // G) * d * 6 + nq * (d // G) * 6 + (L - nq) * d * 2 * 2
+        ns = min(L, w.sinks)
+        nq = (L - ns) - (L - ns) % R    # quantized tokens after the sinks
+        mb = 4 if w.meta else 6
+        out = nq * d * b // 8 * 2 + (nq // G) * d * mb + nq * (d // G) * mb + (L - nq) * d * 2 * 2
     return w.units * (L * d * 2 * 2 + out)
 
 
@@ -183,7 +188,8 @@ def flush_bytes(w):
     d, b, G, R = w.head_dim, w.bits, w.group, w.residual
     if w.scheme == kvq.KVQ_SCHEME_INNERQ:
         return w.units * (d * 2 * 2 + 2 * (d * b // 8 + (d // G) * 6) + d * 2 * 2)
-    return w.units * (R * d * 2 * 2 + R * d * b // 8 * 2 + (R // G) * d * 6 + R * (d // G) * 6 + d * 2 * 2)
+    mb = 4 if w.meta else 6
+    return w.units * (R * d * 2 * 2 + R * d * b // 8 * 2 + (R // G) * d * mb + R * (d // G) * mb + d * 2 * 2)
 
 
 def time_prefill_and_flush(w, dev, stream, reps=5):
@@ -245,6 +251,8 @@ def main():
     ap.add_argument("--v-policy", choices=("chunk", "fifo"), default=None,
                     help="override the workload's value-residual policy (KIVI scheme)")
     ap.add_argument("--sinks", type=int, default=None, help="override the workload's fp16 sink tokens")
+    ap.add_argument("--meta", choices=("f32", "f16"), default=None,
+                    help="group metadata: fp32 scale + int16 zero, or a packed fp16 scale | zero word (KIVI)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -260,6 +268,8 @@ def main():
         w = w.scaled(v_policy=0 if args.v_policy == "chunk" else 1)
     if args.sinks is not None:
         w = w.scaled(sinks=args.sinks)
+    if args.meta is not None:
+        w = w.scaled(meta=0 if args.meta == "f32" else 1, name=w.name + ("-meta16" if args.meta == "f16" else ""))
     steps = w.steps if args.steps is None else args.steps
     layers = w.layers if args.layers is None else args.layers
     dev = torch.device("cuda:0")
@@ -353,7 +363,8 @@ def main():
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": w.context,
                    "bits": w.bits, "group": w.group, "residual": w.residual, "layers": layers,
                    "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo",
-                   "scheme": "innerq" if w.scheme == kvq.KVQ_SCHEME_INNERQ else "kivi", "sinks": w.sinks},
+                   "scheme": "innerq" if w.scheme == kvq.KVQ_SCHEME_INNERQ else "kivi", "sinks": w.sinks,
+                   "meta": "f16-packed" if w.meta else "f32+i16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
                      "kernel": KERNELS[w.scheme][0], "avg_call_us": round(call_us, 2),

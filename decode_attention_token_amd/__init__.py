@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_DEVICE, KVQ_ERR_UNSUPPORTED = range(6)
 KVQ_V_CHUNK, KVQ_V_FIFO = 0, 1
 KVQ_SCHEME_KIVI, KVQ_SCHEME_INNERQ = 0, 1
+KVQ_META_F32, KVQ_META_F16 = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
@@ -30,7 +31,7 @@ EXPORTED = [
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bits", "group", "residual", "batch", "num_q_heads", "num_kv_heads", "head_dim",
-        "max_tokens", "v_policy", "scheme", "sink_tokens")]
+        "max_tokens", "v_policy", "scheme", "sink_tokens", "meta_format")]
 
 
 class kvq_layout(ctypes.Structure):
@@ -100,9 +101,9 @@ def _check(status: int):
 
 
 def make_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0) -> kvq_config:
+                v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0, meta_format=KVQ_META_F32) -> kvq_config:
     return kvq_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                      v_policy, scheme, sink_tokens)
+                      v_policy, scheme, sink_tokens, meta_format)
 
 
 def make_innerq_config(bits, group, window, sink_tokens, batch, num_q_heads, num_kv_heads, head_dim,
@@ -160,14 +161,18 @@ class KVCache:
                                  cfg.group, cfg.residual, cfg.sink_tokens)
         W = d * cfg.bits // 32
         innerq = cfg.scheme == KVQ_SCHEME_INNERQ
+        packed = cfg.meta_format == KVQ_META_F16   # (S, Z) words in *_scale, no *_zero
         kmeta = (B, H, cap, d // G) if innerq else (B, H, cap // G, d)
-        shapes = {"k_codes": (B, H, cap, W), "k_scale": kmeta, "k_zero": kmeta,
-                  "v_codes": (B, H, cap, W), "v_scale": (B, H, cap, d // G),
-                  "v_zero": (B, H, cap, d // G), "k_resid": (B, H, R, d), "v_resid": (B, H, R, d),
+        vmeta = (B, H, cap, d // G)
+        none = lambda shp: shp[:2] + (0,) + shp[3:]
+        shapes = {"k_codes": (B, H, cap, W), "k_scale": kmeta, "k_zero": none(kmeta) if packed else kmeta,
+                  "v_codes": (B, H, cap, W), "v_scale": vmeta, "v_zero": none(vmeta) if packed else vmeta,
+                  "k_resid": (B, H, R, d), "v_resid": (B, H, R, d),
                   "k_sink": (B, H, S, d), "v_sink": (B, H, S, d)}
         self.tensors = {}
         for name, shp in shapes.items():
-            t = torch.zeros(shp, dtype=self._DT[name], device=device)
+            dt = torch.int32 if packed and name in ("k_scale", "v_scale") else self._DT[name]
+            t = torch.zeros(shp, dtype=dt, device=device)
             assert t.numel() * t.element_size() == getattr(lay, name), name
             self.tensors[name] = t
         self.c = kvq_cache()

@@ -54,6 +54,9 @@ kvq_status check_config(const kvq_config *c) {
                 c->residual);
   if (c->v_policy != KVQ_V_CHUNK && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "unknown v_policy");
   if (c->sink_tokens < 0) return fail(KVQ_ERR_ARG, "sink_tokens must be non-negative");
+  if (c->meta_format != KVQ_META_F32 && c->meta_format != KVQ_META_F16) return fail(KVQ_ERR_ARG, "unknown meta_format");
+  if (iq && c->meta_format != KVQ_META_F32)
+    return fail(KVQ_ERR_UNSUPPORTED, "compressed metadata is implemented for the KIVI scheme only");
   if (iq && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "the InnerQ scheme keeps a FIFO window (v_policy 1)");
   if (c->sink_tokens > 512) return fail(KVQ_ERR_UNSUPPORTED, "more than 512 sink tokens is not implemented");
   if (c->max_tokens > (1 << 25)) return fail(KVQ_ERR_UNSUPPORTED, "max_tokens above 2^25 is not implemented");
@@ -71,8 +74,9 @@ kvq_status check_config(const kvq_config *c) {
 
 kvq_status check_cache(const kvq_config *c, const kvq_cache *k) {
   if (!k) return fail(KVQ_ERR_ARG, "cache is null");
-  if (!k->k_codes || !k->k_scale || !k->k_zero || !k->v_codes || !k->v_scale || !k->v_zero || !k->k_resid ||
-      !k->v_resid)
+  const bool zeros = c->meta_format == KVQ_META_F32;   // separate zero-point buffers
+  if (!k->k_codes || !k->k_scale || !k->v_codes || !k->v_scale || !k->k_resid || !k->v_resid ||
+      (zeros && (!k->k_zero || !k->v_zero)))
     return fail(KVQ_ERR_ARG, "a cache buffer pointer is null");
   if (c->sink_tokens > 0 && (!k->k_sink || !k->v_sink)) return fail(KVQ_ERR_ARG, "a sink buffer pointer is null");
   return KVQ_OK;
@@ -95,6 +99,7 @@ kvq::CacheView view_of(const kvq_config *c, const kvq_cache *k) {
   v.group = c->group;
   v.residual = c->residual;
   v.sinks = c->sink_tokens;
+  v.meta = c->meta_format;
   return v;
 }
 
@@ -198,6 +203,7 @@ kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out) {
   out->v_codes = units * cap * words * 4;
   out->v_scale = units * cap * (d / G) * 4;
   out->v_zero = units * cap * (d / G) * 2;
+  if (cfg->meta_format == KVQ_META_F16) out->k_zero = out->v_zero = 0;   // packed into *_scale
   out->k_resid = units * (size_t)cfg->residual * d * 2;
   out->v_resid = out->k_resid;
   out->k_sink = units * (size_t)cfg->sink_tokens * d * 2;

@@ -62,6 +62,20 @@ struct Geo {
   static constexpr int SMEM = WORK + kStageFloats<HPG>;  // floats
 };
 
+// One group's (S, Z) at index idx of a scale / zero-point pair of arrays, in
+// either metadata format.
+__device__ __forceinline__ void group_meta(const float *scale, const int16_t *zero, int64_t idx, int meta,
+                                           float &S, float &Z) {
+  if (meta) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(scale)[idx];
+    S = h2f((uint16_t)(w & 0xffffu));
+    Z = (float)(int16_t)(w >> 16);
+  } else {
+    S = scale[idx];
+    Z = (float)zero[idx];
+  }
+}
+
 // ---------------------------------------------------------------- tail path
 // Tokens [n_main, n): keys and values may each be quantized or fp16 per token.
 // Plain dequantize-then-dot: a wave per token for scores, a thread per
@@ -97,10 +111,12 @@ __device__ void decode_tail(const AttnArgs &a, int unit, float *smem, const Stag
       const int64_t g = t / G;
       const uint32_t word = a.c.k_codes[((int64_t)unit * cap + t) * W + c0 / PER];
       const int sh = (c0 % PER) * BITS;
-      const float *S = a.c.k_scale + ((int64_t)unit * (cap / G) + g) * kHeadDim + c0;
-      const int16_t *Z = a.c.k_zero + ((int64_t)unit * (cap / G) + g) * kHeadDim + c0;
-      k0 = ((float)((word >> sh) & MASK) + (float)Z[0]) * S[0];
-      k1 = ((float)((word >> (sh + BITS)) & MASK) + (float)Z[1]) * S[1];
+      const int64_t gi = ((int64_t)unit * (cap / G) + g) * kHeadDim + c0;
+      float S0, Z0, S1, Z1;
+      group_meta(a.c.k_scale, a.c.k_zero, gi, a.c.meta, S0, Z0);
+      group_meta(a.c.k_scale, a.c.k_zero, gi + 1, a.c.meta, S1, Z1);
+      k0 = ((float)((word >> sh) & MASK) + Z0) * S0;
+      k1 = ((float)((word >> (sh + BITS)) & MASK) + Z1) * S1;
     } else {
       const uint16_t *r = a.c.k_resid + ((int64_t)unit * R + (t % R)) * kHeadDim + c0;
       k0 = h2f(r[0]);
@@ -142,7 +158,9 @@ __device__ void decode_tail(const AttnArgs &a, int unit, float *smem, const Stag
     if (t < a.nq_v) {
       const uint32_t word = a.c.v_codes[((int64_t)unit * cap + t) * W + c / PER];
       const int64_t gi = ((int64_t)unit * cap + t) * VGR + c / G;
-      v = ((float)((word >> ((c % PER) * BITS)) & MASK) + (float)a.c.v_zero[gi]) * a.c.v_scale[gi];
+      float S, Z;
+      group_meta(a.c.v_scale, a.c.v_zero, gi, a.c.meta, S, Z);
+      v = ((float)((word >> ((c % PER) * BITS)) & MASK) + Z) * S;
     } else {
       v = h2f(a.c.v_resid[((int64_t)unit * R + (t % R)) * kHeadDim + c]);
     }
@@ -172,7 +190,8 @@ struct StepBuf {
   uint32_t kz;       // their int16 zero-points
 };
 
-template <int BITS, int GS, int HPG, int LPT>
+// META = 1: group metadata as packed words (fp16 S | Z << 16) in *_scale.
+template <int BITS, int GS, int HPG, int LPT, int META>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
 void decode_attn_kernel(AttnArgs a) {
   using Gm = Geo<BITS, GS, HPG, LPT>;
@@ -244,9 +263,10 @@ void decode_attn_kernel(AttnArgs a) {
   const Rsrc rkc = rsrc_of(a.c.k_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
   const Rsrc rvc = rsrc_of(a.c.v_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
   const Rsrc rvs = rsrc_of(a.c.v_scale + (int64_t)unit * cap * VGR, (uint32_t)(cap * VGR * 4));
-  const Rsrc rvz = rsrc_of(a.c.v_zero + (int64_t)unit * cap * VGR, (uint32_t)(cap * VGR * 2));
   const Rsrc rks = rsrc_of(a.c.k_scale + (int64_t)unit * ngr_cap * kHeadDim, (uint32_t)(ngr_cap * kHeadDim * 4));
-  const Rsrc rkz = rsrc_of(a.c.k_zero + (int64_t)unit * ngr_cap * kHeadDim, (uint32_t)(ngr_cap * kHeadDim * 2));
+  // separate zero-point arrays only with fp32 metadata (null otherwise)
+  const Rsrc rvz = META ? rvs : rsrc_of(a.c.v_zero + (int64_t)unit * cap * VGR, (uint32_t)(cap * VGR * 2));
+  const Rsrc rkz = META ? rks : rsrc_of(a.c.k_zero + (int64_t)unit * ngr_cap * kHeadDim, (uint32_t)(ngr_cap * kHeadDim * 2));
   const uint32_t code_lane = (uint32_t)(tl * W + j * WPL) * 4u;
   const uint32_t vmeta_lane = (uint32_t)(tl * VGR + (j * CPL) / GS);
   const uint32_t kmeta_lane = (uint32_t)(2 * lane);
@@ -257,7 +277,17 @@ void decode_attn_kernel(AttnArgs a) {
     const uint32_t tb = g * GS + (uint32_t)((s % SPG) * TPS);   // first token of the step (uniform)
     bload_words<WPL>(rkc, code_lane, tb * (W * 4), bf.kw);
     bload_words<WPL>(rvc, code_lane, tb * (W * 4), bf.vw);
-    if constexpr (NVG == 2) {
+    if constexpr (META) {
+      // packed words: vs[] carries the raw words, decoded in process()
+      if constexpr (NVG == 2) {
+        const float2 v2 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vmeta_lane * 4, tb * (VGR * 4), kStream));
+        bf.vs[0] = v2.x;
+        bf.vs[1] = v2.y;
+      } else {
+        bf.vs[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvs, vmeta_lane * 4, tb * (VGR * 4), kStream));
+      }
+      bf.vz = 0;
+    } else if constexpr (NVG == 2) {
       const float2 v2 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rvs, vmeta_lane * 4, tb * (VGR * 4), kStream));
       bf.vs[0] = v2.x;
       bf.vs[1] = v2.y;
@@ -268,7 +298,11 @@ void decode_attn_kernel(AttnArgs a) {
       bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, vmeta_lane * 2, tb * (VGR * 2), kStream);
     }
     bf.ks = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rks, kmeta_lane * 4, g * (kHeadDim * 4), 0));
-    bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, kmeta_lane * 2, g * (kHeadDim * 2), 0);
+    if constexpr (META) {
+      bf.kz = 0;   // the zero-points are in the high halves of ks
+    } else {
+      bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, kmeta_lane * 2, g * (kHeadDim * 2), 0);
+    }
   };
 
   auto process = [&](const Buf &bf, int s) {
@@ -276,11 +310,22 @@ void decode_attn_kernel(AttnArgs a) {
       // new key group: fold its per-channel scales into the query; each block
       // of FOLD lanes holds one lane slice's channels and sums its share of
       // the zero-point bias
-      const float z0 = (float)(int16_t)(bf.kz & 0xffffu);
-      const float z1 = (float)(int16_t)(bf.kz >> 16);
+      float ks0, ks1, z0, z1;
+      if constexpr (META) {
+        const uint32_t w0 = __float_as_uint(bf.ks.x), w1 = __float_as_uint(bf.ks.y);
+        ks0 = h2f((uint16_t)(w0 & 0xffffu));
+        ks1 = h2f((uint16_t)(w1 & 0xffffu));
+        z0 = (float)(int16_t)(w0 >> 16);
+        z1 = (float)(int16_t)(w1 >> 16);
+      } else {
+        ks0 = bf.ks.x;
+        ks1 = bf.ks.y;
+        z0 = (float)(int16_t)(bf.kz & 0xffffu);
+        z1 = (float)(int16_t)(bf.kz >> 16);
+      }
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
-        const float p0 = qa[h] * bf.ks.x, p1 = qb[h] * bf.ks.y;   // q'/U
+        const float p0 = qa[h] * ks0, p1 = qb[h] * ks1;   // q'/U
         const float part = block_sum<FOLD>(fmaf(p0, z0, p1 * z1));
         *reinterpret_cast<float2 *>(lds_qp + h * kHeadDim + 2 * lane) = make_float2(p0, p1);
         if (lane % FOLD == 0) lds_beta[h * 8 + lane / FOLD] = part * U;
@@ -321,13 +366,24 @@ void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < HPG; ++h) p[h] = o.weight(h, block_sum<LPT>((sc[h] + d1[h]) + beta[h]));
     // values
-    float vz[NVG];
-    vz[0] = (float)(int16_t)(bf.vz & 0xffffu);
-    if constexpr (NVG == 2) vz[1] = (float)(int16_t)(bf.vz >> 16);
+    float vs[NVG], vz[NVG];
+    if constexpr (META) {
+#pragma unroll
+      for (int k = 0; k < NVG; ++k) {
+        const uint32_t w = __float_as_uint(bf.vs[k]);
+        vs[k] = h2f((uint16_t)(w & 0xffffu));
+        vz[k] = (float)(int16_t)(w >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NVG; ++k) vs[k] = bf.vs[k];
+      vz[0] = (float)(int16_t)(bf.vz & 0xffffu);
+      if constexpr (NVG == 2) vz[1] = (float)(int16_t)(bf.vz >> 16);
+    }
 #pragma unroll
     for (int h = 0; h < HPG; ++h) {
 #pragma unroll
-      for (int k = 0; k < NVG; ++k) o.bias[h][k] = fmaf(p[h] * bf.vs[k], vz[k], o.bias[h][k]);
+      for (int k = 0; k < NVG; ++k) o.bias[h][k] = fmaf(p[h] * vs[k], vz[k], o.bias[h][k]);
     }
 #pragma unroll
     for (int w = 0; w < WPL; ++w) {
@@ -337,7 +393,7 @@ void decode_attn_kernel(AttnArgs a) {
       const int k = (w * PER) / SPAN;
 #pragma unroll
       for (int h = 0; h < HPG; ++h) {
-        const float wt = p[h] * bf.vs[k];
+        const float wt = p[h] * vs[k];
 #pragma unroll
         for (int i = 0; i < PER; ++i) o.acc[h][w * PER + i] = fmaf(wt, vf[i], o.acc[h][w * PER + i]);
       }
@@ -432,31 +488,31 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float *__restrict
   out[bh * kHeadDim + c] = acc / L;
 }
 
-template <int BITS, int GS, int HPG>
+template <int BITS, int GS, int HPG, int META>
 hipError_t launch_kernel(const AttnArgs &a, hipStream_t s) {
   constexpr int LPT = (HPG == 1) ? 4 : (HPG == 2 ? 4 : 8);
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT>), dim3(units * a.nparts), dim3(kThreads), 0,
+  hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META>), dim3(units * a.nparts), dim3(kThreads), 0,
                      s, a);
   return hipGetLastError();
 }
 
-template <int BITS, int GS>
+template <int BITS, int GS, int META>
 hipError_t launch_by_heads(const AttnArgs &a, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_kernel<BITS, GS, 1>(a, s);
-    case 2: return launch_kernel<BITS, GS, 2>(a, s);
-    case 4: return launch_kernel<BITS, GS, 4>(a, s);
+    case 1: return launch_kernel<BITS, GS, 1, META>(a, s);
+    case 2: return launch_kernel<BITS, GS, 2, META>(a, s);
+    case 4: return launch_kernel<BITS, GS, 4, META>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int BITS>
+template <int BITS, int META>
 hipError_t launch_by_group(const AttnArgs &a, hipStream_t s) {
   switch (a.c.group) {
-    case 32: return launch_by_heads<BITS, 32>(a, s);
-    case 64: return launch_by_heads<BITS, 64>(a, s);
-    case 128: return launch_by_heads<BITS, 128>(a, s);
+    case 32: return launch_by_heads<BITS, 32, META>(a, s);
+    case 64: return launch_by_heads<BITS, 64, META>(a, s);
+    case 128: return launch_by_heads<BITS, 128, META>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -470,7 +526,11 @@ hipError_t launch_merge(const AttnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
-  hipError_t e = (a.c.bits == 2) ? launch_by_group<2>(a, s) : launch_by_group<4>(a, s);
+  hipError_t e;
+  if (a.c.meta)
+    e = (a.c.bits == 2) ? launch_by_group<2, 1>(a, s) : launch_by_group<4, 1>(a, s);
+  else
+    e = (a.c.bits == 2) ? launch_by_group<2, 0>(a, s) : launch_by_group<4, 0>(a, s);
   if (e != hipSuccess) return e;
   return launch_merge(a, s);
 }

@@ -24,7 +24,8 @@ struct CacheView {
   uint16_t *v_sink;
   int64_t cap;      // max_tokens
   int bits, group, residual;
-  int sinks;        // sink tokens kept fp16 (InnerQ-style layout; 0 otherwise)
+  int sinks;        // sink tokens kept fp16 (0 = none)
+  int meta;         // 0: fp32 scale + int16 zero; 1: packed fp16 scale | zero << 16 in *_scale
 };
 
 // Quantize `ngroups` key groups per unit.  Source rows: src + (unit * src_rows

@@ -66,13 +66,17 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   mx0 = fmaxf(fmaxf(s_mx[0][ch], s_mx[1][ch]), fmaxf(s_mx[2][ch], s_mx[3][ch]));
   mn1 = fminf(fminf(s_mn[0][ch + 1], s_mn[1][ch + 1]), fminf(s_mn[2][ch + 1], s_mn[3][ch + 1]));
   mx1 = fmaxf(fmaxf(s_mx[0][ch + 1], s_mx[1][ch + 1]), fmaxf(s_mx[2][ch + 1], s_mx[3][ch + 1]));
-  const GroupParams p0 = group_params(mn0, mx0, QMAX);
-  const GroupParams p1 = group_params(mn1, mx1, QMAX);
+  const GroupParams p0 = group_params(mn0, mx0, QMAX, c.meta != 0);
+  const GroupParams p1 = group_params(mn1, mx1, QMAX, c.meta != 0);
   if (part == 0) {
     const int64_t gidx = ((int64_t)unit * (c.cap / GS) + dst_group0 + g) * kHeadDim + ch;
-    *reinterpret_cast<float2 *>(c.k_scale + gidx) = make_float2(p0.s, p1.s);
-    *reinterpret_cast<uint32_t *>(c.k_zero + gidx) =
-        (uint32_t)(uint16_t)(int16_t)p0.z | ((uint32_t)(uint16_t)(int16_t)p1.z << 16);
+    if (c.meta) {
+      *reinterpret_cast<uint2 *>(c.k_scale + gidx) = make_uint2(pack_meta(p0.s, p0.z), pack_meta(p1.s, p1.z));
+    } else {
+      *reinterpret_cast<float2 *>(c.k_scale + gidx) = make_float2(p0.s, p1.s);
+      *reinterpret_cast<uint32_t *>(c.k_zero + gidx) =
+          (uint32_t)(uint16_t)(int16_t)p0.z | ((uint32_t)(uint16_t)(int16_t)p1.z << 16);
+    }
   }
   uint32_t ca[TQ], cb[TQ];
   codes_of<TQ>(xa, p0, 0.0f, QMAX, ca);
@@ -124,10 +128,14 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
       mx = fmaxf(mx, v[k]);
     }
   }
-  const GroupParams p = group_params(mn, mx, QMAX);
+  const GroupParams p = group_params(mn, mx, QMAX, c.meta != 0);
   const int64_t row = (int64_t)unit * c.cap + dst_row0 + i;
-  c.v_scale[row * NG + j] = p.s;
-  c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
+  if (c.meta) {
+    reinterpret_cast<uint32_t *>(c.v_scale)[row * NG + j] = pack_meta(p.s, p.z);
+  } else {
+    c.v_scale[row * NG + j] = p.s;
+    c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
+  }
   uint32_t *dst = c.v_codes + row * W + j * (G / PER);
   for (int k0 = 0; k0 < G; k0 += 32) {
     float v[32];

@@ -21,17 +21,33 @@ struct GroupParams {
   float r;   // RN(1 / s), for the fast quotient
 };
 
+// Smallest fp16 value >= s (s > 0), as a float: round to nearest, then one
+// fp16 step up if that fell below.
+__device__ __forceinline__ float round_up_fp16(float s) {
+  __half h = __float2half_rn(s);
+  if (__half2float(h) < s) h = __ushort_as_half((unsigned short)(__half_as_ushort(h) + 1));
+  return __half2float(h);
+}
+
+// Compressed metadata word: fp16 bits of S (exactly representable) in the low
+// half, the int16 zero-point in the high half.
+__device__ __forceinline__ uint32_t pack_meta(float s, float z) {
+  return (uint32_t)__half_as_ushort(__float2half_rn(s)) | ((uint32_t)(uint16_t)(int16_t)z << 16);
+}
+
 // Scale and zero-point of one group from its minimum and maximum: S spreads
 // the range over the 2^b - 1 steps and Z = rint(min / S), which maps the
 // minimum to code 0.  A constant group takes S = |min| (1 for an all-zero
-// group) and so reconstructs exactly.
-__device__ __forceinline__ GroupParams group_params(float mn, float mx, float qmax) {
+// group) and so reconstructs exactly.  With compressed metadata S is first
+// rounded up to fp16, so the range still fits the levels.
+__device__ __forceinline__ GroupParams group_params(float mn, float mx, float qmax, bool f16_scale = false) {
   float s;
   if (mx > mn) {
     s = (mx - mn) / qmax;
   } else {
     s = (mn != 0.0f) ? fabsf(mn) : 1.0f;
   }
+  if (f16_scale) s = round_up_fp16(s);
   return {s, rintf(mn / s), 1.0f / s};
 }
 

@@ -109,12 +109,22 @@ typedef enum { KVQ_V_CHUNK = 0, KVQ_V_FIFO = 1 } kvq_v_policy;
  *   R.  Requires v_policy == KVQ_V_FIFO. */
 typedef enum { KVQ_SCHEME_KIVI = 0, KVQ_SCHEME_INNERQ = 1 } kvq_scheme;
 
+/* Storage of a group's (S, Z).
+ * KVQ_META_F32: fp32 scale in *_scale and int16 zero-point in *_zero, 6 bytes.
+ * KVQ_META_F16: one 32-bit word per group in *_scale, the fp16 bits of S in
+ *   the low half and Z in the high half (4 bytes); *_zero are unused (0
+ *   bytes).  S is first replaced by the smallest fp16 value >= S, then Z and
+ *   the codes are computed with it, so the group's range still fits the 2^b
+ *   levels.  KIVI scheme only. */
+typedef enum { KVQ_META_F32 = 0, KVQ_META_F16 = 1 } kvq_meta_format;
+
 /* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
  * plus the attention shape and the scheme.  Constraints: bits in {2,4};
  * head_dim % group == 0; group * bits % 32 == 0; num_q_heads % num_kv_heads
  * == 0; residual > 0; max_tokens > 0; sink_tokens >= 0.  KVQ_SCHEME_KIVI
  * also needs residual % group == 0 ([KIVI] how it works) and max_tokens %
- * residual == 0; KVQ_SCHEME_INNERQ needs v_policy == KVQ_V_FIFO. */
+ * residual == 0; KVQ_SCHEME_INNERQ needs v_policy == KVQ_V_FIFO and
+ * meta_format == KVQ_META_F32. */
 typedef struct {
   int32_t bits;
   int32_t group;        /* G */
@@ -127,10 +137,12 @@ typedef struct {
   int32_t v_policy;     /* kvq_v_policy */
   int32_t scheme;       /* kvq_scheme */
   int32_t sink_tokens;  /* leading tokens kept fp16 (both schemes; 0 = none) */
+  int32_t meta_format;  /* kvq_meta_format */
 } kvq_config;
 
 /* Byte sizes of the caller-allocated device buffers of one cache (k_sink and
- * v_sink are 0 unless sink_tokens > 0). */
+ * v_sink are 0 unless sink_tokens > 0; k_zero and v_zero are 0 with
+ * KVQ_META_F16). */
 typedef struct {
   size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, k_sink, v_sink;
 } kvq_layout;
@@ -141,7 +153,8 @@ typedef struct {
  * the quantized key / value tokens, which are [sink_tokens, nq) (InnerQ:
  * nq_k == nq_v), with nq == n_tokens while n_tokens <= sink_tokens;
  * started = prefill has run.  k_sink / v_sink may be null when sink_tokens
- * is 0. */
+ * is 0, k_zero / v_zero with KVQ_META_F16 (k_scale / v_scale then hold the
+ * packed words). */
 typedef struct {
   uint32_t *k_codes;
   float *k_scale;

@@ -17,14 +17,20 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def make_cache(bits, G, R, B, Hq, Hkv, cap, policy=kvq.KVQ_V_CHUNK, d=128):
-    cfg = kvq.make_config(bits, G, R, B, Hq, Hkv, d, cap, policy)
+def make_cache(bits, G, R, B, Hq, Hkv, cap, policy=kvq.KVQ_V_CHUNK, d=128, sinks=0, meta=kvq.KVQ_META_F32):
+    cfg = kvq.make_config(bits, G, R, B, Hq, Hkv, d, cap, policy, kvq.KVQ_SCHEME_KIVI, sinks, meta)
     return cfg, kvq.KVCache(cfg, "cuda")
 
 
 def make_innerq_cache(bits, G, R, S, B, Hq, Hkv, cap, d=128):
     cfg = kvq.make_innerq_config(bits, G, R, S, B, Hq, Hkv, d, cap)
     return cfg, kvq.KVCache(cfg, "cuda")
+
+
+def _bits(x):
+    """Host array with integer words viewed unsigned (packed metadata words are
+    held in int32 tensors on the GPU and as uint32 in the oracle)."""
+    return x.view(np.uint32) if x.dtype == np.int32 else x
 
 
 def compare_innerq_unit(cache, ref, b, h, rb=None, rh=None):
@@ -81,7 +87,7 @@ def compare_unit_buffers(cache, ref, b, h, rb=None, rh=None):
         ("v_zero", np.s_[:nq_v], None),
     ]
     for name, sl, conv in pairs:
-        got = host(T[name][b, h][sl])
+        got = _bits(host(T[name][b, h][sl]))
         if conv:
             got = conv(got)
         want = bufs[name][rb, rh][sl]
@@ -108,7 +114,7 @@ def compare_sink_unit(cache, ref, b, h):
     for name, sl in (("k_codes", np.s_[:inner.nq_k]), ("k_scale", np.s_[:inner.nq_k // G]),
                      ("k_zero", np.s_[:inner.nq_k // G]), ("v_codes", np.s_[:inner.nq_v]),
                      ("v_scale", np.s_[:inner.nq_v]), ("v_zero", np.s_[:inner.nq_v])):
-        got = host(T[name][b, h][sl])
+        got = _bits(host(T[name][b, h][sl]))
         if name.endswith("codes"):
             got = got.view(np.uint32)
         assert np.array_equal(got, bufs[name][b, h][sl]), name

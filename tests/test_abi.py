@@ -60,6 +60,7 @@ int main(void) {
   printf("kvq_config %zu\nkvq_layout %zu\nkvq_cache %zu\n", sizeof(kvq_config), sizeof(kvq_layout),
          sizeof(kvq_cache));
   F(kvq_config, scheme) F(kvq_config, sink_tokens) F(kvq_layout, k_sink) F(kvq_layout, v_sink)
+  F(kvq_config, meta_format)
   F(kvq_cache, k_sink) F(kvq_cache, v_sink) F(kvq_cache, n_tokens) F(kvq_cache, flushes)
   return 0;
 }
@@ -106,6 +107,40 @@ def test_layout_bytes_follow_the_documented_layout(lib):
     assert lay.k_resid == lay.v_resid == units * R * d * 2
     lay4 = kvq.kvq_layout_bytes(cfg(bits=4, group=64))
     assert lay4.k_codes == units * cap * (d * 4 // 32) * 4
+
+
+def test_packed_metadata_layout_bytes(lib):
+    """Compressed metadata: one 32-bit word per group in the scale buffers,
+    no zero-point buffers; codes and residual unchanged."""
+    base, lay = kvq.kvq_layout_bytes(cfg()), kvq.kvq_layout_bytes(cfg(meta_format=kvq.KVQ_META_F16))
+    units, cap, d, G = 16 * 32, 4224, 128, 32
+    assert lay.k_scale == units * (cap // G) * d * 4 and lay.v_scale == units * cap * (d // G) * 4
+    assert lay.k_zero == lay.v_zero == 0
+    for name in ("k_codes", "v_codes", "k_resid", "v_resid", "k_sink", "v_sink"):
+        assert getattr(lay, name) == getattr(base, name), name
+
+
+@pytest.mark.parametrize("bad,status", [
+    (cfg(meta_format=2), kvq.KVQ_ERR_ARG),
+    (cfg(meta_format=-1), kvq.KVQ_ERR_ARG),
+    (iq_cfg(meta_format=kvq.KVQ_META_F16), kvq.KVQ_ERR_UNSUPPORTED),
+])
+def test_invalid_metadata_formats_are_rejected(lib, bad, status):
+    out = kvq.kvq_layout()
+    assert lib.kvq_layout_bytes(ctypes.byref(bad), ctypes.byref(out)) == status
+    assert "meta" in lib.kvq_last_error().decode()
+
+
+def test_packed_metadata_needs_no_zero_buffers(lib):
+    """With packed metadata the zero-point pointers may be null: validation
+    passes them and stops at the next check (here the missing inputs)."""
+    c = cfg(meta_format=kvq.KVQ_META_F16)
+    cache = _fake_cache()
+    cache.k_zero = cache.v_zero = None
+    assert lib.kvq_quantize_prefill(ctypes.byref(c), ctypes.byref(cache), None, None, 10, None) == kvq.KVQ_ERR_ARG
+    assert "zero" not in lib.kvq_last_error().decode()
+    c32 = cfg()
+    assert lib.kvq_quantize_prefill(ctypes.byref(c32), ctypes.byref(cache), None, None, 10, None) == kvq.KVQ_ERR_ARG
 
 
 def test_innerq_layout_bytes(lib):

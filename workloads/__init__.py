@@ -47,7 +47,8 @@ class Workload:
     layers: int           # distinct layer caches the workload cycles through
     v_policy: int = 0     # 0 chunked residual, 1 FIFO value queue
     scheme: int = 0       # 0 KIVI-style, 1 InnerQ-style (R is then the recent window)
-    sinks: int = 0        # InnerQ-style: leading tokens kept fp16
+    sinks: int = 0        # leading tokens kept fp16
+    meta: int = 0         # 0 fp32 scale + int16 zero; 1 packed fp16 scale | zero word
 
     @property
     def units(self) -> int:
