@@ -35,6 +35,9 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "kvq_internal.h"
 #include "kvq_attn_common.h"
 
@@ -212,7 +215,7 @@ void decode_attn_kernel(AttnArgs a) {
   if (a.tail_wg) {
     if (blk < units) {
       decode_tail<BITS, HPG>(a, blk, smem, st);
-      finish_part<HPG>(a, blk, a.splits, st);
+      finish_part<HPG>(a, blk, a.part_base + a.splits, st);
       return;
     }
     blk -= units;
@@ -225,7 +228,7 @@ void decode_attn_kernel(AttnArgs a) {
   const int j = lane % LPT, tl = lane / LPT;
   const int b = unit / a.hkv, hk = unit % a.hkv;
   const int64_t cap = a.c.cap;
-  const int ngroups = (int)(a.n_main / GS);
+  const int ngroups = a.skip_main ? 0 : (int)(a.n_main / GS);
   const int g0 = (int)((int64_t)ngroups * split / a.splits);
   const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
   const int wg0 = g0 + (g1 - g0) * wave / kWaves;
@@ -465,7 +468,7 @@ void decode_attn_kernel(AttnArgs a) {
   }
 
   combine_waves<HPG, LPT, NVG>(o, smem, st, wave, lane, INV_U);
-  finish_part<HPG>(a, unit, split, st);
+  finish_part<HPG>(a, unit, a.part_base + split, st);
 }
 
 // Merge of the part records: m = max m_i, l = sum l_i 2^(m_i - m),
@@ -492,8 +495,8 @@ template <int BITS, int GS, int HPG, int META>
 hipError_t launch_kernel(const AttnArgs &a, hipStream_t s) {
   constexpr int LPT = (HPG == 1) ? 4 : (HPG == 2 ? 4 : 8);
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META>), dim3(units * a.nparts), dim3(kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META>), dim3(units * (a.splits + a.tail_wg)),
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -525,13 +528,46 @@ hipError_t launch_merge(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+
+hipError_t launch_valu(const AttnArgs &a, hipStream_t s) {
+  if (a.c.meta) return (a.c.bits == 2) ? launch_by_group<2, 1>(a, s) : launch_by_group<4, 1>(a, s);
+  return (a.c.bits == 2) ? launch_by_group<2, 0>(a, s) : launch_by_group<4, 0>(a, s);
+}
+
+// The matrix-core kernel takes the quantized groups of four-heads-per-kv-head
+// layouts unless KVQ_GQA_PATH=valu is set in the environment.
+bool gqa_mfma_enabled() {
+  const char *v = getenv("KVQ_GQA_PATH");
+  return v == nullptr || strcmp(v, "valu") != 0;
+}
+
+}  // namespace
+
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
   hipError_t e;
-  if (a.c.meta)
-    e = (a.c.bits == 2) ? launch_by_group<2, 1>(a, s) : launch_by_group<4, 1>(a, s);
-  else
-    e = (a.c.bits == 2) ? launch_by_group<2, 0>(a, s) : launch_by_group<4, 0>(a, s);
-  if (e != hipSuccess) return e;
+  // fp16 tokens (sinks, chunked residual) and the mixed FIFO tail are parts
+  // of their own next to the matrix-core parts; the workspace holds
+  // splits + 1 records per head, so with both the matrix cores take one
+  // split fewer
+  const int fp16_part = (a.nsink > 0 || a.resid_main) ? 1 : 0;
+  const int rest = fp16_part + a.tail_wg;
+  const int msplits = rest == 2 ? a.splits - 1 : a.splits;
+  if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && msplits >= 1 && gqa_mfma_enabled()) {
+    AttnArgs m = a;
+    m.splits = msplits;
+    m.nparts = msplits + rest;
+    if ((e = launch_gqa_mfma(m, s)) != hipSuccess) return e;
+    if (rest > 0) {
+      AttnArgs v = m;
+      v.skip_main = 1;
+      v.part_base = msplits;
+      v.splits = fp16_part;
+      if ((e = launch_valu(v, s)) != hipSuccess) return e;
+    }
+    return launch_merge(m, s);
+  }
+  if ((e = launch_valu(a, s)) != hipSuccess) return e;
   return launch_merge(a, s);
 }
 

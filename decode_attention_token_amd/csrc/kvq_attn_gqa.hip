@@ -1,0 +1,576 @@
+// Grouped-query decode attention on the matrix cores, gfx950: four query
+// heads share each kv head, KIVI layout (keys quantized per channel over
+// groups of G tokens, values per token over groups of G channels).
+//
+// Decoding reads the whole quantized cache once (KIVI part of the juejin.cn
+// page "大模型量化技术原理：KIVI、IntactKV、KVQuant"); with four query heads
+// per kv head each code feeds four products, and doing them one fused
+// multiply-add at a time leaves the kernel limited by vector ALU issue rather
+// than by HBM.  Both products are dense contractions, so this kernel runs
+// them as 16x16 bf16 MFMA tiles with fp32 accumulation, keeping the
+// group-dequantize-inside-the-product structure of the fused kernel in the
+// euno.news InnerQ summary (methodology 3 and 5) and the scale folding of
+// the vector-ALU kernel:
+//
+//   scores  s[t][h] = sum_c code[t][c] * q'[h][c] + beta[h]   (per key group)
+//           q'[h][c] = q[h][c] S[g][c],  beta[h] = sum_c q'[h][c] Z[g][c]
+//   values  o[h][c] += sum_t w[h][t][j] * code[t][c],  bias[h][j] += sum_t w[h][t][j] Z[t][j]
+//           w[h][t][j] = p[h][t] S[t][j]   (j = value group of channel c)
+//
+// The codes are small integers, exact in bf16.  The real-valued operands q'
+// and w are split into two bf16 limbs (high: the value rounded to bf16; low:
+// the exact remainder rounded to bf16), so each product is two MFMAs on the
+// same accumulator and its operand carries about 17 significant bits instead
+// of 8.
+//
+// Tiles (one wave, 32 tokens per step = two 16-token blocks):
+//  * key MFMA (16x16x32): A = codes, rows = 16 tokens, K = 32 channels per
+//    pass (4 passes); B = q' limbs, columns = (head h, key group slot g') for
+//    the four groups of a "super-chunk", so one preparation of q' serves 4G
+//    tokens.  Output lane (column n, row block r) holds 4 tokens' scores for
+//    column n; only columns of the step's own group slot are used.
+//  * value codes are transposed to tokens-along-K by an identity MFMA
+//    (16x16x16): lane (channel, r) then holds the codes of tokens 4r..4r+3 of
+//    each block, which is exactly the token set whose scores the same lane
+//    index holds in the key output.
+//  * value MFMA (16x16x32): A = w limbs, rows = (head, 32-channel slice),
+//    K = the 32 tokens; B = transposed codes, columns = 16 channels.  The
+//    weights move from the key output lanes to the A lanes with one quad
+//    broadcast (same 16-lane row, lane g' of each quad).
+// Key metadata of the next super-chunk and value metadata of the current step
+// arrive with the step's loads (coalesced) and are staged through a per-wave
+// LDS area into the lanes that need them.  The online softmax (log2 units,
+// wave-uniform per-head maximum raised only past a margin) follows the
+// vector-ALU kernel.  Work split: as the vector-ALU kernel, whole key groups
+// of one unit per workgroup, contiguous group ranges per wave; the fp16 tokens
+// (sinks, residual) and the mixed FIFO tail go to the vector-ALU kernel as
+// extra parts of the same unit, merged by the merge kernel.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "kvq_internal.h"
+#include "kvq_attn_common.h"
+
+namespace kvq {
+namespace {
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef float fx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHpg = 4;   // query heads per kv head on this path
+
+__device__ __forceinline__ fx4 mma_x32(u32x4 a, u32x4 b, fx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0,
+                                                 0, 0);
+}
+
+__device__ __forceinline__ fx4 mma_x16(u32x2 a, u32x2 b, fx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf4_t, a), __builtin_bit_cast(bf4_t, b), c,
+                                                   0, 0, 0);
+}
+
+// bf16 pair (lo = a, hi = b) of the upper halves of two fp32 values: the
+// values truncated to bf16 (exact for small integers).
+__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// bf16 pair (lo = a, hi = b), each rounded to nearest even.
+__device__ __forceinline__ uint32_t rne_pair(float a, float b) {
+  const bf2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two-limb split of a pair: hi = the values rounded to bf16, lo = the exact
+// remainders (at most half a bf16 ulp) rounded to bf16, so hi + lo carries
+// about 17 significant bits.
+__device__ __forceinline__ void limbs(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = rne_pair(a, b);
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+  lo = rne_pair(a - ha, b - hb);
+}
+
+// A lane's 32 codes (channels 32 kq .. 32 kq + 31 of one token) as 16 words of
+// exact bf16 pairs.  Word 4p + r holds channels 8p + {0,2}, {1,3}, {4,6},
+// {5,7} for r = 0..3 (the order the converts produce; the key preparation
+// arranges q' the same way).
+template <int BITS>
+struct CodesBf16;
+
+// Byte B of x as two fp4 nibbles -> bf16 pair; nibble c is worth c / 2, so
+// scale 2 gives the code itself.
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, B));
+}
+
+template <>
+struct CodesBf16<2> {
+  static constexpr int WPL = 2;   // code words per lane per token
+  __device__ static __forceinline__ void run(const uint32_t *w, uint32_t *u) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t m0 = w[k] & 0x33333333u;          // nibble i: code 2i
+      const uint32_t m1 = (w[k] >> 2) & 0x33333333u;   // nibble i: code 2i + 1
+      u[8 * k + 0] = fp4_pair<0>(m0);
+      u[8 * k + 1] = fp4_pair<0>(m1);
+      u[8 * k + 2] = fp4_pair<1>(m0);
+      u[8 * k + 3] = fp4_pair<1>(m1);
+      u[8 * k + 4] = fp4_pair<2>(m0);
+      u[8 * k + 5] = fp4_pair<2>(m1);
+      u[8 * k + 6] = fp4_pair<3>(m0);
+      u[8 * k + 7] = fp4_pair<3>(m1);
+    }
+  }
+};
+
+template <>
+struct CodesBf16<4> {
+  static constexpr int WPL = 4;
+  __device__ static __forceinline__ void run(const uint32_t *w, uint32_t *u) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t m0 = w[k] & 0x0F0F0F0Fu;          // byte i: code 2i
+      const uint32_t m1 = (w[k] >> 4) & 0x0F0F0F0Fu;   // byte i: code 2i + 1
+      // fp8 e4m3 byte c (c < 16) is worth c / 512: scale 512
+      u[4 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, false));
+      u[4 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, false));
+      u[4 * k + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, true));
+      u[4 * k + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, true));
+    }
+  }
+};
+
+// Channel offset (within 8) of element e of word r of a pass: 0,2 | 1,3 | 4,6 | 5,7.
+__device__ __host__ constexpr int pass_chan(int r, int e) { return (r >> 1) * 4 + (r & 1) + 2 * e; }
+
+template <int GS>
+struct GqaGeo {
+  static constexpr int SPG = GS / 32;                 // 32-token steps per key group
+  static constexpr int SPC = 4 * SPG;                 // steps per super-chunk (4 groups)
+  static constexpr int VGR = kHeadDim / GS;           // value groups per token
+  static constexpr int EPS = 128 / SPG;               // metadata entries per step (keys and values alike)
+  static constexpr int E = SPG == 1 ? 2 : 1;          // entries per lane per step
+  static constexpr int SH = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);   // 32-channel slice -> value group shift
+  // per-wave LDS staging (floats): key S and Z of a super-chunk [4][128],
+  // value S and Z of a step [VGR][32]
+  static constexpr int KM = 4 * kHeadDim;
+  static constexpr int VM = VGR * 32;
+  static constexpr int PER_WAVE = 2 * KM + 2 * VM;
+  static constexpr int ROWS = kWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
+  static constexpr int WORK = (kWaves * PER_WAVE > ROWS + 2 * kWaves * kHpg) ? kWaves * PER_WAVE
+                                                                              : ROWS + 2 * kWaves * kHpg;
+  static constexpr int SMEM = WORK + kStageFloats<kHpg>;
+};
+
+template <int BITS, int GS>
+struct GqaBuf {
+  static constexpr int WPL = CodesBf16<BITS>::WPL;
+  static constexpr int E = GqaGeo<GS>::E;
+  uint32_t kw[2 * WPL];   // key code words, block 0 then block 1
+  uint32_t vw[2 * WPL];
+  uint32_t ks[E];         // key metadata of the next super-chunk (S, or packed S | Z)
+  uint32_t vs[E];         // value metadata of this step
+  uint32_t kz, vz;        // int16 zero-points (fp32 metadata only)
+};
+
+__device__ __forceinline__ float sel4(int i, float a, float b, float c, float d) {
+  return i == 0 ? a : (i == 1 ? b : (i == 2 ? c : d));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m); }
+
+// One (S, Z) metadata entry from its raw word(s).
+template <int META>
+__device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, float &S, float &Z) {
+  if constexpr (META) {
+    S = h2f((uint16_t)(s_word & 0xffffu));
+    Z = (float)(int16_t)(s_word >> 16);
+  } else {
+    S = __uint_as_float(s_word);
+    Z = (float)(int16_t)zhalf;
+  }
+}
+
+template <int BITS, int GS, int META>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gqa_mfma_kernel(AttnArgs a) {
+  using Gm = GqaGeo<GS>;
+  using Buf = GqaBuf<BITS, GS>;
+  constexpr int WPL = Buf::WPL, E = Gm::E, SPG = Gm::SPG, SPC = Gm::SPC, VGR = Gm::VGR, EPS = Gm::EPS;
+  constexpr int W = kHeadDim * BITS / 32;   // code words per token row
+  constexpr int LOG_SPG = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);
+
+  __shared__ __attribute__((aligned(16))) float smem[Gm::SMEM];
+  const Stage st = stage_of<kHpg>(smem, Gm::WORK);
+
+  const int units = a.batch * a.hkv;
+  const int split = blockIdx.x / units;
+  const int unit = blockIdx.x % units;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15, kq = lane >> 4;
+  const int hk_lane = i16 >> 2;   // head of key-output / value-A lanes
+  const int b = unit / a.hkv, hk = unit % a.hkv;
+  const int64_t cap = a.c.cap;
+  const int ngroups = (int)(a.n_main / GS);
+  const int g0 = (int)((int64_t)ngroups * split / a.splits);
+  const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
+  const int wg0 = g0 + (g1 - g0) * wave / kWaves;
+  const int wg1 = g0 + (g1 - g0) * (wave + 1) / kWaves;
+  const int nsteps = (wg1 - wg0) * SPG;
+
+  float *kmS = smem + wave * Gm::PER_WAVE;
+  float *kmZ = kmS + Gm::KM;
+  float *lvS = kmZ + Gm::KM;
+  float *lvZ = lvS + Gm::VM;
+
+  // scaled query for this lane's head and 32 channels
+  float qs[32];
+  {
+    const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * kHpg + hk_lane)) * kHeadDim + 32 * kq;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) qs[c] = h2f(qp[c]) * a.qscale;
+  }
+
+  // identity operand of the transposing MFMA: column n takes K index n
+  u32x2 ident;
+  {
+    const int s = i16 & 3;
+    const uint32_t one = (kq == (i16 >> 2)) ? (0x3F80u << (16 * (s & 1))) : 0u;
+    ident[0] = (s >> 1) == 0 ? one : 0u;
+    ident[1] = (s >> 1) == 1 ? one : 0u;
+  }
+
+  // online-softmax state
+  float m[kHpg], mthr[kHpg];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) m[h] = mthr[h] = -INFINITY;
+  float m_lane = -INFINITY, mthr_lane = -INFINITY;   // for head hk_lane
+  float lsum = 0.0f;    // key-output lanes: weights of head hk_lane (own group slot only)
+  float vbias = 0.0f;   // value-A lanes: zero-point term of (head hk_lane, slice i16 & 3)
+  fx4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = fx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // q' limbs of the current super-chunk, per pass p and word r
+  uint32_t bhi[4][4], blo[4][4];
+  float beta = 0.0f;
+
+  const int64_t ngr_cap = cap / GS;
+  const Rsrc rkc = rsrc_of(a.c.k_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
+  const Rsrc rvc = rsrc_of(a.c.v_codes + (int64_t)unit * cap * W, (uint32_t)(cap * W * 4));
+  const Rsrc rvs = rsrc_of(a.c.v_scale + (int64_t)unit * cap * VGR, (uint32_t)(cap * VGR * 4));
+  const Rsrc rks = rsrc_of(a.c.k_scale + (int64_t)unit * ngr_cap * kHeadDim, (uint32_t)(ngr_cap * kHeadDim * 4));
+  const Rsrc rvz = META ? rvs : rsrc_of(a.c.v_zero + (int64_t)unit * cap * VGR, (uint32_t)(cap * VGR * 2));
+  const Rsrc rkz = META ? rks
+                        : rsrc_of(a.c.k_zero + (int64_t)unit * ngr_cap * kHeadDim, (uint32_t)(ngr_cap * kHeadDim * 2));
+  const uint32_t code_lane = (uint32_t)(i16 * W + WPL * kq) * 4u;
+  // metadata entry of this lane within a step's block of EPS entries
+  const uint32_t mflat = (uint32_t)(SPG == 4 ? (lane & 31) : lane * E);
+
+  auto load = [&](Buf &bf, int s) {
+    s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
+    const uint32_t g = (uint32_t)(wg0 + (s >> LOG_SPG));
+    const uint32_t t0 = g * GS + (uint32_t)((s & (SPG - 1)) * 32);
+    bload_words<WPL>(rkc, code_lane, t0 * (W * 4), bf.kw);
+    bload_words<WPL>(rkc, code_lane, (t0 + 16) * (W * 4), bf.kw + WPL);
+    bload_words<WPL>(rvc, code_lane, t0 * (W * 4), bf.vw);
+    bload_words<WPL>(rvc, code_lane, (t0 + 16) * (W * 4), bf.vw + WPL);
+    bload_words<E>(rvs, mflat * 4, t0 * (VGR * 4), bf.vs);
+    // key metadata chunk s mod SPC of the next super-chunk; the offset goes
+    // in the lane offset so the range check covers groups past the cache
+    const uint32_t gn = (uint32_t)(wg0 + 4 * ((s / SPC) + 1));
+    const uint32_t koff = gn * kHeadDim + (uint32_t)(s % SPC) * EPS + mflat;
+    bload_words<E>(rks, koff * 4, 0, bf.ks);
+    if constexpr (!META) {
+      if constexpr (E == 2) {
+        bf.vz = __builtin_amdgcn_raw_buffer_load_b32(rvz, mflat * 2, t0 * (VGR * 2), kStream);
+        bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, koff * 2, 0, kStream);
+      } else {
+        bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, mflat * 2, t0 * (VGR * 2), kStream);
+        bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, koff * 2, 0, kStream);
+      }
+    } else {
+      bf.vz = bf.kz = 0;
+    }
+  };
+
+  // stage one step's metadata entries (raw words) into LDS: S and Z as floats
+  auto stage_meta = [&](float *dS, float *dZ, const uint32_t *sw, uint32_t zw, uint32_t base, bool vmeta) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float S, Z;
+      decode_meta<META>(sw[e], (zw >> (16 * e)) & 0xffffu, S, Z);
+      const uint32_t f = base + mflat + e;
+      // value metadata is stored [group][token]; key metadata in cache order
+      const uint32_t idx = vmeta ? (f % VGR) * 32 + f / VGR : f;
+      dS[idx] = S;
+      dZ[idx] = Z;
+    }
+  };
+
+  // q' limbs and bias of the super-chunk whose metadata is in kmS / kmZ
+  auto prep = [&]() {
+    const float *sS = kmS + (i16 & 3) * kHeadDim + 32 * kq;
+    const float *sZ = kmZ + (i16 & 3) * kHeadDim + 32 * kq;
+    float qp[32];
+    float bp = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; c += 4) {
+      const float4 S4 = *reinterpret_cast<const float4 *>(sS + c);
+      const float4 Z4 = *reinterpret_cast<const float4 *>(sZ + c);
+      qp[c] = qs[c] * S4.x;
+      qp[c + 1] = qs[c + 1] * S4.y;
+      qp[c + 2] = qs[c + 2] * S4.z;
+      qp[c + 3] = qs[c + 3] * S4.w;
+      bp = fmaf(qp[c], Z4.x, bp);
+      bp = fmaf(qp[c + 1], Z4.y, bp);
+      bp = fmaf(qp[c + 2], Z4.z, bp);
+      bp = fmaf(qp[c + 3], Z4.w, bp);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) limbs(qp[8 * p + pass_chan(r, 0)], qp[8 * p + pass_chan(r, 1)], bhi[p][r], blo[p][r]);
+    }
+    bp += shfl_xor_f(bp, 16);
+    bp += shfl_xor_f(bp, 32);
+    beta = bp;
+  };
+
+  // raise the per-head maxima past the new scores (uniform branch)
+  auto rescale = [&](float mx_valid) {
+    float hm = block_max<4>(mx_valid);   // the quad of a head's group slots
+    hm = fmaxf(hm, shfl_xor_f(hm, 16));
+    hm = fmaxf(hm, shfl_xor_f(hm, 32));
+    float f[kHpg];
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      const float mn = fmaxf(m[h], lane_of(hm, 4 * h));
+      f[h] = (mn == m[h]) ? 1.0f : fast_exp2(m[h] - mn);
+      m[h] = uniform(mn);
+      mthr[h] = uniform(mn + kMargin);
+    }
+    m_lane = sel4(hk_lane, m[0], m[1], m[2], m[3]);
+    mthr_lane = sel4(hk_lane, mthr[0], mthr[1], mthr[2], mthr[3]);
+    const float fk = sel4(hk_lane, f[0], f[1], f[2], f[3]);
+    const float fv = sel4(kq, f[0], f[1], f[2], f[3]);
+    lsum *= fk;
+    vbias *= fk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= fv;
+  };
+
+  auto process = [&](const Buf &bf, int s) {
+    const int gq = (s >> LOG_SPG) & 3;   // group slot of this step in its super-chunk
+    const int kk = s % SPC;
+    if (kk == 0) prep();
+    wave_sync();
+    stage_meta(kmS, kmZ, bf.ks, bf.kz, (uint32_t)kk * EPS, false);   // next super-chunk
+    stage_meta(lvS, lvZ, bf.vs, bf.vz, 0u, true);
+    wave_sync();
+    // value metadata of this lane's 8 tokens (value-A role)
+    float sv[8], zv[8];
+    {
+      const int gcv = (i16 & 3) >> Gm::SH;
+      const float *pS = lvS + gcv * 32 + 4 * kq;
+      const float *pZ = lvZ + gcv * 32 + 4 * kq;
+      const float4 s0 = *reinterpret_cast<const float4 *>(pS);
+      const float4 s1 = *reinterpret_cast<const float4 *>(pS + 16);
+      const float4 z0 = *reinterpret_cast<const float4 *>(pZ);
+      const float4 z1 = *reinterpret_cast<const float4 *>(pZ + 16);
+      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+      sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+      zv[0] = z0.x; zv[1] = z0.y; zv[2] = z0.z; zv[3] = z0.w;
+      zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
+    }
+
+    // key scores of both blocks
+    uint32_t uk[2][16];
+    CodesBf16<BITS>::run(bf.kw, uk[0]);
+    CodesBf16<BITS>::run(bf.kw + WPL, uk[1]);
+    fx4 sc[2];
+    sc[0] = sc[1] = fx4{beta, beta, beta, beta};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x4 bh = {bhi[p][0], bhi[p][1], bhi[p][2], bhi[p][3]};
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        sc[k] = mma_x32(u32x4{uk[k][4 * p], uk[k][4 * p + 1], uk[k][4 * p + 2], uk[k][4 * p + 3]}, bh, sc[k]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x4 bl = {blo[p][0], blo[p][1], blo[p][2], blo[p][3]};
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        sc[k] = mma_x32(u32x4{uk[k][4 * p], uk[k][4 * p + 1], uk[k][4 * p + 2], uk[k][4 * p + 3]}, bl, sc[k]);
+    }
+
+    // softmax weights (valid in the lanes of this step's group slot)
+    const bool valid = (i16 & 3) == gq;
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = valid ? mx : -INFINITY;
+    if (__any(mx > mthr_lane)) rescale(mx);
+    float pw[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[4 * k + r] = fast_exp2(sc[k][r] - m_lane);
+    }
+    const float psum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+    lsum += valid ? psum : 0.0f;
+
+    // weights of the step's group slot to every lane of the quad
+    float pb[8];
+    if (gq == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = dpp<0x00>(pw[j]);
+    } else if (gq == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = dpp<0x55>(pw[j]);
+    } else if (gq == 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = dpp<0xAA>(pw[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = dpp<0xFF>(pw[j]);
+    }
+    u32x4 ahi, alo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float w0 = pb[2 * q] * sv[2 * q], w1 = pb[2 * q + 1] * sv[2 * q + 1];
+      vbias = fmaf(w0, zv[2 * q], vbias);
+      vbias = fmaf(w1, zv[2 * q + 1], vbias);
+      uint32_t h, l;
+      limbs(w0, w1, h, l);
+      ahi[q] = h;
+      alo[q] = l;
+    }
+
+    // values: transpose 16 channels at a time, then the weighted sums
+    uint32_t uv[2][16];
+    CodesBf16<BITS>::run(bf.vw, uv[0]);
+    CodesBf16<BITS>::run(bf.vw + WPL, uv[1]);
+    const fx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const fx4 t0 = mma_x16(u32x2{uv[0][2 * i], uv[0][2 * i + 1]}, ident, z4);
+      const fx4 t1 = mma_x16(u32x2{uv[1][2 * i], uv[1][2 * i + 1]}, ident, z4);
+      const u32x4 bv = {hi_pair(t0[0], t0[1]), hi_pair(t0[2], t0[3]), hi_pair(t1[0], t1[1]), hi_pair(t1[2], t1[3])};
+      acc[i] = mma_x32(ahi, bv, acc[i]);
+      acc[i] = mma_x32(alo, bv, acc[i]);
+    }
+  };
+
+  if (nsteps > 0) {
+    // metadata of the first super-chunk: EPS entries per chunk, SPC chunks
+    for (int k = 0; k < SPC; ++k) {
+      uint32_t sw[E], zw = 0;
+      const uint32_t koff = (uint32_t)wg0 * kHeadDim + (uint32_t)k * EPS + mflat;
+      bload_words<E>(rks, koff * 4, 0, sw);
+      if constexpr (!META) {
+        if constexpr (E == 2) zw = __builtin_amdgcn_raw_buffer_load_b32(rkz, koff * 2, 0, kStream);
+        else zw = __builtin_amdgcn_raw_buffer_load_b16(rkz, koff * 2, 0, kStream);
+      }
+      stage_meta(kmS, kmZ, sw, zw, (uint32_t)k * EPS, false);
+    }
+    Buf A, B, C;
+    asm volatile("" ::: "memory");
+    load(A, 0);
+    asm volatile("" ::: "memory");
+    load(B, 1);
+    asm volatile("" ::: "memory");
+    wave_sync();
+    for (int s = 0; s < nsteps; s += 3) {
+      load(C, s + 2);
+      process(A, s);
+      load(A, s + 3);
+      if (s + 1 < nsteps) process(B, s + 1);
+      load(B, s + 4);
+      if (s + 2 < nsteps) process(C, s + 2);
+    }
+  }
+
+  // ---- combine: per-wave rows [h][128] in LDS, then across waves
+  float L = block_sum<4>(lsum);
+  L += shfl_xor_f(L, 16);
+  L += shfl_xor_f(L, 32);            // weight sum of head hk_lane
+  float vb = vbias + shfl_xor_f(vbias, 16);
+  vb += shfl_xor_f(vb, 32);          // bias of (head hk_lane, slice i16 & 3)
+  const float vbl = __shfl(vb, 4 * kq + (i16 >> 2));   // bias of (head kq, slice i16 >> 2)
+  __syncthreads();                   // every wave is done with its staging area
+  float *rows = smem;                // [kWaves][kHpg][128]
+  float *wml = smem + Gm::ROWS;      // [kWaves][kHpg][2]
+  {
+    const int sl = i16 >> 2;         // useful accumulator row: slice of this lane's channels
+    const int pc = ((i16 & 1) << 1) | ((i16 & 3) >> 1);   // channel offset 0,2,1,3 of column i16 & 3
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = sel4(sl, acc[i][0], acc[i][1], acc[i][2], acc[i][3]) + vbl;
+      rows[(wave * kHpg + kq) * kHeadDim + 32 * sl + 4 * i + pc] = v;
+    }
+  }
+  if (lane < kHpg) {
+    const float mh = sel4(lane, m[0], m[1], m[2], m[3]);
+    wml[(wave * kHpg + lane) * 2] = mh;
+  }
+  if (kq == 0 && (i16 & 3) == 0) wml[(wave * kHpg + hk_lane) * 2 + 1] = L;
+  __syncthreads();
+  static_assert(kHpg * kHeadDim == kThreads, "one merge element per thread");
+  {
+    const int h = tid / kHeadDim, c = tid % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[(w * kHpg + h) * 2]);
+    float accv = 0.0f, Lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = wml[(w * kHpg + h) * 2];
+      const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+      Lt = fmaf(f, wml[(w * kHpg + h) * 2 + 1], Lt);
+      accv = fmaf(f, rows[(w * kHpg + h) * kHeadDim + c], accv);
+    }
+    st.acc[h * kHeadDim + c] = accv;
+    if (c == 0) {
+      st.ml[2 * h] = M;
+      st.ml[2 * h + 1] = Lt;
+    }
+  }
+  __syncthreads();
+  finish_part<kHpg>(a, unit, split, st);
+}
+
+template <int BITS, int GS, int META>
+hipError_t launch_gqa(const AttnArgs &a, int splits, hipStream_t s) {
+  const int units = a.batch * a.hkv;
+  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * splits), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int META>
+hipError_t launch_gqa_by_group(const AttnArgs &a, int splits, hipStream_t s) {
+  switch (a.c.group) {
+    case 32: return launch_gqa<BITS, 32, META>(a, splits, s);
+    case 64: return launch_gqa<BITS, 64, META>(a, splits, s);
+    case 128: return launch_gqa<BITS, 128, META>(a, splits, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gqa_mfma(const AttnArgs &a, hipStream_t s) {
+  if (a.hq != kHpg * a.hkv) return hipErrorInvalidValue;
+  const int splits = a.splits;
+  if (a.c.meta)
+    return (a.c.bits == 2) ? launch_gqa_by_group<2, 1>(a, splits, s) : launch_gqa_by_group<4, 1>(a, splits, s);
+  return (a.c.bits == 2) ? launch_gqa_by_group<2, 0>(a, splits, s) : launch_gqa_by_group<4, 0>(a, splits, s);
+}
+
+}  // namespace kvq

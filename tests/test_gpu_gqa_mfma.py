@@ -1,0 +1,157 @@
+"""GPU parity of the matrix-core kernel for four query heads per kv head
+(KIVI layout): bf16 MFMA tiles with two-limb operands against the float64
+oracle, across bit widths, group sizes, value policies, sink tokens,
+metadata formats and split counts; and against the vector-ALU kernel
+(KVQ_GQA_PATH=valu) on the same cache."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_token_amd as kvq
+import oracle
+from workloads import Workload, gen_new_tokens, gen_prefill, gen_queries
+from gpu_helpers import ATOL, SPLIT_TOL_MFMA, compare_sink_unit, host, max_err, oracle_attention
+
+pytestmark = pytest.mark.gpu
+
+CHUNK, FIFO = kvq.KVQ_V_CHUNK, kvq.KVQ_V_FIFO
+
+
+def _w(cid, B, L, bits, G, R, steps, policy=CHUNK, sinks=0, meta=0, hkv=2):
+    return Workload(f"mfma{cid}", cid, B, 4 * hkv, hkv, 128, L, bits, G, R, 4, 10.0, steps, 1, policy,
+                    sinks=sinks, meta=meta)
+
+
+# (workload, steps at which attention is checked)
+CASES = [
+    (_w(401, 2, 1000, 2, 32, 128, 30), [1, 24, 25, 30]),                     # flush at 25
+    (_w(402, 1, 700, 4, 32, 64, 6), [1, 4, 5, 6]),                           # 4-bit
+    (_w(403, 2, 900, 2, 64, 128, 5, FIFO), [1, 5]),                          # G = 64, FIFO tail part
+    (_w(404, 1, 1500, 4, 128, 128, 3, CHUNK, 0, 1), [1, 3]),                  # G = 128, packed metadata
+    (_w(405, 2, 500, 2, 32, 64, 13, CHUNK, 4, 1), [1, 12, 13]),               # sinks + packed metadata
+    (_w(406, 1, 800, 4, 64, 128, 2, FIFO, 4), [1, 2]),                       # sinks + FIFO: three kinds of parts
+    (_w(407, 3, 97, 2, 32, 32, 40), [1, 31, 32, 40]),                        # a few groups only
+    (_w(408, 1, 5000, 2, 32, 128, 1, CHUNK, 0, 0, 8), [1]),                  # 8 kv heads, ragged split ranges
+]
+
+
+def _ref(w):
+    if w.sinks:
+        return oracle.KiviSinkCache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_kv_heads, 128,
+                                    w.v_policy, w.meta)
+    return oracle.QuantizedKVCache(w.bits, w.group, w.residual, w.batch, w.num_kv_heads, 128, w.v_policy, w.meta)
+
+
+def _cache(w):
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads, 128,
+                          w.max_tokens + w.residual, w.v_policy, kvq.KVQ_SCHEME_KIVI, w.sinks, w.meta)
+    return kvq.KVCache(cfg, "cuda")
+
+
+def _attention(cache, q, path, **kw):
+    old = os.environ.get("KVQ_GQA_PATH")
+    os.environ["KVQ_GQA_PATH"] = path
+    try:
+        out = cache.attention(q, **kw)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["KVQ_GQA_PATH"]
+        else:
+            os.environ["KVQ_GQA_PATH"] = old
+    return out
+
+
+@pytest.mark.parametrize("w,checks", CASES, ids=[c[0].name for c in CASES])
+def test_gqa_mfma_parity(w, checks):
+    print(f"case {w.name} bits={w.bits} G={w.group} R={w.residual} policy={w.v_policy} sinks={w.sinks} "
+          f"meta={w.meta} L={w.context}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    cache, ref = _cache(w), _ref(w)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    scale = 1.0 / math.sqrt(128)
+    for step in range(1, w.steps + 1):
+        cache.append(kn[step - 1].contiguous(), vn[step - 1].contiguous())
+        ref.append(host(kn[step - 1]), host(vn[step - 1]))
+        if step in checks:
+            q = qs[step - 1].contiguous()
+            want = oracle_attention(ref, host(q), scale)
+            out_m = _attention(cache, q, "mfma")
+            out_v = _attention(cache, q, "valu")
+            em, ev = max_err(out_m, want), max_err(out_v, want)
+            print(f"  step {step}: n={ref.n} nq_k={ref.nq_k} nq_v={ref.nq_v} err mfma={em:.2e} valu={ev:.2e}",
+                  flush=True)
+            assert em <= ATOL and ev <= ATOL
+            if w.sinks:
+                for b in range(w.batch):
+                    for h in range(w.num_kv_heads):
+                        compare_sink_unit(cache, ref, b, h)
+
+
+@pytest.mark.parametrize("bits,G", [(2, 32), (4, 64)])
+def test_gqa_mfma_split_counts_and_reruns(bits, G):
+    w = _w(420 + bits, 2, 4000, bits, G, 128, 1)
+    print(f"case {w.name}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    q = gen_queries(w, 0, "cuda")[0].contiguous()
+    cache, ref = _cache(w), _ref(w)
+    cache.prefill(k, v)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    ref.prefill(host(k), host(v))
+    ref.append(host(kn[0]), host(vn[0]))
+    want = oracle_attention(ref, host(q), 1 / math.sqrt(128))
+    outs = []
+    for s in (1, 2, 7, 31, 64, 0):
+        o = _attention(cache, q, "mfma", workspace=cache.workspace(splits=s), splits=s)
+        err = max_err(o, want)
+        print(f"  splits {s}: err {err:.2e}", flush=True)
+        assert err <= ATOL, s
+        outs.append(host(o))
+    for o in outs[1:]:
+        assert float(np.abs(o - outs[0]).max()) <= SPLIT_TOL_MFMA
+    assert np.array_equal(host(_attention(cache, q, "mfma")), outs[-1]), "reruns must be bit-identical"
+
+
+def test_gqa_mfma_fused_step_matches_append_then_attention():
+    w = _w(430, 2, 300, 2, 32, 64, 40)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    a, b, ref = _cache(w), _cache(w), _ref(w)
+    a.prefill(k, v)
+    b.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    for i in range(w.steps):
+        q = qs[i].contiguous()
+        oa = a.step(kn[i].contiguous(), vn[i].contiguous(), q)
+        b.append(kn[i].contiguous(), vn[i].contiguous())
+        ob = b.attention(q)
+        ref.append(host(kn[i]), host(vn[i]))
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), i
+    assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
+
+
+def test_gqa_mfma_large_magnitudes():
+    """Keys and queries scaled up 64x: the bf16 limbs keep fp32 range, so the
+    result still matches the oracle to the same bound."""
+    w = _w(440, 1, 600, 2, 32, 128, 1)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    q = gen_queries(w, 0, "cuda")[0].contiguous()
+    k, kn0, q = (k.float() * 64).half(), (kn[0].float() * 64).half(), (q.float() / 8).half()
+    cache, ref = _cache(w), _ref(w)
+    cache.prefill(k, v)
+    cache.append(kn0.contiguous(), vn[0].contiguous())
+    ref.prefill(host(k), host(v))
+    ref.append(host(kn0), host(vn[0]))
+    err = max_err(_attention(cache, q, "mfma"), oracle_attention(ref, host(q), 1 / math.sqrt(128)))
+    print(f"  err {err:.2e}", flush=True)
+    assert err <= ATOL
