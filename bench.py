@@ -81,7 +81,19 @@ KERNELS = {
         "decode_attn_llama2_7b_2bit_traffic.txt"),
     1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_internal.h"),
         "innerq_attn_b4_h32_L131072_4bit_traffic.txt"),
+    "gqa4": ("gqa_mfma_kernel", ("kvq_attn_gqa.hip", "kvq_attn_common.h", "kvq_internal.h"),
+             "gqa_mfma_b8_q32_kv8_L32768_2bit_traffic.txt"),
 }
+
+
+def kernel_key(w):
+    """Which decode kernel dominates the workload: the matrix-core kernel for
+    four query heads per kv head (KIVI layout, unless KVQ_GQA_PATH=valu),
+    else the scheme's vector-ALU kernel."""
+    if (w.scheme == kvq.KVQ_SCHEME_KIVI and w.num_q_heads == 4 * w.num_kv_heads
+            and os.environ.get("KVQ_GQA_PATH") != "valu"):
+        return "gqa4"
+    return w.scheme
 
 
 def kernel_source_digest(scheme=0):
@@ -98,12 +110,12 @@ def measured_traffic(w):
     summary, or None when it is missing, for another workload, or taken on a
     different kernel source."""
     try:
-        with open(os.path.join(ROOT, "profiles", KERNELS[w.scheme][2])) as f:
+        with open(os.path.join(ROOT, "profiles", KERNELS[kernel_key(w)][2])) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("kernel_source_digest") != kernel_source_digest(w.scheme) or kv.get("workload") != w.name:
+    if kv.get("kernel_source_digest") != kernel_source_digest(kernel_key(w)) or kv.get("workload") != w.name:
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -367,7 +379,7 @@ def main():
                    "meta": "f16-packed" if w.meta else "f32+i16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
-                     "kernel": KERNELS[w.scheme][0], "avg_call_us": round(call_us, 2),
+                     "kernel": KERNELS[kernel_key(w)][0], "avg_call_us": round(call_us, 2),
                      "bytes_per_call": int(call_bytes)},
     }
     if side is not None:

@@ -117,7 +117,7 @@ int64_t main_tokens(const kvq_config *c, const kvq_cache *k) {
 // sixteen key groups, two per wave) in every split.
 int32_t auto_splits_for(const kvq_config *c, int64_t nq) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
-  int64_t s = (512 + units - 1) / units;
+  int64_t s = (512 + units - 1) / units;   // 512 workgroups: two per CU
   const int64_t by_work = is_innerq(c) ? nq / 512 : nq / c->group / 16;
   if (s > by_work) s = by_work;
   if (s < 1) s = 1;

@@ -48,6 +48,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <utility>
+
 #include "kvq_internal.h"
 #include "kvq_attn_common.h"
 
@@ -62,6 +64,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHpg = 4;   // query heads per kv head on this path
+// Four waves per workgroup, two waves per SIMD (up to 256 VGPRs: the
+// accumulators, both q' limb sets and a three-step load ring stay in
+// registers; at three waves per SIMD the kernel spills and runs slower).
+constexpr int kGqaWaves = 4;
+constexpr int kGqaThreads = kGqaWaves * kWave;
+constexpr int kGqaWavesPerEU = 2;
+
 
 __device__ __forceinline__ fx4 mma_x32(u32x4 a, u32x4 b, fx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0,
@@ -95,55 +104,48 @@ __device__ __forceinline__ void limbs(float a, float b, uint32_t &hi, uint32_t &
 }
 
 // A lane's 32 codes (channels 32 kq .. 32 kq + 31 of one token) as 16 words of
-// exact bf16 pairs.  Word 4p + r holds channels 8p + {0,2}, {1,3}, {4,6},
-// {5,7} for r = 0..3 (the order the converts produce; the key preparation
-// arranges q' the same way).
+// exact bf16 pairs, produced one word at a time from the raw code words w[].
+// Word 4p + r holds channels 8p + {0,2}, {1,3}, {4,6}, {5,7} for r = 0..3
+// (the order the converts produce; the key preparation arranges q' the same
+// way).  J is a compile-time index: the converts take a literal byte select.
 template <int BITS>
 struct CodesBf16;
-
-// Byte B of x as two fp4 nibbles -> bf16 pair; nibble c is worth c / 2, so
-// scale 2 gives the code itself.
-template <int B>
-__device__ __forceinline__ uint32_t fp4_pair(uint32_t x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, B));
-}
 
 template <>
 struct CodesBf16<2> {
   static constexpr int WPL = 2;   // code words per lane per token
-  __device__ static __forceinline__ void run(const uint32_t *w, uint32_t *u) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t m0 = w[k] & 0x33333333u;          // nibble i: code 2i
-      const uint32_t m1 = (w[k] >> 2) & 0x33333333u;   // nibble i: code 2i + 1
-      u[8 * k + 0] = fp4_pair<0>(m0);
-      u[8 * k + 1] = fp4_pair<0>(m1);
-      u[8 * k + 2] = fp4_pair<1>(m0);
-      u[8 * k + 3] = fp4_pair<1>(m1);
-      u[8 * k + 4] = fp4_pair<2>(m0);
-      u[8 * k + 5] = fp4_pair<2>(m1);
-      u[8 * k + 6] = fp4_pair<3>(m0);
-      u[8 * k + 7] = fp4_pair<3>(m1);
-    }
+  template <int J>
+  __device__ static __forceinline__ uint32_t word(const uint32_t *w) {
+    constexpr int k = J / 8, b = (J % 8) / 2;
+    // nibble i of m holds code 2i (even J) or 2i + 1 (odd J); fp4 nibble c is
+    // worth c / 2, so scale 2 gives the code itself
+    const uint32_t m = ((J & 1) ? (w[k] >> 2) : w[k]) & 0x33333333u;
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, b));
   }
 };
 
 template <>
 struct CodesBf16<4> {
   static constexpr int WPL = 4;
-  __device__ static __forceinline__ void run(const uint32_t *w, uint32_t *u) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t m0 = w[k] & 0x0F0F0F0Fu;          // byte i: code 2i
-      const uint32_t m1 = (w[k] >> 4) & 0x0F0F0F0Fu;   // byte i: code 2i + 1
-      // fp8 e4m3 byte c (c < 16) is worth c / 512: scale 512
-      u[4 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, false));
-      u[4 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, false));
-      u[4 * k + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, true));
-      u[4 * k + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, true));
-    }
+  template <int J>
+  __device__ static __forceinline__ uint32_t word(const uint32_t *w) {
+    constexpr int k = J / 4, r = J % 4;
+    // byte i of m holds code 2i (r even) or 2i + 1 (r odd); fp8 e4m3 byte c
+    // (c < 16) is worth c / 512, so scale 512 gives the code itself
+    const uint32_t m = ((r & 1) ? (w[k] >> 4) : w[k]) & 0x0F0F0F0Fu;
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m, 512.0f, r >= 2));
   }
 };
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Channel offset (within 8) of element e of word r of a pass: 0,2 | 1,3 | 4,6 | 5,7.
 __device__ __host__ constexpr int pass_chan(int r, int e) { return (r >> 1) * 4 + (r & 1) + 2 * e; }
@@ -161,10 +163,11 @@ struct GqaGeo {
   static constexpr int KM = 4 * kHeadDim;
   static constexpr int VM = VGR * 32;
   static constexpr int PER_WAVE = 2 * KM + 2 * VM;
-  static constexpr int ROWS = kWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
-  static constexpr int WORK = (kWaves * PER_WAVE > ROWS + 2 * kWaves * kHpg) ? kWaves * PER_WAVE
-                                                                              : ROWS + 2 * kWaves * kHpg;
-  static constexpr int SMEM = WORK + kStageFloats<kHpg>;
+  static constexpr int ROWS = kGqaWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
+  static constexpr int STAGING = kGqaWaves * PER_WAVE;
+  static constexpr int WORK = (STAGING > ROWS + 2 * kGqaWaves * kHpg) ? STAGING : ROWS + 2 * kGqaWaves * kHpg;
+  static constexpr int QS = kHpg * kHeadDim;                  // scaled query [h][128]
+  static constexpr int SMEM = WORK + QS + kStageFloats<kHpg>;
 };
 
 template <int BITS, int GS>
@@ -177,6 +180,12 @@ struct GqaBuf {
   uint32_t vs[E];         // value metadata of this step
   uint32_t kz, vz;        // int16 zero-points (fp32 metadata only)
 };
+
+// Lane L of each quad to all four lanes of the quad.
+template <int L>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), L * 0x55, 0xF, 0xF, true));
+}
 
 __device__ __forceinline__ float sel4(int i, float a, float b, float c, float d) {
   return i == 0 ? a : (i == 1 ? b : (i == 2 ? c : d));
@@ -197,7 +206,7 @@ __device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, flo
 }
 
 template <int BITS, int GS, int META>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(kGqaWavesPerEU, kGqaWavesPerEU)))
 void gqa_mfma_kernel(AttnArgs a) {
   using Gm = GqaGeo<GS>;
   using Buf = GqaBuf<BITS, GS>;
@@ -206,7 +215,8 @@ void gqa_mfma_kernel(AttnArgs a) {
   constexpr int LOG_SPG = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);
 
   __shared__ __attribute__((aligned(16))) float smem[Gm::SMEM];
-  const Stage st = stage_of<kHpg>(smem, Gm::WORK);
+  const Stage st = stage_of<kHpg>(smem, Gm::WORK + Gm::QS);
+  float *qsm = smem + Gm::WORK;   // scaled query [h][128], shared by the workgroup's waves
 
   const int units = a.batch * a.hkv;
   const int split = blockIdx.x / units;
@@ -220,8 +230,8 @@ void gqa_mfma_kernel(AttnArgs a) {
   const int ngroups = (int)(a.n_main / GS);
   const int g0 = (int)((int64_t)ngroups * split / a.splits);
   const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
-  const int wg0 = g0 + (g1 - g0) * wave / kWaves;
-  const int wg1 = g0 + (g1 - g0) * (wave + 1) / kWaves;
+  const int wg0 = g0 + (g1 - g0) * wave / kGqaWaves;
+  const int wg1 = g0 + (g1 - g0) * (wave + 1) / kGqaWaves;
   const int nsteps = (wg1 - wg0) * SPG;
 
   float *kmS = smem + wave * Gm::PER_WAVE;
@@ -229,13 +239,10 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *lvS = kmZ + Gm::KM;
   float *lvZ = lvS + Gm::VM;
 
-  // scaled query for this lane's head and 32 channels
-  float qs[32];
-  {
-    const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * kHpg + hk_lane)) * kHeadDim + 32 * kq;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) qs[c] = h2f(qp[c]) * a.qscale;
-  }
+  // scaled query of the unit's four heads
+  for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads)
+    qsm[i] = h2f(a.q[((int64_t)(b * a.hq + hk * kHpg)) * kHeadDim + i]) * a.qscale;
+  __syncthreads();
 
   // identity operand of the transposing MFMA: column n takes K index n
   u32x2 ident;
@@ -318,16 +325,18 @@ void gqa_mfma_kernel(AttnArgs a) {
   auto prep = [&]() {
     const float *sS = kmS + (i16 & 3) * kHeadDim + 32 * kq;
     const float *sZ = kmZ + (i16 & 3) * kHeadDim + 32 * kq;
+    const float *sq = qsm + hk_lane * kHeadDim + 32 * kq;
     float qp[32];
     float bp = 0.0f;
 #pragma unroll
     for (int c = 0; c < 32; c += 4) {
       const float4 S4 = *reinterpret_cast<const float4 *>(sS + c);
       const float4 Z4 = *reinterpret_cast<const float4 *>(sZ + c);
-      qp[c] = qs[c] * S4.x;
-      qp[c + 1] = qs[c + 1] * S4.y;
-      qp[c + 2] = qs[c + 2] * S4.z;
-      qp[c + 3] = qs[c + 3] * S4.w;
+      const float4 Q4 = *reinterpret_cast<const float4 *>(sq + c);
+      qp[c] = Q4.x * S4.x;
+      qp[c + 1] = Q4.y * S4.y;
+      qp[c + 2] = Q4.z * S4.z;
+      qp[c + 3] = Q4.w * S4.w;
       bp = fmaf(qp[c], Z4.x, bp);
       bp = fmaf(qp[c + 1], Z4.y, bp);
       bp = fmaf(qp[c + 2], Z4.z, bp);
@@ -374,6 +383,50 @@ void gqa_mfma_kernel(AttnArgs a) {
     stage_meta(kmS, kmZ, bf.ks, bf.kz, (uint32_t)kk * EPS, false);   // next super-chunk
     stage_meta(lvS, lvZ, bf.vs, bf.vz, 0u, true);
     wave_sync();
+    // key scores of both blocks; the high and low limb products accumulate
+    // separately so four MFMA chains interleave
+    fx4 sc[2], sl2[2];
+    sc[0] = sc[1] = fx4{beta, beta, beta, beta};
+    sl2[0] = sl2[1] = fx4{0.0f, 0.0f, 0.0f, 0.0f};
+    static_for<4>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      using C = CodesBf16<BITS>;
+      const u32x4 bh = {bhi[p][0], bhi[p][1], bhi[p][2], bhi[p][3]};
+      const u32x4 bl = {blo[p][0], blo[p][1], blo[p][2], blo[p][3]};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t *w = bf.kw + k * WPL;
+        const u32x4 ak = {C::template word<4 * p>(w), C::template word<4 * p + 1>(w), C::template word<4 * p + 2>(w),
+                          C::template word<4 * p + 3>(w)};
+        sc[k] = mma_x32(ak, bh, sc[k]);
+        sl2[k] = mma_x32(ak, bl, sl2[k]);
+      }
+    });
+    sc[0] += sl2[0];
+    sc[1] += sl2[1];
+
+    // softmax weights (valid in the lanes of this step's group slot)
+    const bool valid = (i16 & 3) == gq;
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) over |= sc[k][r] > mthr_lane;
+    }
+    if (__any(over && valid)) {
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      rescale(valid ? mx : -INFINITY);
+    }
+    float pw[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[4 * k + r] = fast_exp2(sc[k][r] - m_lane);
+    }
+    const float psum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+    lsum += valid ? psum : 0.0f;
+
     // value metadata of this lane's 8 tokens (value-A role)
     float sv[8], zv[8];
     {
@@ -390,56 +443,20 @@ void gqa_mfma_kernel(AttnArgs a) {
       zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
     }
 
-    // key scores of both blocks
-    uint32_t uk[2][16];
-    CodesBf16<BITS>::run(bf.kw, uk[0]);
-    CodesBf16<BITS>::run(bf.kw + WPL, uk[1]);
-    fx4 sc[2];
-    sc[0] = sc[1] = fx4{beta, beta, beta, beta};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const u32x4 bh = {bhi[p][0], bhi[p][1], bhi[p][2], bhi[p][3]};
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        sc[k] = mma_x32(u32x4{uk[k][4 * p], uk[k][4 * p + 1], uk[k][4 * p + 2], uk[k][4 * p + 3]}, bh, sc[k]);
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const u32x4 bl = {blo[p][0], blo[p][1], blo[p][2], blo[p][3]};
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        sc[k] = mma_x32(u32x4{uk[k][4 * p], uk[k][4 * p + 1], uk[k][4 * p + 2], uk[k][4 * p + 3]}, bl, sc[k]);
-    }
-
-    // softmax weights (valid in the lanes of this step's group slot)
-    const bool valid = (i16 & 3) == gq;
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = valid ? mx : -INFINITY;
-    if (__any(mx > mthr_lane)) rescale(mx);
-    float pw[8];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[4 * k + r] = fast_exp2(sc[k][r] - m_lane);
-    }
-    const float psum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-    lsum += valid ? psum : 0.0f;
-
     // weights of the step's group slot to every lane of the quad
     float pb[8];
     if (gq == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = dpp<0x00>(pw[j]);
+      for (int j = 0; j < 8; ++j) pb[j] = quad_bcast<0>(pw[j]);
     } else if (gq == 1) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = dpp<0x55>(pw[j]);
+      for (int j = 0; j < 8; ++j) pb[j] = quad_bcast<1>(pw[j]);
     } else if (gq == 2) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = dpp<0xAA>(pw[j]);
+      for (int j = 0; j < 8; ++j) pb[j] = quad_bcast<2>(pw[j]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = dpp<0xFF>(pw[j]);
+      for (int j = 0; j < 8; ++j) pb[j] = quad_bcast<3>(pw[j]);
     }
     u32x4 ahi, alo;
 #pragma unroll
@@ -454,18 +471,17 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
 
     // values: transpose 16 channels at a time, then the weighted sums
-    uint32_t uv[2][16];
-    CodesBf16<BITS>::run(bf.vw, uv[0]);
-    CodesBf16<BITS>::run(bf.vw + WPL, uv[1]);
     const fx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const fx4 t0 = mma_x16(u32x2{uv[0][2 * i], uv[0][2 * i + 1]}, ident, z4);
-      const fx4 t1 = mma_x16(u32x2{uv[1][2 * i], uv[1][2 * i + 1]}, ident, z4);
+    static_for<8>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      using C = CodesBf16<BITS>;
+      const fx4 t0 = mma_x16(u32x2{C::template word<2 * i>(bf.vw), C::template word<2 * i + 1>(bf.vw)}, ident, z4);
+      const fx4 t1 = mma_x16(u32x2{C::template word<2 * i>(bf.vw + WPL), C::template word<2 * i + 1>(bf.vw + WPL)},
+                             ident, z4);
       const u32x4 bv = {hi_pair(t0[0], t0[1]), hi_pair(t0[2], t0[3]), hi_pair(t1[0], t1[1]), hi_pair(t1[2], t1[3])};
       acc[i] = mma_x32(ahi, bv, acc[i]);
       acc[i] = mma_x32(alo, bv, acc[i]);
-    }
+    });
   };
 
   if (nsteps > 0) {
@@ -505,8 +521,8 @@ void gqa_mfma_kernel(AttnArgs a) {
   vb += shfl_xor_f(vb, 32);          // bias of (head hk_lane, slice i16 & 3)
   const float vbl = __shfl(vb, 4 * kq + (i16 >> 2));   // bias of (head kq, slice i16 >> 2)
   __syncthreads();                   // every wave is done with its staging area
-  float *rows = smem;                // [kWaves][kHpg][128]
-  float *wml = smem + Gm::ROWS;      // [kWaves][kHpg][2]
+  float *rows = smem;                // [kGqaWaves][kHpg][128]
+  float *wml = smem + Gm::ROWS;      // [kGqaWaves][kHpg][2]
   {
     const int sl = i16 >> 2;         // useful accumulator row: slice of this lane's channels
     const int pc = ((i16 & 1) << 1) | ((i16 & 3) >> 1);   // channel offset 0,2,1,3 of column i16 & 3
@@ -522,15 +538,15 @@ void gqa_mfma_kernel(AttnArgs a) {
   }
   if (kq == 0 && (i16 & 3) == 0) wml[(wave * kHpg + hk_lane) * 2 + 1] = L;
   __syncthreads();
-  static_assert(kHpg * kHeadDim == kThreads, "one merge element per thread");
-  {
-    const int h = tid / kHeadDim, c = tid % kHeadDim;
+  static_assert((kHpg * kHeadDim) % kGqaThreads == 0, "whole merge passes");
+  for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads) {
+    const int h = i / kHeadDim, c = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[(w * kHpg + h) * 2]);
+    for (int w = 0; w < kGqaWaves; ++w) M = fmaxf(M, wml[(w * kHpg + h) * 2]);
     float accv = 0.0f, Lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kGqaWaves; ++w) {
       const float mw = wml[(w * kHpg + h) * 2];
       const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
       Lt = fmaf(f, wml[(w * kHpg + h) * 2 + 1], Lt);
@@ -549,7 +565,7 @@ void gqa_mfma_kernel(AttnArgs a) {
 template <int BITS, int GS, int META>
 hipError_t launch_gqa(const AttnArgs &a, int splits, hipStream_t s) {
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * splits), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * splits), dim3(kGqaThreads), 0, s, a);
   return hipGetLastError();
 }
 
