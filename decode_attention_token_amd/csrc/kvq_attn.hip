@@ -215,7 +215,7 @@ void decode_attn_kernel(AttnArgs a) {
   if (a.tail_wg) {
     if (blk < units) {
       decode_tail<BITS, HPG>(a, blk, smem, st);
-      finish_part<HPG>(a, blk, a.part_base + a.splits, st);
+      finish_part<HPG>(a, blk, a.splits, st);
       return;
     }
     blk -= units;
@@ -228,7 +228,7 @@ void decode_attn_kernel(AttnArgs a) {
   const int j = lane % LPT, tl = lane / LPT;
   const int b = unit / a.hkv, hk = unit % a.hkv;
   const int64_t cap = a.c.cap;
-  const int ngroups = a.skip_main ? 0 : (int)(a.n_main / GS);
+  const int ngroups = (int)(a.n_main / GS);
   const int g0 = (int)((int64_t)ngroups * split / a.splits);
   const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
   const int wg0 = g0 + (g1 - g0) * wave / kWaves;
@@ -468,7 +468,7 @@ void decode_attn_kernel(AttnArgs a) {
   }
 
   combine_waves<HPG, LPT, NVG>(o, smem, st, wave, lane, INV_U);
-  finish_part<HPG>(a, unit, a.part_base + split, st);
+  finish_part<HPG>(a, unit, split, st);
 }
 
 // Merge of the part records: m = max m_i, l = sum l_i 2^(m_i - m),
@@ -546,25 +546,17 @@ bool gqa_mfma_enabled() {
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
   hipError_t e;
-  // fp16 tokens (sinks, chunked residual) and the mixed FIFO tail are parts
-  // of their own next to the matrix-core parts; the workspace holds
-  // splits + 1 records per head, so with both the matrix cores take one
-  // split fewer
-  const int fp16_part = (a.nsink > 0 || a.resid_main) ? 1 : 0;
-  const int rest = fp16_part + a.tail_wg;
-  const int msplits = rest == 2 ? a.splits - 1 : a.splits;
-  if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && msplits >= 1 && gqa_mfma_enabled()) {
+  // four query heads per kv head: the matrix-core kernel, whose extra
+  // workgroups (one per unit) take the sinks and tokens [n_main, n) as one
+  // more part
+  const int64_t rest_tokens = a.nsink + (a.n - a.n_main);
+  if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && a.splits >= 1 && rest_tokens <= kGqaMaxRest &&
+      gqa_mfma_enabled()) {
     AttnArgs m = a;
-    m.splits = msplits;
-    m.nparts = msplits + rest;
+    m.tail_wg = rest_tokens > 0 ? 1 : 0;
+    m.resid_main = 0;
+    m.nparts = m.splits + m.tail_wg;
     if ((e = launch_gqa_mfma(m, s)) != hipSuccess) return e;
-    if (rest > 0) {
-      AttnArgs v = m;
-      v.skip_main = 1;
-      v.part_base = msplits;
-      v.splits = fp16_part;
-      if ((e = launch_valu(v, s)) != hipSuccess) return e;
-    }
     return launch_merge(m, s);
   }
   if ((e = launch_valu(a, s)) != hipSuccess) return e;

@@ -64,6 +64,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHpg = 4;   // query heads per kv head on this path
+// Tokens the fp16 part can take: sinks (<= 512), the residual (<= 512) and a
+// partial key group (< 128).
+constexpr int kMaxRest = kGqaMaxRest;
+
+// Lane byte offset past every buffer this kernel reads (resources cover at
+// most 2^31 bytes): such a load returns zero and touches no memory.
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 // Four waves per workgroup, two waves per SIMD (up to 256 VGPRs: the
 // accumulators, both q' limb sets and a three-step load ring stay in
 // registers; at three waves per SIMD the kernel spills and runs slower).
@@ -165,7 +172,9 @@ struct GqaGeo {
   static constexpr int PER_WAVE = 2 * KM + 2 * VM;
   static constexpr int ROWS = kGqaWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
   static constexpr int STAGING = kGqaWaves * PER_WAVE;
-  static constexpr int WORK = (STAGING > ROWS + 2 * kGqaWaves * kHpg) ? STAGING : ROWS + 2 * kGqaWaves * kHpg;
+  static constexpr int COMBINE = ROWS + 2 * kGqaWaves * kHpg;
+  static constexpr int REST = kHpg * kMaxRest + 2 * kHpg * kHeadDim;   // fp16-part scores + half sums
+  static constexpr int WORK = STAGING > COMBINE ? (STAGING > REST ? STAGING : REST) : (COMBINE > REST ? COMBINE : REST);
   static constexpr int QS = kHpg * kHeadDim;                  // scaled query [h][128]
   static constexpr int SMEM = WORK + QS + kStageFloats<kHpg>;
 };
@@ -205,6 +214,148 @@ __device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, flo
   }
 }
 
+// The unit's fp16 part: sink rows [0, nsink) and tokens [n_main, n), whose
+// keys and values are each quantized (rows below nq_k / nq_v) or fp16 (ring
+// slot t mod R, or k_new / v_new for token n - 1 of a fused step).  Plain
+// dequantize-then-dot: 16 lanes per token for the scores (8 channels each),
+// one wave per head for the softmax, a thread per channel and token parity
+// for P.V.  Leaves the part's (acc, max, sum) in st.
+static_assert(kGqaWaves == kHpg, "the fp16 part runs one wave per head in its softmax");
+
+template <int BITS, int META>
+__device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const float *qsm, const Stage &st) {
+  constexpr int PER = 32 / BITS;
+  constexpr int W = kHeadDim / PER;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  const int G = a.c.group, VGR = kHeadDim / G, R = a.c.residual, S = a.c.sinks;
+  const int64_t cap = a.c.cap;
+  const int ns = a.nsink;
+  const int nt = ns + (int)(a.n - a.n_main);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float *s_sc = smem;                         // [kHpg][nt] scores, then weights
+  float *s_half = smem + kHpg * kMaxRest;     // [2][kHpg][128]
+  if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
+    // fused step: the new token goes into its ring slot
+    constexpr int CH = kHeadDim * 2 / 16;
+    const int which = tid / CH, ch = tid % CH;
+    const uint4 *src = reinterpret_cast<const uint4 *>((which ? a.v_new : a.k_new) + (int64_t)unit * kHeadDim);
+    uint4 *dst = reinterpret_cast<uint4 *>((which ? a.c.v_resid : a.c.k_resid) +
+                                           ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
+    dst[ch] = src[ch];
+  }
+  // scores: lanes 16 sub .. 16 sub + 15 take token i0 + sub, lane j channels 8j .. 8j + 7
+  const int j = lane & 15, sub = lane >> 4;
+  float qv[kHpg][8];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[h][e] = qsm[h * kHeadDim + 8 * j + e];
+  }
+  for (int i0 = wave * 4; i0 < nt; i0 += kGqaWaves * 4) {
+    const int i = i0 + sub;
+    float kf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[e] = 0.0f;
+    if (i < nt) {
+      const uint16_t *row = nullptr;
+      if (i < ns) {
+        row = a.c.k_sink + ((int64_t)unit * S + i) * kHeadDim;
+      } else {
+        const int64_t t = a.n_main + (i - ns);
+        if (t < a.nq_k) {
+          const uint32_t w = a.c.k_codes[((int64_t)unit * cap + t) * W + (8 * j) / PER];
+          const int sh = ((8 * j) % PER) * BITS;
+          const int64_t mi = ((int64_t)unit * (cap / G) + t / G) * kHeadDim + 8 * j;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float Sc, Z;
+            if constexpr (META) {
+              const uint32_t mw = reinterpret_cast<const uint32_t *>(a.c.k_scale)[mi + e];
+              decode_meta<1>(mw, 0, Sc, Z);
+            } else {
+              decode_meta<0>(__float_as_uint(a.c.k_scale[mi + e]), (uint16_t)a.c.k_zero[mi + e], Sc, Z);
+            }
+            kf[e] = ((float)((w >> (sh + e * BITS)) & MASK) + Z) * Sc;
+          }
+        } else {
+          row = (a.k_new != nullptr && t == a.n - 1) ? a.k_new + (int64_t)unit * kHeadDim
+                                                     : a.c.k_resid + ((int64_t)unit * R + t % R) * kHeadDim;
+        }
+      }
+      if (row != nullptr) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(row + 8 * j);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[2 * e] = h2f((uint16_t)(w4[e] & 0xffffu));
+          kf[2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
+      d = block_sum<16>(d);
+      if (j == 0 && i < nt) s_sc[h * nt + i] = d;
+    }
+  }
+  __syncthreads();
+  {
+    const int h = wave;   // one wave per head
+    float mx = -INFINITY;
+    for (int i = lane; i < nt; i += kWave) mx = fmaxf(mx, s_sc[h * nt + i]);
+    mx = wave_max(mx);
+    float l = 0.0f;
+    for (int i = lane; i < nt; i += kWave) {
+      const float p = exp2f(s_sc[h * nt + i] - mx);
+      s_sc[h * nt + i] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      st.ml[2 * h] = nt > 0 ? mx : -INFINITY;
+      st.ml[2 * h + 1] = l;
+    }
+  }
+  __syncthreads();
+  const int c = tid & (kHeadDim - 1), half = tid >> 7;
+  float acc[kHpg];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) acc[h] = 0.0f;
+  for (int i = half; i < nt; i += 2) {
+    float v;
+    if (i < ns) {
+      v = h2f(a.c.v_sink[((int64_t)unit * S + i) * kHeadDim + c]);
+    } else {
+      const int64_t t = a.n_main + (i - ns);
+      if (t < a.nq_v) {
+        const uint32_t w = a.c.v_codes[((int64_t)unit * cap + t) * W + c / PER];
+        const int64_t mi = ((int64_t)unit * cap + t) * VGR + c / G;
+        float Sc, Z;
+        if constexpr (META) {
+          decode_meta<1>(reinterpret_cast<const uint32_t *>(a.c.v_scale)[mi], 0, Sc, Z);
+        } else {
+          decode_meta<0>(__float_as_uint(a.c.v_scale[mi]), (uint16_t)a.c.v_zero[mi], Sc, Z);
+        }
+        v = ((float)((w >> ((c % PER) * BITS)) & MASK) + Z) * Sc;
+      } else if (a.v_new != nullptr && t == a.n - 1) {
+        v = h2f(a.v_new[(int64_t)unit * kHeadDim + c]);
+      } else {
+        v = h2f(a.c.v_resid[((int64_t)unit * R + t % R) * kHeadDim + c]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) acc[h] = fmaf(s_sc[h * nt + i], v, acc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) s_half[(half * kHpg + h) * kHeadDim + c] = acc[h];
+  __syncthreads();
+  for (int idx = tid; idx < kHpg * kHeadDim; idx += kGqaThreads) st.acc[idx] = s_half[idx] + s_half[kHpg * kHeadDim + idx];
+  __syncthreads();
+}
+
 template <int BITS, int GS, int META>
 __global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(kGqaWavesPerEU, kGqaWavesPerEU)))
 void gqa_mfma_kernel(AttnArgs a) {
@@ -219,8 +370,12 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *qsm = smem + Gm::WORK;   // scaled query [h][128], shared by the workgroup's waves
 
   const int units = a.batch * a.hkv;
-  const int split = blockIdx.x / units;
-  const int unit = blockIdx.x % units;
+  // the first units workgroups (when a.tail_wg) take the fp16 part of their
+  // unit; the others split its quantized groups
+  const bool rest_wg = a.tail_wg && (int)blockIdx.x < units;
+  const int blk = (int)blockIdx.x - (a.tail_wg ? units : 0);
+  const int split = rest_wg ? a.splits : blk / units;
+  const int unit = rest_wg ? (int)blockIdx.x : blk % units;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, kq = lane >> 4;
@@ -243,6 +398,11 @@ void gqa_mfma_kernel(AttnArgs a) {
   for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads)
     qsm[i] = h2f(a.q[((int64_t)(b * a.hq + hk * kHpg)) * kHeadDim + i]) * a.qscale;
   __syncthreads();
+  if (rest_wg) {
+    gqa_fp16_part<BITS, META>(a, unit, smem, qsm, st);
+    finish_part<kHpg>(a, unit, split, st);
+    return;
+  }
 
   // identity operand of the transposing MFMA: column n takes K index n
   u32x2 ident;
@@ -289,18 +449,21 @@ void gqa_mfma_kernel(AttnArgs a) {
     bload_words<WPL>(rvc, code_lane, t0 * (W * 4), bf.vw);
     bload_words<WPL>(rvc, code_lane, (t0 + 16) * (W * 4), bf.vw + WPL);
     bload_words<E>(rvs, mflat * 4, t0 * (VGR * 4), bf.vs);
-    // key metadata chunk s mod SPC of the next super-chunk; the offset goes
-    // in the lane offset so the range check covers groups past the cache
+    // key metadata chunk s mod SPC of the next super-chunk; entries of
+    // groups past the wave's range get an out-of-range lane offset, so they
+    // read zero without touching memory
     const uint32_t gn = (uint32_t)(wg0 + 4 * ((s / SPC) + 1));
-    const uint32_t koff = gn * kHeadDim + (uint32_t)(s % SPC) * EPS + mflat;
-    bload_words<E>(rks, koff * 4, 0, bf.ks);
+    const uint32_t kent = (uint32_t)(s % SPC) * EPS + mflat;   // entry within the super-chunk
+    const bool kneed = gn + (kent / kHeadDim) < (uint32_t)wg1;
+    const uint32_t koff = gn * kHeadDim + kent;
+    bload_words<E>(rks, kneed ? koff * 4 : kOutOfRange, 0, bf.ks);
     if constexpr (!META) {
       if constexpr (E == 2) {
         bf.vz = __builtin_amdgcn_raw_buffer_load_b32(rvz, mflat * 2, t0 * (VGR * 2), kStream);
-        bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, koff * 2, 0, kStream);
+        bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
       } else {
         bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, mflat * 2, t0 * (VGR * 2), kStream);
-        bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, koff * 2, 0, kStream);
+        bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
       }
     } else {
       bf.vz = bf.kz = 0;
@@ -488,11 +651,13 @@ void gqa_mfma_kernel(AttnArgs a) {
     // metadata of the first super-chunk: EPS entries per chunk, SPC chunks
     for (int k = 0; k < SPC; ++k) {
       uint32_t sw[E], zw = 0;
-      const uint32_t koff = (uint32_t)wg0 * kHeadDim + (uint32_t)k * EPS + mflat;
-      bload_words<E>(rks, koff * 4, 0, sw);
+      const uint32_t kent = (uint32_t)k * EPS + mflat;
+      const bool kneed = (uint32_t)wg0 + (kent / kHeadDim) < (uint32_t)wg1;
+      const uint32_t koff = (uint32_t)wg0 * kHeadDim + kent;
+      bload_words<E>(rks, kneed ? koff * 4 : kOutOfRange, 0, sw);
       if constexpr (!META) {
-        if constexpr (E == 2) zw = __builtin_amdgcn_raw_buffer_load_b32(rkz, koff * 2, 0, kStream);
-        else zw = __builtin_amdgcn_raw_buffer_load_b16(rkz, koff * 2, 0, kStream);
+        if constexpr (E == 2) zw = __builtin_amdgcn_raw_buffer_load_b32(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
+        else zw = __builtin_amdgcn_raw_buffer_load_b16(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
       }
       stage_meta(kmS, kmZ, sw, zw, (uint32_t)k * EPS, false);
     }
@@ -565,7 +730,8 @@ void gqa_mfma_kernel(AttnArgs a) {
 template <int BITS, int GS, int META>
 hipError_t launch_gqa(const AttnArgs &a, int splits, hipStream_t s) {
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * splits), dim3(kGqaThreads), 0, s, a);
+  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * (splits + a.tail_wg)), dim3(kGqaThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 

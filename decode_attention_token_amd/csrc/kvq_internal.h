@@ -87,18 +87,15 @@ struct AttnArgs {
   // slot.  Null when the token was appended beforehand.
   const uint16_t *k_new;
   const uint16_t *v_new;
-  // Part numbering when one unit's parts come from two kernels: this launch
-  // writes parts part_base + [0, splits + tail_wg); skip_main = 1 leaves the
-  // quantized groups [0, n_main) to the other kernel.
-  int part_base = 0;
-  int skip_main = 0;
 };
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s);
 
 // Matrix-core kernel for four query heads per kv head (KIVI layout): the
-// quantized groups [0, n_main) in a.splits parts [0, a.splits); writes the
-// normalized output when a.nparts == 1.
+// quantized groups [0, n_main) in a.splits parts [0, a.splits) and, when
+// a.tail_wg, the sinks and tokens [n_main, n) (at most kGqaMaxRest of them)
+// as part a.splits; writes the normalized output when a.nparts == 1.
+constexpr int kGqaMaxRest = 512 + 512 + 127;
 hipError_t launch_gqa_mfma(const AttnArgs &a, hipStream_t s);
 
 // InnerQ-style attention: quantized tokens [min(n, sinks), nq_k) split over
