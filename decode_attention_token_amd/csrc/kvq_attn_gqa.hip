@@ -173,7 +173,7 @@ struct GqaGeo {
   static constexpr int ROWS = kGqaWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
   static constexpr int STAGING = kGqaWaves * PER_WAVE;
   static constexpr int COMBINE = ROWS + 2 * kGqaWaves * kHpg;
-  static constexpr int REST = kHpg * kMaxRest + 2 * kHpg * kHeadDim;   // fp16-part scores + half sums
+  static constexpr int REST = kHpg * kMaxRest + kGqaWaves * kHpg * kHeadDim;   // fp16-part scores + wave sums
   static constexpr int WORK = STAGING > COMBINE ? (STAGING > REST ? STAGING : REST) : (COMBINE > REST ? COMBINE : REST);
   static constexpr int QS = kHpg * kHeadDim;                  // scaled query [h][128]
   static constexpr int SMEM = WORK + QS + kStageFloats<kHpg>;
@@ -217,23 +217,64 @@ __device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, flo
 // The unit's fp16 part: sink rows [0, nsink) and tokens [n_main, n), whose
 // keys and values are each quantized (rows below nq_k / nq_v) or fp16 (ring
 // slot t mod R, or k_new / v_new for token n - 1 of a fused step).  Plain
-// dequantize-then-dot: 16 lanes per token for the scores (8 channels each),
-// one wave per head for the softmax, a thread per channel and token parity
-// for P.V.  Leaves the part's (acc, max, sum) in st.
+// dequantize-then-dot.  Scores: 16 lanes per token (8 channels each), four
+// tokens per wave at a time.  Softmax: one wave per head.  P.V: 16 token
+// slots x 16 channel octets.  Row loads of kRestBatch rounds are issued
+// before any of them is used, so the part costs a few memory round trips.
+// Leaves the part's (acc, max, sum) in st.
+constexpr int kRestBatch = 8;
+
+// 8 channels (8 c .. 8 c + 7) of token i of the fp16 part, as raw fp16 pairs
+// (fp16 rows) or dequantized (quantized rows, via `quant`).
+struct RestRow {
+  const uint16_t *row;   // fp16 row, or null for a quantized one
+  int64_t t;             // token index when quantized
+};
+
+template <int BITS, int META>
+__device__ __forceinline__ void dequant8(const uint32_t *codes, const float *scale, const int16_t *zero, int64_t unit,
+                                         int64_t cap, int64_t t, int c8, int G, bool keys, float *out) {
+  constexpr int PER = 32 / BITS;
+  constexpr int W = kHeadDim / PER;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  const uint32_t w = codes[(unit * cap + t) * W + (8 * c8) / PER];
+  const int sh = ((8 * c8) % PER) * BITS;
+  // keys: (S, Z) per (group of G tokens, channel); values: per (token, group
+  // of G channels) -- the 8 channels share one value group since G >= 32
+  const int64_t mi = keys ? (unit * (cap / G) + t / G) * kHeadDim + 8 * c8 : (unit * cap + t) * (kHeadDim / G) + (8 * c8) / G;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float Sc, Z;
+    const int64_t m = keys ? mi + e : mi;
+    if constexpr (META) {
+      decode_meta<1>(reinterpret_cast<const uint32_t *>(scale)[m], 0, Sc, Z);
+    } else {
+      decode_meta<0>(__float_as_uint(scale[m]), (uint16_t)zero[m], Sc, Z);
+    }
+    out[e] = ((float)((w >> (sh + e * BITS)) & MASK) + Z) * Sc;
+  }
+}
+
+__device__ __forceinline__ void fp16x8(uint4 v, float *out) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    out[2 * e] = h2f((uint16_t)(w4[e] & 0xffffu));
+    out[2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
+  }
+}
+
 static_assert(kGqaWaves == kHpg, "the fp16 part runs one wave per head in its softmax");
 
 template <int BITS, int META>
 __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const float *qsm, const Stage &st) {
-  constexpr int PER = 32 / BITS;
-  constexpr int W = kHeadDim / PER;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  const int G = a.c.group, VGR = kHeadDim / G, R = a.c.residual, S = a.c.sinks;
+  const int G = a.c.group, R = a.c.residual, S = a.c.sinks;
   const int64_t cap = a.c.cap;
   const int ns = a.nsink;
   const int nt = ns + (int)(a.n - a.n_main);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float *s_sc = smem;                         // [kHpg][nt] scores, then weights
-  float *s_half = smem + kHpg * kMaxRest;     // [2][kHpg][128]
+  float *s_red = smem + kHpg * kMaxRest;      // [kGqaWaves][kHpg][128]
   if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
     // fused step: the new token goes into its ring slot
     constexpr int CH = kHeadDim * 2 / 16;
@@ -243,62 +284,53 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
                                            ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
     dst[ch] = src[ch];
   }
-  // scores: lanes 16 sub .. 16 sub + 15 take token i0 + sub, lane j channels 8j .. 8j + 7
-  const int j = lane & 15, sub = lane >> 4;
-  float qv[kHpg][8];
-#pragma unroll
-  for (int h = 0; h < kHpg; ++h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[h][e] = qsm[h * kHeadDim + 8 * j + e];
-  }
-  for (int i0 = wave * 4; i0 < nt; i0 += kGqaWaves * 4) {
-    const int i = i0 + sub;
-    float kf[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kf[e] = 0.0f;
-    if (i < nt) {
-      const uint16_t *row = nullptr;
-      if (i < ns) {
-        row = a.c.k_sink + ((int64_t)unit * S + i) * kHeadDim;
-      } else {
-        const int64_t t = a.n_main + (i - ns);
-        if (t < a.nq_k) {
-          const uint32_t w = a.c.k_codes[((int64_t)unit * cap + t) * W + (8 * j) / PER];
-          const int sh = ((8 * j) % PER) * BITS;
-          const int64_t mi = ((int64_t)unit * (cap / G) + t / G) * kHeadDim + 8 * j;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float Sc, Z;
-            if constexpr (META) {
-              const uint32_t mw = reinterpret_cast<const uint32_t *>(a.c.k_scale)[mi + e];
-              decode_meta<1>(mw, 0, Sc, Z);
-            } else {
-              decode_meta<0>(__float_as_uint(a.c.k_scale[mi + e]), (uint16_t)a.c.k_zero[mi + e], Sc, Z);
-            }
-            kf[e] = ((float)((w >> (sh + e * BITS)) & MASK) + Z) * Sc;
-          }
-        } else {
-          row = (a.k_new != nullptr && t == a.n - 1) ? a.k_new + (int64_t)unit * kHeadDim
-                                                     : a.c.k_resid + ((int64_t)unit * R + t % R) * kHeadDim;
-        }
-      }
-      if (row != nullptr) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(row + 8 * j);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = h2f((uint16_t)(w4[e] & 0xffffu));
-          kf[2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
-        }
-      }
-    }
+  // row of token i of the part for keys (k = true) or values
+  auto row_of = [&](int i, bool k) -> RestRow {
+    if (i < ns) return {(k ? a.c.k_sink : a.c.v_sink) + ((int64_t)unit * S + i) * kHeadDim, 0};
+    const int64_t t = a.n_main + (i - ns);
+    if (t < (k ? a.nq_k : a.nq_v)) return {nullptr, t};
+    if ((k ? a.k_new : a.v_new) != nullptr && t == a.n - 1)
+      return {(k ? a.k_new : a.v_new) + (int64_t)unit * kHeadDim, 0};
+    return {(k ? a.c.k_resid : a.c.v_resid) + ((int64_t)unit * R + t % R) * kHeadDim, 0};
+  };
+
+  // ---- scores: lane j of token group sub takes channels 8j .. 8j + 7
+  {
+    const int j = lane & 15, sub = lane >> 4;
+    float qv[kHpg][8];
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) {
-      float d = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
-      d = block_sum<16>(d);
-      if (j == 0 && i < nt) s_sc[h * nt + i] = d;
+      for (int e = 0; e < 8; ++e) qv[h][e] = qsm[h * kHeadDim + 8 * j + e];
+    }
+    constexpr int STRIDE = kGqaWaves * 4;   // tokens per round
+    for (int i0 = wave * 4 + sub; i0 < nt; i0 += STRIDE * kRestBatch) {
+      uint4 raw[kRestBatch];
+      RestRow rr[kRestBatch];
+#pragma unroll
+      for (int r = 0; r < kRestBatch; ++r) {
+        const int i = i0 + r * STRIDE;
+        rr[r] = i < nt ? row_of(i, true) : RestRow{nullptr, -1};
+        raw[r] = rr[r].row != nullptr ? *reinterpret_cast<const uint4 *>(rr[r].row + 8 * j) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < kRestBatch; ++r) {
+        const int i = i0 + r * STRIDE;
+        float kf[8];
+        if (rr[r].row != nullptr || rr[r].t < 0) {
+          fp16x8(raw[r], kf);
+        } else {
+          dequant8<BITS, META>(a.c.k_codes, a.c.k_scale, a.c.k_zero, unit, cap, rr[r].t, j, G, true, kf);
+        }
+#pragma unroll
+        for (int h = 0; h < kHpg; ++h) {
+          float d = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(qv[h][e], kf[e], d);
+          d = block_sum<16>(d);
+          if (j == 0 && i < nt) s_sc[h * nt + i] = d;
+        }
+      }
     }
   }
   __syncthreads();
@@ -320,39 +352,69 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
     }
   }
   __syncthreads();
-  const int c = tid & (kHeadDim - 1), half = tid >> 7;
-  float acc[kHpg];
+  // ---- P.V: thread (token slot ts, channel octet c8)
+  {
+    const int c8 = tid & 15, ts = tid >> 4;
+    float acc[kHpg][8];
 #pragma unroll
-  for (int h = 0; h < kHpg; ++h) acc[h] = 0.0f;
-  for (int i = half; i < nt; i += 2) {
-    float v;
-    if (i < ns) {
-      v = h2f(a.c.v_sink[((int64_t)unit * S + i) * kHeadDim + c]);
-    } else {
-      const int64_t t = a.n_main + (i - ns);
-      if (t < a.nq_v) {
-        const uint32_t w = a.c.v_codes[((int64_t)unit * cap + t) * W + c / PER];
-        const int64_t mi = ((int64_t)unit * cap + t) * VGR + c / G;
-        float Sc, Z;
-        if constexpr (META) {
-          decode_meta<1>(reinterpret_cast<const uint32_t *>(a.c.v_scale)[mi], 0, Sc, Z);
+    for (int h = 0; h < kHpg; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    }
+    constexpr int SLOTS = kGqaThreads / 16;
+    for (int i0 = ts; i0 < nt; i0 += SLOTS * kRestBatch) {
+      uint4 raw[kRestBatch];
+      RestRow rr[kRestBatch];
+#pragma unroll
+      for (int r = 0; r < kRestBatch; ++r) {
+        const int i = i0 + r * SLOTS;
+        rr[r] = i < nt ? row_of(i, false) : RestRow{nullptr, -1};
+        raw[r] = rr[r].row != nullptr ? *reinterpret_cast<const uint4 *>(rr[r].row + 8 * c8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < kRestBatch; ++r) {
+        const int i = i0 + r * SLOTS;
+        if (i >= nt) continue;
+        float vf[8];
+        if (rr[r].row != nullptr) {
+          fp16x8(raw[r], vf);
         } else {
-          decode_meta<0>(__float_as_uint(a.c.v_scale[mi]), (uint16_t)a.c.v_zero[mi], Sc, Z);
+          dequant8<BITS, META>(a.c.v_codes, a.c.v_scale, a.c.v_zero, unit, cap, rr[r].t, c8, G, false, vf);
         }
-        v = ((float)((w >> ((c % PER) * BITS)) & MASK) + Z) * Sc;
-      } else if (a.v_new != nullptr && t == a.n - 1) {
-        v = h2f(a.v_new[(int64_t)unit * kHeadDim + c]);
-      } else {
-        v = h2f(a.c.v_resid[((int64_t)unit * R + t % R) * kHeadDim + c]);
+#pragma unroll
+        for (int h = 0; h < kHpg; ++h) {
+          const float p = s_sc[h * nt + i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
       }
     }
+    // sum the four token slots of each wave (lanes xor 16, xor 32), then the waves
 #pragma unroll
-    for (int h = 0; h < kHpg; ++h) acc[h] = fmaf(s_sc[h * nt + i], v, acc[h]);
+    for (int h = 0; h < kHpg; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[h][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[h][e] = v;
+      }
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int h = 0; h < kHpg; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_red[(wave * kHpg + h) * kHeadDim + 8 * c8 + e] = acc[h][e];
+      }
+    }
   }
-#pragma unroll
-  for (int h = 0; h < kHpg; ++h) s_half[(half * kHpg + h) * kHeadDim + c] = acc[h];
   __syncthreads();
-  for (int idx = tid; idx < kHpg * kHeadDim; idx += kGqaThreads) st.acc[idx] = s_half[idx] + s_half[kHpg * kHeadDim + idx];
+  for (int idx = tid; idx < kHpg * kHeadDim; idx += kGqaThreads) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) v += s_red[w * kHpg * kHeadDim + idx];
+    st.acc[idx] = v;
+  }
   __syncthreads();
 }
 
