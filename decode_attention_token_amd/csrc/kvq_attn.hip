@@ -546,16 +546,15 @@ bool gqa_mfma_enabled() {
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
   hipError_t e;
-  // four query heads per kv head: the matrix-core kernel, whose extra
-  // workgroups (one per unit) take the sinks and tokens [n_main, n) as one
-  // more part
+  // four query heads per kv head: the matrix-core kernel; each split also
+  // takes a share of the sinks and tokens [n_main, n)
   const int64_t rest_tokens = a.nsink + (a.n - a.n_main);
   if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && a.splits >= 1 && rest_tokens <= kGqaMaxRest &&
       gqa_mfma_enabled()) {
     AttnArgs m = a;
-    m.tail_wg = rest_tokens > 0 ? 1 : 0;
+    m.tail_wg = 0;
     m.resid_main = 0;
-    m.nparts = m.splits + m.tail_wg;
+    m.nparts = m.splits;
     if ((e = launch_gqa_mfma(m, s)) != hipSuccess) return e;
     return launch_merge(m, s);
   }

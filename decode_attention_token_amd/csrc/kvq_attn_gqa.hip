@@ -29,10 +29,11 @@
 //    the four groups of a "super-chunk", so one preparation of q' serves 4G
 //    tokens.  Output lane (column n, row block r) holds 4 tokens' scores for
 //    column n; only columns of the step's own group slot are used.
-//  * value codes are transposed to tokens-along-K by an identity MFMA
-//    (16x16x16): lane (channel, r) then holds the codes of tokens 4r..4r+3 of
-//    each block, which is exactly the token set whose scores the same lane
-//    index holds in the key output.
+//  * value codes are transposed to tokens-along-K through LDS: each wave
+//    writes its step's bf16 codes as token rows and reads them back with the
+//    gfx950 transposing LDS read (16-bit elements), so lane (channel, r)
+//    holds the codes of tokens 4r..4r+3 of each block -- exactly the token
+//    set whose scores the same lane index holds in the key output.
 //  * value MFMA (16x16x32): A = w limbs, rows = (head, 32-channel slice),
 //    K = the 32 tokens; B = transposed codes, columns = 16 channels.  The
 //    weights move from the key output lanes to the A lanes with one quad
@@ -62,6 +63,8 @@ typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kHpg = 4;   // query heads per kv head on this path
 // Tokens the fp16 part can take: sinks (<= 512), the residual (<= 512) and a
@@ -82,17 +85,6 @@ constexpr int kGqaWavesPerEU = 2;
 __device__ __forceinline__ fx4 mma_x32(u32x4 a, u32x4 b, fx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0,
                                                  0, 0);
-}
-
-__device__ __forceinline__ fx4 mma_x16(u32x2 a, u32x2 b, fx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf4_t, a), __builtin_bit_cast(bf4_t, b), c,
-                                                   0, 0, 0);
-}
-
-// bf16 pair (lo = a, hi = b) of the upper halves of two fp32 values: the
-// values truncated to bf16 (exact for small integers).
-__device__ __forceinline__ uint32_t hi_pair(float a, float b) {
-  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // bf16 pair (lo = a, hi = b), each rounded to nearest even.
@@ -154,6 +146,9 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Row length (u16) of the per-wave bf16 value-code tile.
+constexpr int kVRow = kHeadDim + 8;
+
 // Channel offset (within 8) of element e of word r of a pass: 0,2 | 1,3 | 4,6 | 5,7.
 __device__ __host__ constexpr int pass_chan(int r, int e) { return (r >> 1) * 4 + (r & 1) + 2 * e; }
 
@@ -169,14 +164,18 @@ struct GqaGeo {
   // value S and Z of a step [VGR][32]
   static constexpr int KM = 4 * kHeadDim;
   static constexpr int VM = VGR * 32;
-  static constexpr int PER_WAVE = 2 * KM + 2 * VM;
+  // value codes of a step as bf16, [32 tokens][kVRow] u16 (rows padded by 8
+  // elements so the 16 rows of a 16-token block start on different banks)
+  static constexpr int VT = 32 * kVRow / 2;
+  static constexpr int PER_WAVE = 2 * KM + 2 * VM + VT;
   static constexpr int ROWS = kGqaWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
   static constexpr int STAGING = kGqaWaves * PER_WAVE;
   static constexpr int COMBINE = ROWS + 2 * kGqaWaves * kHpg;
   static constexpr int REST = kHpg * kMaxRest + kGqaWaves * kHpg * kHeadDim;   // fp16-part scores + wave sums
   static constexpr int WORK = STAGING > COMBINE ? (STAGING > REST ? STAGING : REST) : (COMBINE > REST ? COMBINE : REST);
   static constexpr int QS = kHpg * kHeadDim;                  // scaled query [h][128]
-  static constexpr int SMEM = WORK + QS + kStageFloats<kHpg>;
+  static constexpr int STAGE2 = kStageFloats<kHpg>;                // second result: the fp16 share
+  static constexpr int SMEM = WORK + QS + kStageFloats<kHpg> + kHpg * kHeadDim + 2 * kHpg;
 };
 
 template <int BITS, int GS>
@@ -185,9 +184,14 @@ struct GqaBuf {
   static constexpr int E = GqaGeo<GS>::E;
   uint32_t kw[2 * WPL];   // key code words, block 0 then block 1
   uint32_t vw[2 * WPL];
-  uint32_t ks[E];         // key metadata of the next super-chunk (S, or packed S | Z)
-  uint32_t vs[E];         // value metadata of this step
-  uint32_t kz, vz;        // int16 zero-points (fp32 metadata only)
+  uint32_t vs[E];         // value metadata of this step (S, or packed S | Z)
+  uint32_t vz;            // int16 zero-points (fp32 metadata only)
+};
+
+// Key metadata of one super-chunk (4 groups x 128 channels = 512 entries),
+// entries 8 lane .. 8 lane + 7: raw S (or packed S | Z) words and int16 Z.
+struct GqaKMeta {
+  uint4 s0, s1, z;
 };
 
 // Lane L of each quad to all four lanes of the quad.
@@ -214,14 +218,14 @@ __device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, flo
   }
 }
 
-// The unit's fp16 part: sink rows [0, nsink) and tokens [n_main, n), whose
-// keys and values are each quantized (rows below nq_k / nq_v) or fp16 (ring
-// slot t mod R, or k_new / v_new for token n - 1 of a fused step).  Plain
-// dequantize-then-dot.  Scores: 16 lanes per token (8 channels each), four
+// A share of the unit's fp16 list -- sink rows [0, nsink), then tokens
+// [n_main, n), whose keys and values are each quantized (rows below nq_k /
+// nq_v) or fp16 (ring slot t mod R, or k_new / v_new for token n - 1 of a
+// fused step): entries [ib, ie).  Plain dequantize-then-dot.  Scores: 16 lanes per token (8 channels each), four
 // tokens per wave at a time.  Softmax: one wave per head.  P.V: 16 token
 // slots x 16 channel octets.  Row loads of kRestBatch rounds are issued
 // before any of them is used, so the part costs a few memory round trips.
-// Leaves the part's (acc, max, sum) in st.
+// Leaves the share's (acc, max, sum) in out_acc / out_ml.
 constexpr int kRestBatch = 8;
 
 // 8 channels (8 c .. 8 c + 7) of token i of the fp16 part, as raw fp16 pairs
@@ -267,25 +271,18 @@ __device__ __forceinline__ void fp16x8(uint4 v, float *out) {
 static_assert(kGqaWaves == kHpg, "the fp16 part runs one wave per head in its softmax");
 
 template <int BITS, int META>
-__device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const float *qsm, const Stage &st) {
+__device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const float *qsm, float *out_acc,
+                              float *out_ml, int ib, int ie) {
   const int G = a.c.group, R = a.c.residual, S = a.c.sinks;
   const int64_t cap = a.c.cap;
   const int ns = a.nsink;
-  const int nt = ns + (int)(a.n - a.n_main);
+  const int nt = ie - ib;                     // tokens [ib, ie) of the unit's fp16 list
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float *s_sc = smem;                         // [kHpg][nt] scores, then weights
   float *s_red = smem + kHpg * kMaxRest;      // [kGqaWaves][kHpg][128]
-  if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
-    // fused step: the new token goes into its ring slot
-    constexpr int CH = kHeadDim * 2 / 16;
-    const int which = tid / CH, ch = tid % CH;
-    const uint4 *src = reinterpret_cast<const uint4 *>((which ? a.v_new : a.k_new) + (int64_t)unit * kHeadDim);
-    uint4 *dst = reinterpret_cast<uint4 *>((which ? a.c.v_resid : a.c.k_resid) +
-                                           ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
-    dst[ch] = src[ch];
-  }
-  // row of token i of the part for keys (k = true) or values
-  auto row_of = [&](int i, bool k) -> RestRow {
+  // row of local token li (list entry ib + li) for keys (k = true) or values
+  auto row_of = [&](int li, bool k) -> RestRow {
+    const int i = ib + li;
     if (i < ns) return {(k ? a.c.k_sink : a.c.v_sink) + ((int64_t)unit * S + i) * kHeadDim, 0};
     const int64_t t = a.n_main + (i - ns);
     if (t < (k ? a.nq_k : a.nq_v)) return {nullptr, t};
@@ -347,8 +344,8 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
     }
     l = wave_sum(l);
     if (lane == 0) {
-      st.ml[2 * h] = nt > 0 ? mx : -INFINITY;
-      st.ml[2 * h + 1] = l;
+      out_ml[2 * h] = nt > 0 ? mx : -INFINITY;
+      out_ml[2 * h + 1] = l;
     }
   }
   __syncthreads();
@@ -413,7 +410,7 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < kGqaWaves; ++w) v += s_red[w * kHpg * kHeadDim + idx];
-    st.acc[idx] = v;
+    out_acc[idx] = v;
   }
   __syncthreads();
 }
@@ -432,12 +429,8 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *qsm = smem + Gm::WORK;   // scaled query [h][128], shared by the workgroup's waves
 
   const int units = a.batch * a.hkv;
-  // the first units workgroups (when a.tail_wg) take the fp16 part of their
-  // unit; the others split its quantized groups
-  const bool rest_wg = a.tail_wg && (int)blockIdx.x < units;
-  const int blk = (int)blockIdx.x - (a.tail_wg ? units : 0);
-  const int split = rest_wg ? a.splits : blk / units;
-  const int unit = rest_wg ? (int)blockIdx.x : blk % units;
+  const int split = (int)blockIdx.x / units;
+  const int unit = (int)blockIdx.x % units;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, kq = lane >> 4;
@@ -455,25 +448,21 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *kmZ = kmS + Gm::KM;
   float *lvS = kmZ + Gm::KM;
   float *lvZ = lvS + Gm::VM;
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lvZ + Gm::VM);   // bf16 value codes [32][kVRow]
 
   // scaled query of the unit's four heads
   for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads)
     qsm[i] = h2f(a.q[((int64_t)(b * a.hq + hk * kHpg)) * kHeadDim + i]) * a.qscale;
   __syncthreads();
-  if (rest_wg) {
-    gqa_fp16_part<BITS, META>(a, unit, smem, qsm, st);
-    finish_part<kHpg>(a, unit, split, st);
-    return;
-  }
 
-  // identity operand of the transposing MFMA: column n takes K index n
-  u32x2 ident;
-  {
-    const int s = i16 & 3;
-    const uint32_t one = (kq == (i16 >> 2)) ? (0x3F80u << (16 * (s & 1))) : 0u;
-    ident[0] = (s >> 1) == 0 ? one : 0u;
-    ident[1] = (s >> 1) == 1 ? one : 0u;
-  }
+  // value codes: lane (token i16 of block k, kq) writes its 32 bf16 codes
+  // (convert order) at row 16k + i16, positions 32 kq ..; the transposed
+  // reads then give lane (column i16, kq) positions c0 + i16 of tokens
+  // 4 kq + e (first read) and 16 + 4 kq + e (second read), e = 0..3: input
+  // lane j of a 16-lane group supplies row 4 kq + j / 4, positions
+  // c0 + 4 (j mod 4) .. + 3
+  uint16_t *vt_w = vt + i16 * kVRow + 32 * kq;
+  const uint16_t *vt_r = vt + (4 * kq + (i16 >> 2)) * kVRow + 4 * (i16 & 3);
 
   // online-softmax state
   float m[kHpg], mthr[kHpg];
@@ -502,7 +491,38 @@ void gqa_mfma_kernel(AttnArgs a) {
   // metadata entry of this lane within a step's block of EPS entries
   const uint32_t mflat = (uint32_t)(SPG == 4 ? (lane & 31) : lane * E);
 
+  // key metadata of the super-chunk starting at group gfirst, in two or three
+  // 16-byte loads per lane; entries of groups past the wave's range get an
+  // out-of-range lane offset, so they read zero without touching memory
+  auto load_kmeta = [&](GqaKMeta &km, uint32_t gfirst) {
+    const bool kneed = gfirst + (uint32_t)(lane >> 4) < (uint32_t)wg1;
+    const uint32_t koff = gfirst * kHeadDim + 8u * (uint32_t)lane;
+    const uint32_t so = kneed ? koff * 4 : kOutOfRange;
+    km.s0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, so, 0, kStream));
+    km.s1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, kneed ? so + 16 : kOutOfRange, 0, kStream));
+    if constexpr (!META) {
+      km.z = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream));
+    } else {
+      km.z = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage_kmeta = [&](const GqaKMeta &km) {
+    const uint32_t sw[8] = {km.s0.x, km.s0.y, km.s0.z, km.s0.w, km.s1.x, km.s1.y, km.s1.z, km.s1.w};
+    const uint32_t zw[4] = {km.z.x, km.z.y, km.z.z, km.z.w};
+    float S[8], Z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) decode_meta<META>(sw[e], (zw[e / 2] >> (16 * (e & 1))) & 0xffffu, S[e], Z[e]);
+    *reinterpret_cast<float4 *>(kmS + 8 * lane) = make_float4(S[0], S[1], S[2], S[3]);
+    *reinterpret_cast<float4 *>(kmS + 8 * lane + 4) = make_float4(S[4], S[5], S[6], S[7]);
+    *reinterpret_cast<float4 *>(kmZ + 8 * lane) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+    *reinterpret_cast<float4 *>(kmZ + 8 * lane + 4) = make_float4(Z[4], Z[5], Z[6], Z[7]);
+  };
+  GqaKMeta kmr;   // key metadata of the next super-chunk, loaded at its predecessor's first step
+
   auto load = [&](Buf &bf, int s) {
+    // key metadata of the next super-chunk with the loads of a super-chunk's
+    // first step; staged into LDS at its second step, after the preparation
+    if (s < nsteps && s % SPC == 0) load_kmeta(kmr, (uint32_t)(wg0 + 4 * (s / SPC + 1)));
     s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
     const uint32_t g = (uint32_t)(wg0 + (s >> LOG_SPG));
     const uint32_t t0 = g * GS + (uint32_t)((s & (SPG - 1)) * 32);
@@ -511,38 +531,28 @@ void gqa_mfma_kernel(AttnArgs a) {
     bload_words<WPL>(rvc, code_lane, t0 * (W * 4), bf.vw);
     bload_words<WPL>(rvc, code_lane, (t0 + 16) * (W * 4), bf.vw + WPL);
     bload_words<E>(rvs, mflat * 4, t0 * (VGR * 4), bf.vs);
-    // key metadata chunk s mod SPC of the next super-chunk; entries of
-    // groups past the wave's range get an out-of-range lane offset, so they
-    // read zero without touching memory
-    const uint32_t gn = (uint32_t)(wg0 + 4 * ((s / SPC) + 1));
-    const uint32_t kent = (uint32_t)(s % SPC) * EPS + mflat;   // entry within the super-chunk
-    const bool kneed = gn + (kent / kHeadDim) < (uint32_t)wg1;
-    const uint32_t koff = gn * kHeadDim + kent;
-    bload_words<E>(rks, kneed ? koff * 4 : kOutOfRange, 0, bf.ks);
     if constexpr (!META) {
       if constexpr (E == 2) {
         bf.vz = __builtin_amdgcn_raw_buffer_load_b32(rvz, mflat * 2, t0 * (VGR * 2), kStream);
-        bf.kz = __builtin_amdgcn_raw_buffer_load_b32(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
       } else {
         bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, mflat * 2, t0 * (VGR * 2), kStream);
-        bf.kz = __builtin_amdgcn_raw_buffer_load_b16(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
       }
     } else {
-      bf.vz = bf.kz = 0;
+      bf.vz = 0;
     }
   };
 
-  // stage one step's metadata entries (raw words) into LDS: S and Z as floats
-  auto stage_meta = [&](float *dS, float *dZ, const uint32_t *sw, uint32_t zw, uint32_t base, bool vmeta) {
+  // stage one step's value metadata entries (raw words) into LDS as
+  // [group][token] floats
+  auto stage_vmeta = [&](const uint32_t *sw, uint32_t zw) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float S, Z;
       decode_meta<META>(sw[e], (zw >> (16 * e)) & 0xffffu, S, Z);
-      const uint32_t f = base + mflat + e;
-      // value metadata is stored [group][token]; key metadata in cache order
-      const uint32_t idx = vmeta ? (f % VGR) * 32 + f / VGR : f;
-      dS[idx] = S;
-      dZ[idx] = Z;
+      const uint32_t f = mflat + e;
+      const uint32_t idx = (f % VGR) * 32 + f / VGR;
+      lvS[idx] = S;
+      lvZ[idx] = Z;
     }
   };
 
@@ -605,8 +615,20 @@ void gqa_mfma_kernel(AttnArgs a) {
     const int kk = s % SPC;
     if (kk == 0) prep();
     wave_sync();
-    stage_meta(kmS, kmZ, bf.ks, bf.kz, (uint32_t)kk * EPS, false);   // next super-chunk
-    stage_meta(lvS, lvZ, bf.vs, bf.vz, 0u, true);
+    if (kk == 1) stage_kmeta(kmr);   // next super-chunk (its first step is at least SPC away)
+    stage_vmeta(bf.vs, bf.vz);
+    // bf16 value codes of both blocks into the tile
+    static_for<2>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      using C = CodesBf16<BITS>;
+      const uint32_t *w = bf.vw + k * WPL;
+      static_for<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
+            make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
+                       C::template word<4 * q + 3>(w));
+      });
+    });
     wave_sync();
     // key scores of both blocks; the high and low limb products accumulate
     // separately so four MFMA chains interleave
@@ -695,33 +717,24 @@ void gqa_mfma_kernel(AttnArgs a) {
       alo[q] = l;
     }
 
-    // values: transpose 16 channels at a time, then the weighted sums
-    const fx4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    static_for<8>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      using C = CodesBf16<BITS>;
-      const fx4 t0 = mma_x16(u32x2{C::template word<2 * i>(bf.vw), C::template word<2 * i + 1>(bf.vw)}, ident, z4);
-      const fx4 t1 = mma_x16(u32x2{C::template word<2 * i>(bf.vw + WPL), C::template word<2 * i + 1>(bf.vw + WPL)},
-                             ident, z4);
-      const u32x4 bv = {hi_pair(t0[0], t0[1]), hi_pair(t0[2], t0[3]), hi_pair(t1[0], t1[1]), hi_pair(t1[2], t1[3])};
-      acc[i] = mma_x32(ahi, bv, acc[i]);
-      acc[i] = mma_x32(alo, bv, acc[i]);
+    // values: 16 channel positions at a time, transposed by the LDS reads
+    static_for<8>([&](auto cc) {
+      constexpr int cb = decltype(cc)::value;
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * cb));
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * kVRow + 16 * cb));
+      const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+      const u32x4 bv = {h0[0], h0[1], h1[0], h1[1]};
+      acc[cb] = mma_x32(ahi, bv, acc[cb]);
+      acc[cb] = mma_x32(alo, bv, acc[cb]);
     });
   };
 
   if (nsteps > 0) {
-    // metadata of the first super-chunk: EPS entries per chunk, SPC chunks
-    for (int k = 0; k < SPC; ++k) {
-      uint32_t sw[E], zw = 0;
-      const uint32_t kent = (uint32_t)k * EPS + mflat;
-      const bool kneed = (uint32_t)wg0 + (kent / kHeadDim) < (uint32_t)wg1;
-      const uint32_t koff = (uint32_t)wg0 * kHeadDim + kent;
-      bload_words<E>(rks, kneed ? koff * 4 : kOutOfRange, 0, sw);
-      if constexpr (!META) {
-        if constexpr (E == 2) zw = __builtin_amdgcn_raw_buffer_load_b32(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
-        else zw = __builtin_amdgcn_raw_buffer_load_b16(rkz, kneed ? koff * 2 : kOutOfRange, 0, kStream);
-      }
-      stage_meta(kmS, kmZ, sw, zw, (uint32_t)k * EPS, false);
+    // metadata of the first super-chunk
+    {
+      GqaKMeta km0;
+      load_kmeta(km0, (uint32_t)wg0);
+      stage_kmeta(km0);
     }
     Buf A, B, C;
     asm volatile("" ::: "memory");
@@ -731,6 +744,7 @@ void gqa_mfma_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
     wave_sync();
     for (int s = 0; s < nsteps; s += 3) {
+      progress_priority(nsteps - s, nsteps);
       load(C, s + 2);
       process(A, s);
       load(A, s + 3);
@@ -746,17 +760,21 @@ void gqa_mfma_kernel(AttnArgs a) {
   L += shfl_xor_f(L, 32);            // weight sum of head hk_lane
   float vb = vbias + shfl_xor_f(vbias, 16);
   vb += shfl_xor_f(vb, 32);          // bias of (head hk_lane, slice i16 & 3)
-  const float vbl = __shfl(vb, 4 * kq + (i16 >> 2));   // bias of (head kq, slice i16 >> 2)
+  float vbs[4];                      // bias of (head kq, slice s)
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) vbs[sl] = __shfl(vb, 4 * kq + sl);
   __syncthreads();                   // every wave is done with its staging area
   float *rows = smem;                // [kGqaWaves][kHpg][128]
   float *wml = smem + Gm::ROWS;      // [kGqaWaves][kHpg][2]
   {
-    const int sl = i16 >> 2;         // useful accumulator row: slice of this lane's channels
-    const int pc = ((i16 & 1) << 1) | ((i16 & 3) >> 1);   // channel offset 0,2,1,3 of column i16 & 3
+    // column i16 of block cb holds tile position 16 cb + i16, i.e. channel
+    // 32 (cb / 2) + 8 p + pass_chan(r, e) with 16 (cb mod 2) + i16 = 8 p + 2 r + e;
+    // its 32-channel slice is cb / 2, the accumulator row to keep
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = sel4(sl, acc[i][0], acc[i][1], acc[i][2], acc[i][3]) + vbl;
-      rows[(wave * kHpg + kq) * kHeadDim + 32 * sl + 4 * i + pc] = v;
+    for (int cb = 0; cb < 8; ++cb) {
+      const int pp = 16 * (cb & 1) + i16;
+      const int ch = 32 * (cb >> 1) + 8 * (pp >> 3) + pass_chan((pp >> 1) & 3, pp & 1);
+      rows[(wave * kHpg + kq) * kHeadDim + ch] = acc[cb][cb >> 1] + vbs[cb >> 1];
     }
   }
   if (lane < kHpg) {
@@ -786,14 +804,52 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+
+  // this split's share of the unit's fp16 tokens (sinks, then [n_main, n)),
+  // merged into the part's result
+  const int nrest = a.nsink + (int)(a.n - a.n_main);
+  if (split == 0 && a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
+    // fused step: the new token goes into its ring slot (the shares read it from k_new / v_new)
+    constexpr int CH = kHeadDim * 2 / 16;
+    const int which = tid / CH, ch = tid % CH;
+    const uint4 *src = reinterpret_cast<const uint4 *>((which ? a.v_new : a.k_new) + (int64_t)unit * kHeadDim);
+    uint4 *dst = reinterpret_cast<uint4 *>((which ? a.c.v_resid : a.c.k_resid) +
+                                           ((int64_t)unit * a.c.residual + (a.n - 1) % a.c.residual) * kHeadDim);
+    dst[ch] = src[ch];
+  }
+  const int ib = (int)((int64_t)nrest * split / a.splits), ie = (int)((int64_t)nrest * (split + 1) / a.splits);
+  if (ie > ib) {
+    float *acc2 = st.acc + Gm::STAGE2;   // [kHpg][128], then (max, sum)[kHpg]
+    float *ml2 = acc2 + kHpg * kHeadDim;
+    gqa_fp16_part<BITS, META>(a, unit, smem, qsm, acc2, ml2, ib, ie);
+    float f1[kHpg], f2[kHpg], mn[kHpg];
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      const float M = st.ml[2 * h], m2 = ml2[2 * h];
+      mn[h] = fmaxf(M, m2);
+      f1[h] = M == -INFINITY ? 0.0f : fast_exp2(M - mn[h]);
+      f2[h] = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - mn[h]);
+    }
+    for (int idx = tid; idx < kHpg * kHeadDim; idx += kGqaThreads) {
+      const int h = idx / kHeadDim;
+      st.acc[idx] = st.acc[idx] * f1[h] + acc2[idx] * f2[h];
+    }
+    __syncthreads();
+    if (tid < kHpg) {
+      const int h = tid;
+      const float L = st.ml[2 * h + 1] * f1[h] + ml2[2 * h + 1] * f2[h];
+      st.ml[2 * h] = mn[h];
+      st.ml[2 * h + 1] = L;
+    }
+    __syncthreads();
+  }
   finish_part<kHpg>(a, unit, split, st);
 }
 
 template <int BITS, int GS, int META>
 hipError_t launch_gqa(const AttnArgs &a, int splits, hipStream_t s) {
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * (splits + a.tail_wg)), dim3(kGqaThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((gqa_mfma_kernel<BITS, GS, META>), dim3(units * splits), dim3(kGqaThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -92,9 +92,9 @@ struct AttnArgs {
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s);
 
 // Matrix-core kernel for four query heads per kv head (KIVI layout): the
-// quantized groups [0, n_main) in a.splits parts [0, a.splits) and, when
-// a.tail_wg, the sinks and tokens [n_main, n) (at most kGqaMaxRest of them)
-// as part a.splits; writes the normalized output when a.nparts == 1.
+// quantized groups [0, n_main) in a.splits parts, each part also taking its
+// share of the sinks and tokens [n_main, n) (at most kGqaMaxRest of them);
+// writes the normalized output when a.nparts == 1.
 constexpr int kGqaMaxRest = 512 + 512 + 127;
 hipError_t launch_gqa_mfma(const AttnArgs &a, hipStream_t s);
 
