@@ -614,22 +614,6 @@ void gqa_mfma_kernel(AttnArgs a) {
     const int gq = (s >> LOG_SPG) & 3;   // group slot of this step in its super-chunk
     const int kk = s % SPC;
     if (kk == 0) prep();
-    wave_sync();
-    if (kk == 1) stage_kmeta(kmr);   // next super-chunk (its first step is at least SPC away)
-    stage_vmeta(bf.vs, bf.vz);
-    // bf16 value codes of both blocks into the tile
-    static_for<2>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      using C = CodesBf16<BITS>;
-      const uint32_t *w = bf.vw + k * WPL;
-      static_for<4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
-            make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
-                       C::template word<4 * q + 3>(w));
-      });
-    });
-    wave_sync();
     // key scores of both blocks; the high and low limb products accumulate
     // separately so four MFMA chains interleave
     fx4 sc[2], sl2[2];
@@ -649,6 +633,23 @@ void gqa_mfma_kernel(AttnArgs a) {
         sl2[k] = mma_x32(ak, bl, sl2[k]);
       }
     });
+    // staging while the key products run: metadata and the value tile
+    wave_sync();
+    if (kk == 1) stage_kmeta(kmr);   // next super-chunk (its first step is at least SPC away)
+    stage_vmeta(bf.vs, bf.vz);
+    // bf16 value codes of both blocks into the tile
+    static_for<2>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      using C = CodesBf16<BITS>;
+      const uint32_t *w = bf.vw + k * WPL;
+      static_for<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
+            make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
+                       C::template word<4 * q + 3>(w));
+      });
+    });
+    wave_sync();
     sc[0] += sl2[0];
     sc[1] += sl2[1];
 

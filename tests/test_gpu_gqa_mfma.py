@@ -35,6 +35,8 @@ CASES = [
     (_w(406, 1, 800, 4, 64, 128, 2, FIFO, 4), [1, 2]),                       # sinks + FIFO: three kinds of parts
     (_w(407, 3, 97, 2, 32, 32, 40), [1, 31, 32, 40]),                        # a few groups only
     (_w(408, 1, 5000, 2, 32, 128, 1, CHUNK, 0, 0, 8), [1]),                  # 8 kv heads, ragged split ranges
+    (_w(409, 1, 3000, 2, 128, 512, 3, FIFO, 512), [1, 3]),                   # largest fp16 list: 512 sinks + 639
+    (_w(410, 2, 1200, 4, 64, 128, 4, FIFO, 8, 1), [1, 4]),                   # 4-bit FIFO, sinks, packed metadata
 ]
 
 
