@@ -72,7 +72,8 @@ constexpr int kHpg = 4;   // query heads per kv head on this path
 constexpr int kMaxRest = kGqaMaxRest;
 
 // Lane byte offset past every buffer this kernel reads (resources cover at
-// most 2^31 bytes): such a load returns zero and touches no memory.
+// most 2^31 bytes; loads that use it add at most a few KiB of uniform offset): such a load
+// returns zero and touches no memory.
 constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
 // Four waves per workgroup, two waves per SIMD (up to 256 VGPRs: the
 // accumulators, both q' limb sets and a three-step load ring stay in
@@ -523,19 +524,23 @@ void gqa_mfma_kernel(AttnArgs a) {
     // key metadata of the next super-chunk with the loads of a super-chunk's
     // first step; staged into LDS at its second step, after the preparation
     if (s < nsteps && s % SPC == 0) load_kmeta(kmr, (uint32_t)(wg0 + 4 * (s / SPC + 1)));
-    s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
+    // past the end (never processed): out-of-range lane offsets, so the
+    // ring's last loads read zero instead of fetching data again
+    const bool live = s < nsteps;
     const uint32_t g = (uint32_t)(wg0 + (s >> LOG_SPG));
-    const uint32_t t0 = g * GS + (uint32_t)((s & (SPG - 1)) * 32);
-    bload_words<WPL>(rkc, code_lane, t0 * (W * 4), bf.kw);
-    bload_words<WPL>(rkc, code_lane, (t0 + 16) * (W * 4), bf.kw + WPL);
-    bload_words<WPL>(rvc, code_lane, t0 * (W * 4), bf.vw);
-    bload_words<WPL>(rvc, code_lane, (t0 + 16) * (W * 4), bf.vw + WPL);
-    bload_words<E>(rvs, mflat * 4, t0 * (VGR * 4), bf.vs);
+    const uint32_t t0 = live ? g * GS + (uint32_t)((s & (SPG - 1)) * 32) : 0u;
+    const uint32_t cl = live ? code_lane : kOutOfRange;
+    const uint32_t ml4 = live ? mflat * 4 : kOutOfRange, ml2 = live ? mflat * 2 : kOutOfRange;
+    bload_words<WPL>(rkc, cl, t0 * (W * 4), bf.kw);
+    bload_words<WPL>(rkc, cl, (t0 + 16) * (W * 4), bf.kw + WPL);
+    bload_words<WPL>(rvc, cl, t0 * (W * 4), bf.vw);
+    bload_words<WPL>(rvc, cl, (t0 + 16) * (W * 4), bf.vw + WPL);
+    bload_words<E>(rvs, ml4, t0 * (VGR * 4), bf.vs);
     if constexpr (!META) {
       if constexpr (E == 2) {
-        bf.vz = __builtin_amdgcn_raw_buffer_load_b32(rvz, mflat * 2, t0 * (VGR * 2), kStream);
+        bf.vz = __builtin_amdgcn_raw_buffer_load_b32(rvz, ml2, t0 * (VGR * 2), kStream);
       } else {
-        bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, mflat * 2, t0 * (VGR * 2), kStream);
+        bf.vz = __builtin_amdgcn_raw_buffer_load_b16(rvz, ml2, t0 * (VGR * 2), kStream);
       }
     } else {
       bf.vz = 0;
