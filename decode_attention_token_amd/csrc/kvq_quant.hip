@@ -19,143 +19,304 @@
 namespace kvq {
 namespace {
 
-// One workgroup of 256 threads quantizes one key group (GS tokens x 128
-// channels) of one unit.  Thread (pair, part) owns channels 2*pair, 2*pair+1
-// and a quarter of the group's tokens, held in registers: it reduces min/max
-// over its quarter (the quarters combine in LDS), codes its values into an LDS
-// byte tile, and the tile is packed into token rows word by word with
-// coalesced stores.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ f16x2 hmin(f16x2 a, f16x2 b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ f16x2 hmax(f16x2 a, f16x2 b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Packed codes of the 8 fp16 values of one 16-byte word (8 consecutive
+// channels of one token row), value k coded with r[k] = RN(1/S), z[k] and the
+// tie threshold thr[k].  The code map is the fast quotient of codes_of: a
+// product x * r (fp16 x read straight into the fused multiply), its rint, and
+// the tie test |y - rint(y)| >= thr, which flags every value whose fast code
+// could differ from the correctly rounded one (near is set, and the caller
+// redoes the word with code8_exact).  Codes accumulate as exact small
+// integers in fp32 (sum of code * 2^(BITS k) < 2^16 per half word).
+// 2-bit: bits 0..15 hold the 8 codes; 4-bit: all 32 bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t code8_fast(const uint4 &raw, const float *r, const float *z, const float *thr,
+                                               bool &near) {
+  constexpr float QMAX = float((1 << BITS) - 1);
+  float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f16x2 h = as_h2(word_of(raw, k >> 1));
+    const float y = __builtin_fmaf((float)h[k & 1], r[k], 0.0f);
+    const float t = rintf(y);
+    near |= fabsf(y - t) >= thr[k];
+    const float code = __builtin_amdgcn_fmed3f(t - z[k], 0.0f, QMAX);
+    const int half = (BITS == 4 && k >= 4) ? 1 : 0;
+    const int pos = (BITS == 4) ? (k & 3) : k;
+    acc[half] = __builtin_fmaf(code, float(1u << (BITS * pos)), acc[half]);
+  }
+  if constexpr (BITS == 2) return (uint32_t)acc[0];
+  return (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
+}
+
+// The same word through the correctly rounded quotient (code_of).
+template <int BITS>
+__device__ __forceinline__ uint32_t code8_exact(const uint4 &raw, const float *s, const float *z) {
+  constexpr float QMAX = float((1 << BITS) - 1);
+  uint32_t word = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t w = word_of(raw, k >> 1);
+    const float x = h2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xffffu)));
+    word |= code_of(x, GroupParams{s[k], z[k], 0.0f}, 0.0f, QMAX) << (BITS * k);
+  }
+  return word;
+}
+
+// 2-bit rows: a lane's 8 codes fill half a word.  Lanes cs and cs ^ 1 hold the
+// two halves of one word for the same rows, so for a pair of rows (a, b) the
+// even lane assembles row a's word and the odd lane row b's, each taking the
+// other half from its neighbour (a quad swap).  Returns the word of row
+// a + (cs & 1).
+__device__ __forceinline__ uint32_t pair_words(uint32_t ua, uint32_t ub, bool odd) {
+  const uint32_t send = odd ? ua : ub;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+  return odd ? (recv | (ub << 16)) : (ua | (recv << 16));
+}
+
+// One wave quantizes one key group (GS tokens x 128 channels) of one unit.
+// Lane l holds channels 8 (l % 16) .. + 7 of the group's token rows
+// 4 i + l / 16 as 16-byte words (each load instruction reads 1 KB of
+// consecutive rows).  Per-channel minimum and maximum reduce in packed fp16
+// over the lane's rows, then across the four lanes that hold the same
+// channels.  Each of those four lanes derives scale, zero-point and tie
+// threshold for two of the eight channels (the divisions are spread over the
+// wave) and hands them to the others through LDS.  Codes are packed into
+// token rows in registers and stored as 256 contiguous bytes per instruction.
 template <int BITS, int GS>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
                                                             int64_t src_rows, int64_t src_row0,
-                                                            int64_t dst_group0) {
+                                                            int64_t dst_group0, int ngroups, int total) {
+  constexpr int RL = GS / 4;                  // rows per lane
   constexpr int PER = 32 / BITS;              // codes per word
   constexpr int W = kHeadDim / PER;           // words per token row
-  constexpr int TQ = GS / 4;                  // tokens per thread
   constexpr float QMAX = float((1 << BITS) - 1);
-  const int g = blockIdx.x;
-  const int unit = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int pair = tid & 63, part = tid >> 6;
-  const int ch = 2 * pair;
-  __shared__ float s_mn[4][kHeadDim], s_mx[4][kHeadDim];
-  __shared__ uint8_t s_code[GS][kHeadDim];
+  __shared__ float4 s_par[4][kHeadDim];       // per wave and channel: r, z, thr, s
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gi = (int)blockIdx.x * 4 + wave;
+  if (gi >= total) return;                    // wave-uniform
+  const int unit = gi / ngroups, g = gi - unit * ngroups;
+  const int cs = lane & 15, q = lane >> 4;
 
-  const uint16_t *rows = src + ((int64_t)unit * src_rows + src_row0 + (int64_t)g * GS + part * TQ) * kHeadDim + ch;
-  float xa[TQ], xb[TQ];
+  const uint4 *in =
+      reinterpret_cast<const uint4 *>(src + ((int64_t)unit * src_rows + src_row0 + (int64_t)g * GS + q) * kHeadDim) +
+      cs;
+  uint4 raw[RL];
 #pragma unroll
-  for (int t = 0; t < TQ; ++t) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(rows + (int64_t)t * kHeadDim);
-    xa[t] = h2f((uint16_t)(w & 0xffffu));
-    xb[t] = h2f((uint16_t)(w >> 16));
-  }
-  float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+  for (int i = 0; i < RL; ++i) raw[i] = in[i * 4 * (kHeadDim / 8)];
+
+  f16x2 mn[4], mx[4];
 #pragma unroll
-  for (int t = 0; t < TQ; ++t) {
-    mn0 = fminf(mn0, xa[t]);
-    mx0 = fmaxf(mx0, xa[t]);
-    mn1 = fminf(mn1, xb[t]);
-    mx1 = fmaxf(mx1, xb[t]);
-  }
-  s_mn[part][ch] = mn0;
-  s_mn[part][ch + 1] = mn1;
-  s_mx[part][ch] = mx0;
-  s_mx[part][ch + 1] = mx1;
-  __syncthreads();
-  mn0 = fminf(fminf(s_mn[0][ch], s_mn[1][ch]), fminf(s_mn[2][ch], s_mn[3][ch]));
-  mx0 = fmaxf(fmaxf(s_mx[0][ch], s_mx[1][ch]), fmaxf(s_mx[2][ch], s_mx[3][ch]));
-  mn1 = fminf(fminf(s_mn[0][ch + 1], s_mn[1][ch + 1]), fminf(s_mn[2][ch + 1], s_mn[3][ch + 1]));
-  mx1 = fmaxf(fmaxf(s_mx[0][ch + 1], s_mx[1][ch + 1]), fmaxf(s_mx[2][ch + 1], s_mx[3][ch + 1]));
-  const GroupParams p0 = group_params(mn0, mx0, QMAX, c.meta != 0);
-  const GroupParams p1 = group_params(mn1, mx1, QMAX, c.meta != 0);
-  if (part == 0) {
-    const int64_t gidx = ((int64_t)unit * (c.cap / GS) + dst_group0 + g) * kHeadDim + ch;
-    if (c.meta) {
-      *reinterpret_cast<uint2 *>(c.k_scale + gidx) = make_uint2(pack_meta(p0.s, p0.z), pack_meta(p1.s, p1.z));
-    } else {
-      *reinterpret_cast<float2 *>(c.k_scale + gidx) = make_float2(p0.s, p1.s);
-      *reinterpret_cast<uint32_t *>(c.k_zero + gidx) =
-          (uint32_t)(uint16_t)(int16_t)p0.z | ((uint32_t)(uint16_t)(int16_t)p1.z << 16);
+  for (int e = 0; e < 4; ++e) mn[e] = mx[e] = as_h2(word_of(raw[0], e));
+#pragma unroll
+  for (int i = 1; i < RL; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 h = as_h2(word_of(raw[i], e));
+      mn[e] = hmin(mn[e], h);
+      mx[e] = hmax(mx[e], h);
     }
   }
-  uint32_t ca[TQ], cb[TQ];
-  codes_of<TQ>(xa, p0, 0.0f, QMAX, ca);
-  codes_of<TQ>(xb, p1, 0.0f, QMAX, cb);
 #pragma unroll
-  for (int t = 0; t < TQ; ++t)
-    *reinterpret_cast<uint16_t *>(&s_code[part * TQ + t][ch]) = (uint16_t)(ca[t] | (cb[t] << 8));
-  __syncthreads();
-  uint32_t *dst = c.k_codes + ((int64_t)unit * c.cap + (dst_group0 + g) * (int64_t)GS) * W;
-  for (int i = tid; i < GS * W; i += blockDim.x) {
-    const int t = i / W, w = i % W;
-    const uint8_t *b = &s_code[t][w * PER];
-    uint32_t word = 0;
+  for (int e = 0; e < 4; ++e) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) word |= (uint32_t)b[k] << (k * BITS);
-    dst[i] = word;
+    for (int m = 16; m <= 32; m *= 2) {
+      mn[e] = hmin(mn[e], as_h2((uint32_t)__shfl_xor((int)as_u32(mn[e]), m)));
+      mx[e] = hmax(mx[e], as_h2((uint32_t)__shfl_xor((int)as_u32(mx[e]), m)));
+    }
+  }
+
+  // lane (cs, q) derives the parameters of channels 8 cs + 2 q and 8 cs + 2 q + 1
+  const f16x2 a = q == 0 ? mn[0] : q == 1 ? mn[1] : q == 2 ? mn[2] : mn[3];
+  const f16x2 b = q == 0 ? mx[0] : q == 1 ? mx[1] : q == 2 ? mx[2] : mx[3];
+  GroupParams p[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float lo = (float)a[e], hi = (float)b[e];
+    p[e] = group_params(lo, hi, QMAX, c.meta != 0);
+    s_par[wave][8 * cs + 2 * q + e] = make_float4(p[e].r, p[e].z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p[e].r),
+                                                  p[e].s);
+  }
+  const int64_t gidx = ((int64_t)unit * (c.cap / GS) + dst_group0 + g) * kHeadDim + 8 * cs + 2 * q;
+  if (c.meta) {
+    *reinterpret_cast<uint2 *>(c.k_scale + gidx) = make_uint2(pack_meta(p[0].s, p[0].z), pack_meta(p[1].s, p[1].z));
+  } else {
+    *reinterpret_cast<float2 *>(c.k_scale + gidx) = make_float2(p[0].s, p[1].s);
+    *reinterpret_cast<uint32_t *>(c.k_zero + gidx) =
+        (uint32_t)(uint16_t)(int16_t)p[0].z | ((uint32_t)(uint16_t)(int16_t)p[1].z << 16);
+  }
+  lds_wave_sync();
+  float r[8], z[8], thr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 v = s_par[wave][8 * cs + k];
+    r[k] = v.x;
+    z[k] = v.y;
+    thr[k] = v.z;
+  }
+  auto code_row = [&](const uint4 &v) {
+    bool near = false;
+    uint32_t u = code8_fast<BITS>(v, r, z, thr, near);
+    if (__any(near)) {
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = s_par[wave][8 * cs + k].w;
+      u = code8_exact<BITS>(v, sv, z);
+    }
+    return u;
+  };
+
+  uint32_t *dst = c.k_codes + ((int64_t)unit * c.cap + (dst_group0 + g) * (int64_t)GS + q) * W;
+  if constexpr (BITS == 2) {
+    const bool odd = cs & 1;
+#pragma unroll
+    for (int k = 0; k < RL / 2; ++k) {
+      const uint32_t ua = code_row(raw[2 * k]), ub = code_row(raw[2 * k + 1]);
+      dst[4 * (2 * k + (odd ? 1 : 0)) * W + (cs >> 1)] = pair_words(ua, ub, odd);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RL; ++i) dst[4 * i * W + cs] = code_row(raw[i]);
   }
 }
 
-// One thread quantizes one value group (G channels of one token row) in
-// chunks of 32 channels held in registers: a min/max pass, then a coding
-// pass over the same 16-byte loads (served by the cache).
-template <int BITS>
+// One wave quantizes 32 consecutive token rows of the flattened (unit, token)
+// range, one value group per row and G channels.  Lane l holds channels
+// 8 (l % 16) .. + 7 of rows 4 i + l / 16 (16-byte loads, 1 KB of consecutive
+// rows per load instruction where the rows are contiguous), so a group spans
+// G / 8 neighbouring lanes: its minimum and maximum reduce with DPP moves as
+// one packed (min, -max) fp16 pair.  The group's lanes split the rows for
+// the parameter divisions and share the results through LDS; codes are
+// packed and stored as for keys.
+template <int BITS, int G>
 __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const uint16_t *__restrict__ src,
                                                               int64_t src_rows, int64_t src_row0, int count,
-                                                              int64_t dst_row0, int units) {
+                                                              int64_t dst_row0, int total_rows) {
+  constexpr int NR = 8;                       // rows per lane
+  constexpr int LPG = G / 8;                  // lanes per value group
+  constexpr int NG = kHeadDim / G;            // value groups per row
+  constexpr int NS = NR / LPG > 0 ? NR / LPG : 1;  // parameter rows per lane
   constexpr int PER = 32 / BITS;
   constexpr int W = kHeadDim / PER;
   constexpr float QMAX = float((1 << BITS) - 1);
-  const int G = c.group;
-  const int NG = kHeadDim / G;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)units * count * NG;
-  if (idx >= total) return;
-  const int j = (int)(idx % NG);
-  const int64_t r = idx / NG;
-  const int i = (int)(r % count);
-  const int unit = (int)(r / count);
+  __shared__ float4 s_par[4][4][NR][NG];      // [wave][l / 16][row][group]: r, z, thr, s
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cs = lane & 15, q = lane >> 4, j = cs / LPG, gl = cs % LPG;
+  const int row0 = ((int)blockIdx.x * 4 + wave) * 4 * NR;
+  if (row0 >= total_rows) return;             // wave-uniform
+  // (unit, token) of the lane's row i; rows advance 4 tokens at a time
+  const int u0 = (row0 + q) / count, t0 = (row0 + q) - u0 * count;
+  auto locate = [&](int i, int &u, int &t) {
+    u = u0;
+    t = t0 + 4 * i;
+    while (t >= count) {
+      t -= count;
+      ++u;
+    }
+  };
+  auto valid = [&](int i) { return row0 + 4 * i + q < total_rows; };
 
-  const uint16_t *x = src + ((int64_t)unit * src_rows + src_row0 + i) * kHeadDim + j * G;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int k0 = 0; k0 < G; k0 += 32) {
-    float v[32];
+  uint4 raw[NR];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      mn = fminf(mn, v[k]);
-      mx = fmaxf(mx, v[k]);
+  for (int i = 0; i < NR; ++i) {
+    raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (valid(i)) {
+      int u, t;
+      locate(i, u, t);
+      raw[i] = *(reinterpret_cast<const uint4 *>(src + ((int64_t)u * src_rows + src_row0 + t) * kHeadDim) + cs);
     }
   }
-  const GroupParams p = group_params(mn, mx, QMAX, c.meta != 0);
-  const int64_t row = (int64_t)unit * c.cap + dst_row0 + i;
-  if (c.meta) {
-    reinterpret_cast<uint32_t *>(c.v_scale)[row * NG + j] = pack_meta(p.s, p.z);
+
+  float mnr[NR], mxr[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const f16x2 h0 = as_h2(raw[i].x), h1 = as_h2(raw[i].y), h2 = as_h2(raw[i].z), h3 = as_h2(raw[i].w);
+    const f16x2 lo = hmin(hmin(h0, h1), hmin(h2, h3)), hi = hmax(hmax(h0, h1), hmax(h2, h3));
+    const f16x2 lo2 = hmin(lo, lo.yx), hi2 = hmax(hi, hi.yx);
+    f16x2 v = {lo2.x, -hi2.x};                // (min, -max): one packed minimum reduces both
+    v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0xB1, 0xF, 0xF, true)));   // lane ^ 1
+    v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x4E, 0xF, 0xF, true)));   // lane ^ 2
+    if constexpr (LPG >= 8)
+      v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x141, 0xF, 0xF, true)));  // other quad of 8
+    if constexpr (LPG >= 16)
+      v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x140, 0xF, 0xF, true)));  // other half of 16
+    mnr[i] = (float)v.x;
+    mxr[i] = -(float)v.y;
+  }
+
+  // lane gl of a group derives the parameters of rows gl, gl + LPG, ...
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int i = gl + LPG * sl;
+    float lo = mnr[0], hi = mxr[0];
+#pragma unroll
+    for (int ii = 1; ii < NR; ++ii) {
+      lo = (i == ii) ? mnr[ii] : lo;
+      hi = (i == ii) ? mxr[ii] : hi;
+    }
+    const GroupParams p = group_params(lo, hi, QMAX, c.meta != 0);
+    if (i < NR) {
+      s_par[wave][q][i][j] = make_float4(p.r, p.z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p.r), p.s);
+      if (valid(i)) {
+        int u, t;
+        locate(i, u, t);
+        const int64_t row = (int64_t)u * c.cap + dst_row0 + t;
+        if (c.meta) {
+          reinterpret_cast<uint32_t *>(c.v_scale)[row * NG + j] = pack_meta(p.s, p.z);
+        } else {
+          c.v_scale[row * NG + j] = p.s;
+          c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
+        }
+      }
+    }
+  }
+  lds_wave_sync();
+
+  auto code_row = [&](int i) {
+    const float4 pv = s_par[wave][q][i][j];
+    float r[8], z[8], thr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      r[k] = pv.x;
+      z[k] = pv.y;
+      thr[k] = pv.z;
+    }
+    bool near = false;
+    uint32_t u = code8_fast<BITS>(raw[i], r, z, thr, near);
+    if (__any(near)) {
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = pv.w;
+      u = code8_exact<BITS>(raw[i], sv, z);
+    }
+    return u;
+  };
+  auto store = [&](int i, uint32_t word, int w) {
+    if (valid(i)) {
+      int u, t;
+      locate(i, u, t);
+      c.v_codes[((int64_t)u * c.cap + dst_row0 + t) * W + w] = word;
+    }
+  };
+  if constexpr (BITS == 2) {
+    const bool odd = cs & 1;
+#pragma unroll
+    for (int k = 0; k < NR / 2; ++k) {
+      const uint32_t ua = code_row(2 * k), ub = code_row(2 * k + 1);
+      store(2 * k + (odd ? 1 : 0), pair_words(ua, ub, odd), cs >> 1);
+    }
   } else {
-    c.v_scale[row * NG + j] = p.s;
-    c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
-  }
-  uint32_t *dst = c.v_codes + row * W + j * (G / PER);
-  for (int k0 = 0; k0 < G; k0 += 32) {
-    float v[32];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
-    uint32_t cd[32];
-    codes_of<32>(v, p, 0.0f, QMAX, cd);
-    uint32_t words[32 / PER];
-#pragma unroll
-    for (int w = 0; w < 32 / PER; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) word |= cd[w * PER + k] << (k * BITS);
-      words[w] = word;
-    }
-    if constexpr (BITS == 2) {
-      *reinterpret_cast<uint2 *>(dst + k0 / PER) = make_uint2(words[0], words[1]);
-    } else {
-      *reinterpret_cast<uint4 *>(dst + k0 / PER) = make_uint4(words[0], words[1], words[2], words[3]);
-    }
+    for (int i = 0; i < NR; ++i) store(i, code_row(i), cs);
   }
 }
 
@@ -192,10 +353,12 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(uint16_t *__restrict__ k
 hipError_t launch_quantize_keys(const CacheView &c, int units, const uint16_t *src, int64_t src_rows,
                                 int64_t src_row0, int ngroups, int64_t dst_group0, hipStream_t s) {
   if (ngroups <= 0 || units <= 0) return hipSuccess;
-  dim3 grid(ngroups, units);
+  const int64_t total = (int64_t)units * ngroups;
+  if (total > INT32_MAX - 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((total + 3) / 4));
 #define KVQ_QK(B, G)                                                                                     \
   hipLaunchKernelGGL((quantize_keys_kernel<B, G>), grid, dim3(256), 0, s, c, src, src_rows, src_row0, \
-                     dst_group0)
+                     dst_group0, ngroups, (int)total)
   if (c.bits == 2) {
     if (c.group == 32) KVQ_QK(2, 32);
     else if (c.group == 64) KVQ_QK(2, 64);
@@ -212,14 +375,22 @@ hipError_t launch_quantize_keys(const CacheView &c, int units, const uint16_t *s
 hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t *src, int64_t src_rows,
                                   int64_t src_row0, int count, int64_t dst_row0, hipStream_t s) {
   if (count <= 0 || units <= 0) return hipSuccess;
-  const int64_t total = (int64_t)units * count * (kHeadDim / c.group);
-  const int64_t blocks = (total + 255) / 256;
-  if (c.bits == 2)
-    hipLaunchKernelGGL(quantize_values_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, c, src, src_rows,
-                       src_row0, count, dst_row0, units);
-  else
-    hipLaunchKernelGGL(quantize_values_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, c, src, src_rows,
-                       src_row0, count, dst_row0, units);
+  const int64_t total = (int64_t)units * count;
+  if (total > INT32_MAX - 256) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((total + 127) / 128));
+#define KVQ_QV(B, G)                                                                                       \
+  hipLaunchKernelGGL((quantize_values_kernel<B, G>), grid, dim3(256), 0, s, c, src, src_rows, src_row0, \
+                     count, dst_row0, (int)total)
+  if (c.bits == 2) {
+    if (c.group == 32) KVQ_QV(2, 32);
+    else if (c.group == 64) KVQ_QV(2, 64);
+    else KVQ_QV(2, 128);
+  } else {
+    if (c.group == 32) KVQ_QV(4, 32);
+    else if (c.group == 64) KVQ_QV(4, 64);
+    else KVQ_QV(4, 128);
+  }
+#undef KVQ_QV
   return hipGetLastError();
 }
 

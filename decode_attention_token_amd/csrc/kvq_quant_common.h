@@ -82,6 +82,23 @@ __device__ __forceinline__ void codes_of(const float *x, GroupParams p, float lo
   }
 }
 
+// Orders a wave's LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Threshold of the tile coder's tie test for a group whose values are at most
+// amax in magnitude: the fast quotient y = x * RN(1/S) can round differently
+// from RN(x / S) only when y lies within 2^-20 max(|y|, 1) of a half-integer,
+// i.e. when |y - rint(y)| >= 0.5 - 2^-20 max(|y|, 1).  |y| <= RN(amax * r)
+// (rounding is monotonic), and subtracting twice that tolerance keeps the
+// rounded threshold below the exact one (its rounding error is far smaller).
+__device__ __forceinline__ float tie_threshold(float amax, float r) {
+  return 0.5f - 2.0f * (fmaxf(amax * r, 1.0f) * 0x1p-20f);
+}
+
 // Unpacks 8 fp16 values (one 16-byte load) to fp32.
 __device__ __forceinline__ void load8(const uint16_t *p, float *x) {
   const uint4 v = *reinterpret_cast<const uint4 *>(p);
