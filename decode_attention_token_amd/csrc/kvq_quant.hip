@@ -29,6 +29,23 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
+// Packed fp16 minimum / maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48.  A
+// 16-lane row swap of a register with itself leaves lane l's and lane
+// (l ^ 16)'s values in the two results at every lane; a 32-lane swap does the
+// same for l ^ 32.  Both are plain VALU lane swaps (no LDS traffic).
+__device__ __forceinline__ f16x2 min_over_rows(f16x2 x) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = hmin(as_h2(p[0]), as_h2(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return hmin(as_h2(p[0]), as_h2(p[1]));
+}
+__device__ __forceinline__ f16x2 max_over_rows(f16x2 x) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = hmax(as_h2(p[0]), as_h2(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return hmax(as_h2(p[0]), as_h2(p[1]));
+}
+
 // Packed codes of the 8 fp16 values of one 16-byte word (8 consecutive
 // channels of one token row), value k coded with r[k] = RN(1/S), z[k] and the
 // tie threshold thr[k].  The code map is the fast quotient of codes_of: a
@@ -90,7 +107,8 @@ __device__ __forceinline__ uint32_t pair_words(uint32_t ua, uint32_t ub, bool od
 // over the lane's rows, then across the four lanes that hold the same
 // channels.  Each of those four lanes derives scale, zero-point and tie
 // threshold for two of the eight channels (the divisions are spread over the
-// wave) and hands them to the others through LDS.  Codes are packed into
+// wave) and hands them to the others through LDS, laid out so that each read
+// instruction touches 16 consecutive entries.  Codes are packed into
 // token rows in registers and stored as 256 contiguous bytes per instruction.
 template <int BITS, int GS>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
@@ -100,7 +118,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   constexpr int PER = 32 / BITS;              // codes per word
   constexpr int W = kHeadDim / PER;           // words per token row
   constexpr float QMAX = float((1 << BITS) - 1);
-  __shared__ float4 s_par[4][kHeadDim];       // per wave and channel: r, z, thr, s
+  __shared__ float4 s_par[4][8][16];          // [wave][channel % 8][channel / 8]: r, z, thr, s
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gi = (int)blockIdx.x * 4 + wave;
   if (gi >= total) return;                    // wave-uniform
@@ -128,11 +146,8 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int m = 16; m <= 32; m *= 2) {
-      mn[e] = hmin(mn[e], as_h2((uint32_t)__shfl_xor((int)as_u32(mn[e]), m)));
-      mx[e] = hmax(mx[e], as_h2((uint32_t)__shfl_xor((int)as_u32(mx[e]), m)));
-    }
+    mn[e] = min_over_rows(mn[e]);
+    mx[e] = max_over_rows(mx[e]);
   }
 
   // lane (cs, q) derives the parameters of channels 8 cs + 2 q and 8 cs + 2 q + 1
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   for (int e = 0; e < 2; ++e) {
     const float lo = (float)a[e], hi = (float)b[e];
     p[e] = group_params(lo, hi, QMAX, c.meta != 0);
-    s_par[wave][8 * cs + 2 * q + e] = make_float4(p[e].r, p[e].z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p[e].r),
+    s_par[wave][2 * q + e][cs] = make_float4(p[e].r, p[e].z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p[e].r),
                                                   p[e].s);
   }
   const int64_t gidx = ((int64_t)unit * (c.cap / GS) + dst_group0 + g) * kHeadDim + 8 * cs + 2 * q;
@@ -158,7 +173,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   float r[8], z[8], thr[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float4 v = s_par[wave][8 * cs + k];
+    const float4 v = s_par[wave][k][cs];
     r[k] = v.x;
     z[k] = v.y;
     thr[k] = v.z;
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
     if (__any(near)) {
       float sv[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sv[k] = s_par[wave][8 * cs + k].w;
+      for (int k = 0; k < 8; ++k) sv[k] = s_par[wave][k][cs].w;
       u = code8_exact<BITS>(v, sv, z);
     }
     return u;
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   constexpr int PER = 32 / BITS;
   constexpr int W = kHeadDim / PER;
   constexpr float QMAX = float((1 << BITS) - 1);
-  __shared__ float4 s_par[4][4][NR][NG];      // [wave][l / 16][row][group]: r, z, thr, s
+  __shared__ float4 s_par[4][NR][4][NG];      // [wave][row][l / 16][group]: r, z, thr, s
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cs = lane & 15, q = lane >> 4, j = cs / LPG, gl = cs % LPG;
   const int row0 = ((int)blockIdx.x * 4 + wave) * 4 * NR;
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
     }
     const GroupParams p = group_params(lo, hi, QMAX, c.meta != 0);
     if (i < NR) {
-      s_par[wave][q][i][j] = make_float4(p.r, p.z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p.r), p.s);
+      s_par[wave][i][q][j] = make_float4(p.r, p.z, tie_threshold(fmaxf(fabsf(lo), fabsf(hi)), p.r), p.s);
       if (valid(i)) {
         int u, t;
         locate(i, u, t);
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   lds_wave_sync();
 
   auto code_row = [&](int i) {
-    const float4 pv = s_par[wave][q][i][j];
+    const float4 pv = s_par[wave][i][q][j];
     float r[8], z[8], thr[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
