@@ -106,26 +106,177 @@ __device__ __forceinline__ void quantize_into(const CacheView &c, bool values, c
   quantize_group_hybrid<BITS>(x, G, codes, scale, zero);
 }
 
-// One thread per (tensor, unit, row, group): keys in the first half of the
-// grid, values in the second.  Source row src_row0 + i of [unit][src_rows]
-// [128] goes to cache row dst_row0 + i.
-template <int BITS>
+// One wave quantizes a block of 32 consecutive rows of the flattened
+// (unit, row) range of one tensor: key blocks in the first half of the grid,
+// value blocks in the second.  Source row src_row0 + i of [unit][src_rows]
+// [128] goes to cache row dst_row0 + i.  Lane l loads channels 8 (l % 16) ..
+// + 7 of rows 4 i + l / 16 with 16-byte loads (1 KB of consecutive rows per
+// instruction) and stages them in a per-wave LDS tile.  The group statistics
+// (the index-order float64 sums of the mode test, minimum, maximum) then run
+// one lane per (row, group), reading the group from the tile; the lane
+// writes the group's scale and zero-point and leaves r = RN(1/S), Z, the tie
+// threshold and the lower code bound in LDS.  Finally every lane codes its
+// own 8 values per row from registers with the tile coder (the same codes as
+// quantize_group_hybrid) and stores packed words.
+template <int BITS, int G>
 __global__ __launch_bounds__(256) void innerq_quantize_kernel(CacheView c, const uint16_t *__restrict__ ksrc,
                                                               const uint16_t *__restrict__ vsrc, int64_t src_rows,
                                                               int64_t src_row0, int count, int64_t dst_row0,
-                                                              int units) {
-  const int NG = kHeadDim / c.group;
-  const int64_t per = (int64_t)units * count * NG;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= 2 * per) return;
-  const bool values = idx >= per;
-  if (values) idx -= per;
-  const int j = (int)(idx % NG);
-  const int64_t r = idx / NG;
-  const int i = (int)(r % count);
-  const int unit = (int)(r / count);
-  const uint16_t *x = (values ? vsrc : ksrc) + ((int64_t)unit * src_rows + src_row0 + i) * kHeadDim + j * c.group;
-  quantize_into<BITS>(c, values, x, (int64_t)unit * c.cap + dst_row0 + i, j);
+                                                              int units, int nblocks) {
+  constexpr int NR = 8, BR = 4 * NR;          // rows per lane, rows per block
+  constexpr int LPG = G / 8, NG = kHeadDim / G;
+  constexpr int PER = 32 / BITS, W = kHeadDim / PER;
+  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr float QM = float((1 << (BITS - 1)) - 1);
+  constexpr float HALF = float(1 << (BITS - 1));
+  constexpr int TS = kHeadDim + 8;            // tile row stride (halves): rows 4 banks apart
+  static_assert(BR * NG * 20 <= BR * TS * 2, "parameters reuse the tile");
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[4][BR * TS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int cs = lane & 15, q = lane >> 4, j = cs / LPG;
+  const int wb = (int)blockIdx.x * 4 + wave;
+  if (wb >= 2 * nblocks) return;
+  const bool values = wb >= nblocks;
+  const int row0 = (values ? wb - nblocks : wb) * BR;
+  const int total_rows = units * count;
+  const uint16_t *src = values ? vsrc : ksrc;
+  uint32_t *codes = values ? c.v_codes : c.k_codes;
+  float *scale = values ? c.v_scale : c.k_scale;
+  int16_t *zero = values ? c.v_zero : c.k_zero;
+
+  // (unit, row) of block row r, stepped from the block's first row (one
+  // wave-uniform division per block)
+  const int ub = row0 / count, tb = row0 - ub * count;
+  auto locate = [&](int r, int &u, int &t) {
+    u = ub;
+    t = tb + r;
+    while (t >= count) {
+      t -= count;
+      ++u;
+    }
+  };
+  auto valid = [&](int r) { return row0 + r < total_rows; };
+
+  uint4 raw[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int r = 4 * i + q;
+    if (valid(r)) {
+      int u, t;
+      locate(r, u, t);
+      raw[i] = *(reinterpret_cast<const uint4 *>(src + ((int64_t)u * src_rows + src_row0 + t) * kHeadDim) + cs);
+    }
+  }
+  uint16_t *tile = s_tile[wave];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) *reinterpret_cast<uint4 *>(tile + (4 * i + q) * TS + 8 * cs) = raw[i];
+  lds_wave_sync();
+
+  // group statistics and parameters, one lane per (row, group)
+  float4 par[(BR * NG + 63) / 64];
+  float sc[(BR * NG + 63) / 64];
+#pragma unroll
+  for (int k = 0; k < (BR * NG + 63) / 64; ++k) {
+    const int gg = lane + 64 * k;
+    const int r = gg / NG, jj = gg % NG;
+    double s1 = 0.0, s2 = 0.0;
+    f16x2 mn2 = as_h2(0x7C007C00u), mx2 = as_h2(0xFC00FC00u);   // +inf, -inf
+    if (gg < BR * NG) {
+      const uint16_t *x = tile + r * TS + jj * G;
+      for (int k0 = 0; k0 < G; k0 += 8) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(x + k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h = as_h2(word_of(w, e));
+          mn2 = hmin(mn2, h);
+          mx2 = hmax(mx2, h);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const double xd = (double)(float)h[hh];
+            s1 = s1 + xd;
+            s2 = __builtin_fma(xd, xd, s2);   // x^2 is exact, so this is s2 + x * x rounded once
+          }
+        }
+      }
+    }
+    const float mn = fminf((float)mn2[0], (float)mn2[1]), mx = fmaxf((float)mx2[0], (float)mx2[1]);
+    const float amax = fmaxf(fabsf(mn), fabsf(mx));
+    const bool sym = 101.0 * (s1 * s1) < (double)G * s2;
+    GroupParams p;
+    float lo;
+    if (sym) {
+      const float sv = amax > 0.0f ? amax / QM : 1.0f;
+      p = {sv, -HALF, 1.0f / sv};
+      lo = 1.0f;
+    } else {
+      p = group_params(mn, mx, QMAX);
+      lo = 0.0f;
+    }
+    par[k] = make_float4(p.r, p.z, tie_threshold(amax, p.r), lo);
+    sc[k] = p.s;
+    if (gg < BR * NG && valid(r)) {
+      int u, t;
+      locate(r, u, t);
+      const int64_t row = (int64_t)u * c.cap + dst_row0 + t;
+      scale[row * NG + jj] = p.s;
+      zero[row * NG + jj] = static_cast<int16_t>(p.z);
+    }
+  }
+  // the parameter tables reuse the start of the tile: [row][group] float4,
+  // then [row][group] S
+  lds_wave_sync();
+  float4 *s_par = reinterpret_cast<float4 *>(tile);
+  float *s_s = reinterpret_cast<float *>(tile) + 4 * BR * NG;
+#pragma unroll
+  for (int k = 0; k < (BR * NG + 63) / 64; ++k) {
+    const int gg = lane + 64 * k;
+    if (gg < BR * NG) {
+      s_par[gg] = par[k];
+      s_s[gg] = sc[k];
+    }
+  }
+  lds_wave_sync();
+
+  auto code_row = [&](int i) {
+    const int r = 4 * i + q;
+    const float4 pv = s_par[r * NG + j];
+    float rr[8], z[8], thr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rr[k] = pv.x;
+      z[k] = pv.y;
+      thr[k] = pv.z;
+    }
+    bool near = false;
+    uint32_t u = code8_fast<BITS>(raw[i], rr, z, thr, pv.w, near);
+    if (__any(near)) {
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = s_s[r * NG + j];
+      u = code8_exact<BITS>(raw[i], sv, z, pv.w);
+    }
+    return u;
+  };
+  auto store = [&](int i, uint32_t word, int w) {
+    const int r = 4 * i + q;
+    if (valid(r)) {
+      int u, t;
+      locate(r, u, t);
+      codes[((int64_t)u * c.cap + dst_row0 + t) * W + w] = word;
+    }
+  };
+  if constexpr (BITS == 2) {
+    const bool odd = cs & 1;
+#pragma unroll
+    for (int k = 0; k < NR / 2; ++k) {
+      const uint32_t ua = code_row(2 * k), ub = code_row(2 * k + 1);
+      store(2 * k + (odd ? 1 : 0), pair_words(ua, ub, odd), cs >> 1);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) store(i, code_row(i), cs);
+  }
 }
 
 // One workgroup (one wave) per unit.  When pop_row >= 0 the window is full:
@@ -383,14 +534,23 @@ hipError_t launch_iq_by_group(const AttnArgs &a, hipStream_t s) {
 hipError_t launch_innerq_quantize(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
                                   int64_t src_rows, int64_t src_row0, int count, int64_t dst_row0, hipStream_t s) {
   if (count <= 0 || units <= 0) return hipSuccess;
-  const int64_t total = 2 * (int64_t)units * count * (kHeadDim / c.group);
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (c.bits == 2)
-    hipLaunchKernelGGL(innerq_quantize_kernel<2>, dim3(blocks), dim3(256), 0, s, c, ksrc, vsrc, src_rows, src_row0,
-                       count, dst_row0, units);
-  else
-    hipLaunchKernelGGL(innerq_quantize_kernel<4>, dim3(blocks), dim3(256), 0, s, c, ksrc, vsrc, src_rows, src_row0,
-                       count, dst_row0, units);
+  const int64_t total = (int64_t)units * count;
+  if (total > INT32_MAX / 2) return hipErrorInvalidValue;
+  const int nblocks = (int)((total + 31) / 32);   // 32 rows per wave, per tensor
+  const dim3 grid((unsigned)((2 * (int64_t)nblocks + 3) / 4));
+#define KVQ_IQQ(B, G)                                                                                        \
+  hipLaunchKernelGGL((innerq_quantize_kernel<B, G>), grid, dim3(256), 0, s, c, ksrc, vsrc, src_rows, src_row0, \
+                     count, dst_row0, units, nblocks)
+  if (c.bits == 2) {
+    if (c.group == 32) KVQ_IQQ(2, 32);
+    else if (c.group == 64) KVQ_IQQ(2, 64);
+    else KVQ_IQQ(2, 128);
+  } else {
+    if (c.group == 32) KVQ_IQQ(4, 32);
+    else if (c.group == 64) KVQ_IQQ(4, 64);
+    else KVQ_IQQ(4, 128);
+  }
+#undef KVQ_IQQ
   return hipGetLastError();
 }
 

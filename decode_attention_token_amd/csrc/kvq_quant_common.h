@@ -1,6 +1,7 @@
 // Device-side quantizer pieces shared by kvq_quant.hip (KIVI layout) and
 // kvq_innerq.hip (InnerQ-style layout): group scale and zero-point, the
-// exactly rounded code map with its fast path, and 16-byte fp16 loads.
+// exactly rounded code map with its fast path, 16-byte fp16 loads and the
+// 8-channel tile coder.
 // Private to the HIP sources.
 //
 // Bit-exactness: every arithmetic step is one IEEE fp32 operation with round
@@ -108,6 +109,74 @@ __device__ __forceinline__ void load8(const uint16_t *p, float *x) {
     x[2 * i] = h2f((uint16_t)(w[i] & 0xffffu));
     x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
   }
+}
+
+// ---------------------------------------------------------------- tile coder
+// Pieces of the wave-per-tile quantizers: lanes hold 16-byte words of 8
+// consecutive fp16 channels of one token row.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ f16x2 hmin(f16x2 a, f16x2 b) { return __builtin_elementwise_minimum(a, b); }
+__device__ __forceinline__ f16x2 hmax(f16x2 a, f16x2 b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Packed codes of the 8 fp16 values of one 16-byte word (8 consecutive
+// channels of one token row), value k coded with r[k] = RN(1/S), z[k] and the
+// tie threshold thr[k], clamped to [lo, 2^b - 1] (lo = 1 for symmetric
+// groups, 0 otherwise).  The code map is the fast quotient of codes_of: a
+// product x * r (fp16 x read straight into the fused multiply), its rint, and
+// the tie test |y - rint(y)| >= thr, which flags every value whose fast code
+// could differ from the correctly rounded one (near is set, and the caller
+// redoes the word with code8_exact).  Codes accumulate as exact small
+// integers in fp32 (sum of code * 2^(BITS k) < 2^16 per half word).
+// 2-bit: bits 0..15 hold the 8 codes; 4-bit: all 32 bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t code8_fast(const uint4 &raw, const float *r, const float *z, const float *thr,
+                                               float lo, bool &near) {
+  constexpr float QMAX = float((1 << BITS) - 1);
+  float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const f16x2 h = as_h2(word_of(raw, k >> 1));
+    const float y = __builtin_fmaf((float)h[k & 1], r[k], 0.0f);
+    const float t = rintf(y);
+    near |= fabsf(y - t) >= thr[k];
+    const float code = __builtin_amdgcn_fmed3f(t - z[k], lo, QMAX);
+    const int half = (BITS == 4 && k >= 4) ? 1 : 0;
+    const int pos = (BITS == 4) ? (k & 3) : k;
+    acc[half] = __builtin_fmaf(code, float(1u << (BITS * pos)), acc[half]);
+  }
+  if constexpr (BITS == 2) return (uint32_t)acc[0];
+  return (uint32_t)acc[0] | ((uint32_t)acc[1] << 16);
+}
+
+// The same word through the correctly rounded quotient (code_of).
+template <int BITS>
+__device__ __forceinline__ uint32_t code8_exact(const uint4 &raw, const float *s, const float *z, float lo) {
+  constexpr float QMAX = float((1 << BITS) - 1);
+  uint32_t word = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t w = word_of(raw, k >> 1);
+    const float x = h2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xffffu)));
+    word |= code_of(x, GroupParams{s[k], z[k], 0.0f}, lo, QMAX) << (BITS * k);
+  }
+  return word;
+}
+
+// 2-bit rows: a lane's 8 codes fill half a word.  Lanes cs and cs ^ 1 hold the
+// two halves of one word for the same rows, so for a pair of rows (a, b) the
+// even lane assembles row a's word and the odd lane row b's, each taking the
+// other half from its neighbour (a quad swap).  Returns the word of row
+// a + (cs & 1).
+__device__ __forceinline__ uint32_t pair_words(uint32_t ua, uint32_t ub, bool odd) {
+  const uint32_t send = odd ? ua : ub;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+  return odd ? (recv | (ub << 16)) : (ua | (recv << 16));
 }
 
 }  // namespace

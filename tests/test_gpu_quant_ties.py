@@ -16,7 +16,7 @@ import torch
 
 import decode_attention_token_amd as kvq
 import oracle
-from gpu_helpers import compare_all_buffers, host, make_cache
+from gpu_helpers import compare_all_buffers, compare_innerq_buffers, host, make_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,67 @@ def test_quantizer_ties_bit_exact(bits, G, meta):
     ref.append(host(kn), host(vn))
     torch.cuda.synchronize()
     compare_all_buffers(cache, ref)
+
+
+def _sym_tie_groups(bits, seed, want=48, trials=20000):
+    """[(amax, xs)] with xs in (0, amax] whose fast and correctly rounded
+    quotients by S = amax / (2^(b-1) - 1) round to different integers."""
+    rng = np.random.default_rng(seed)
+    qm = np.float32(2 ** (bits - 1) - 1)
+    out = []
+    for _ in range(trials):
+        amax = np.float32(np.float16(abs(rng.normal()) * rng.choice([0.01, 1.0, 30.0])))
+        if not amax > 0:
+            continue
+        s = np.float32(amax / qm)
+        r = np.float32(np.float32(1.0) / s)
+        x = _ALL_F16[np.searchsorted(_ALL_F16, 0, side="right"):np.searchsorted(_ALL_F16, amax, side="right")]
+        xs = x[np.rint(x / s) != np.rint(x * r)]
+        if len(xs):
+            out.append((amax, xs))
+            if len(out) == want:
+                break
+    return out
+
+
+@pytest.mark.parametrize("bits,G", [(2, 32), (4, 64), (4, 128)])
+def test_innerq_quantizer_ties_bit_exact(bits, G):
+    """Per-token groups of the InnerQ-style cache: zero-centred groups
+    (amax, -amax and +-x pairs: mean exactly 0, so symmetric) and offset
+    groups (a, b and tie values), for keys and values."""
+    print(f"case innerq bits={bits} G={G}", flush=True)
+    sym = _sym_tie_groups(bits, seed=8000 + 10 * bits + G)
+    asym = _tie_pairs(bits, False, seed=8500 + 10 * bits + G)
+    # with 2 bits S = max|x| and the quotients stay within [-1, 1], where the
+    # two roundings agree: zero-centred groups of random values stand in
+    assert (len(sym) >= 8 or bits == 2) and len(asym) >= 8, "no tie inputs found"
+    if not sym:
+        rng0 = np.random.default_rng(8000 + G)
+        sym = [(np.float32(1.0), np.abs(np.float16(rng0.normal(size=64) * 0.4)).astype(np.float32).clip(0, 1))]
+    B, H, d, L, R, S = 2, 2, 128, 200, 16, 4
+    n = B * H * L * (d // G)
+    groups = np.empty((n, G), np.float32)
+    for i in range(n):
+        if i % 2 == 0:
+            amax, xs = sym[(i // 2) % len(sym)]
+            half = xs[np.arange(G // 2 - 1) % len(xs)]
+            groups[i] = np.concatenate([[amax], half, [-amax], -half])
+        else:
+            a, b, xs = asym[(i // 2) % len(asym)]
+            groups[i, 0], groups[i, 1] = a, b
+            groups[i, 2:] = xs[np.arange(G - 2) % len(xs)]
+    rng = np.random.default_rng(13)
+    kg = groups.astype(np.float16)
+    rng.shuffle(kg)
+    vg = groups.astype(np.float16)[::-1].copy()
+    k = np.ascontiguousarray(kg.reshape(B, H, L, d))
+    v = np.ascontiguousarray(vg.reshape(B, H, L, d))
+    ref = oracle.InnerQCache(bits, G, R, S, B, H, d)
+    assert oracle.hybrid_is_symmetric(kg[:64]).any() and not oracle.hybrid_is_symmetric(kg[:64]).all()
+    cfg = kvq.make_innerq_config(bits, G, R, S, B, H, H, d, 256)
+    cache = kvq.KVCache(cfg, "cuda")
+    cache.prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    ref.prefill(k, v)
+    torch.cuda.synchronize()
+    assert ref.nq > S
+    compare_innerq_buffers(cache, ref)
