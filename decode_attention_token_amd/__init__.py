@@ -210,7 +210,9 @@ class KVCache:
     def workspace(self, n_tokens=None, splits=0) -> torch.Tensor:
         n = self.cfg.max_tokens if n_tokens is None else n_tokens
         nbytes = kvq_workspace_bytes(self.cfg, n, splits)
-        return torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=self.tensors["k_codes"].device)
+        # zero-filled: the leading work-queue counters must start at zero
+        # (every call leaves them at zero)
+        return torch.zeros(max(nbytes, 4) // 4, dtype=torch.float32, device=self.tensors["k_codes"].device)
 
     def step(self, k_new, v_new, q, softmax_scale=None, out=None, workspace=None, splits=0, stream=None):
         """Append one token and attend (one launch when no flush is due)."""

@@ -15,9 +15,13 @@ SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_gqa.hip", "
 # -packed-fp32-ops keeps the compiler from forming packed fp32 arithmetic;
 # correctly rounded fp32 division (the hipcc default) is required for the
 # bit-exact quantizer, so no fast-math flags appear here.
+# The atomic optimizer is off: it rewrites a work-queue ticket grab into a
+# read of the result right after the atomic, behind a wait for every load in
+# flight, while the kernels read a ticket a whole super-chunk later.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

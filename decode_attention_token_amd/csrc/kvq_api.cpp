@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/kvq.h"
@@ -125,10 +126,27 @@ int32_t auto_splits_for(const kvq_config *c, int64_t nq) {
   return (int32_t)s;
 }
 
-// Workspace: fp32 partial (acc[128], max, sum) records, (splits + 1) per
-// query head.
+// Workspace: per-unit work-queue counters (zero between calls), then fp32
+// partial (acc[128], max, sum) records, (splits + 1) per query head.
 size_t workspace_for(const kvq_config *c, int32_t splits) {
-  return (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
+  return kvq::counter_bytes((int64_t)c->batch * c->num_kv_heads) +
+         (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
+}
+
+// KVQ_DETERMINISTIC=1 (any value but "0") in the environment: the
+// matrix-core kernel hands super-chunks to waves in a fixed order, so reruns
+// are bit-identical; by default waves take them from a work queue, which
+// only changes the order of fp32 partial sums from run to run.
+bool deterministic_schedule() {
+  const char *v = getenv("KVQ_DETERMINISTIC");
+  return v != nullptr && strcmp(v, "0") != 0;
+}
+
+void set_workspace(kvq::AttnArgs &a, const kvq_config *c, void *workspace) {
+  a.dynamic = deterministic_schedule() ? 0 : 1;
+  a.ctr = static_cast<uint32_t *>(workspace);
+  a.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                         kvq::counter_bytes((int64_t)c->batch * c->num_kv_heads));
 }
 
 // InnerQ-style state (euno.news InnerQ summary, methodology 4): tokens
@@ -373,7 +391,7 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.c = view_of(cfg, cache);
   a.q = q;
   a.out = out;
-  a.partials = static_cast<float *>(workspace);
+  set_workspace(a, cfg, workspace);
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;
@@ -412,7 +430,7 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.c = view_of(cfg, cache);
   a.q = q;
   a.out = out;
-  a.partials = static_cast<float *>(workspace);
+  set_workspace(a, cfg, workspace);
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;

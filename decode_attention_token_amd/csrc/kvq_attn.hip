@@ -473,20 +473,45 @@ void decode_attn_kernel(AttnArgs a) {
 
 // Merge of the part records: m = max m_i, l = sum l_i 2^(m_i - m),
 // out = sum acc_i 2^(m_i - m) / l.
+// Split records are read kMergeBatch at a time: every load of a batch is
+// issued before any is used, so a batch costs one memory round trip.  The
+// batches fold into a running (max, sum, acc) by the same rescaling rule the
+// attention kernels use inside a split.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float *__restrict__ partials,
                                                          float *__restrict__ out, int nparts) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
   const float *p = partials + bh * nparts * kPartialStride;
-  float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, p[i * kPartialStride + kHeadDim]);
-  float L = 0.0f, acc = 0.0f;
-  for (int i = 0; i < nparts; ++i) {
-    const float mi = p[i * kPartialStride + kHeadDim];
-    if (mi == -INFINITY) continue;
-    const float f = exp2f(mi - M);
-    L = fmaf(f, p[i * kPartialStride + kHeadDim + 1], L);
-    acc = fmaf(f, p[i * kPartialStride + c], acc);
+  float M = -INFINITY, L = 0.0f, acc = 0.0f;
+  for (int i0 = 0; i0 < nparts; i0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool in = i0 + j < nparts;
+      const float *r = p + (int64_t)(in ? i0 + j : i0) * kPartialStride;
+      mv[j] = in ? r[kHeadDim] : -INFINITY;
+      lv[j] = r[kHeadDim + 1];
+      av[j] = r[c];
+    }
+    float bm = mv[0];
+#pragma unroll
+    for (int j = 1; j < kMergeBatch; ++j) bm = fmaxf(bm, mv[j]);
+    if (bm == -INFINITY) continue;   // no tokens in this batch's records
+    if (bm > M) {
+      const float f = (M == -INFINITY) ? 0.0f : exp2f(M - bm);
+      L *= f;
+      acc *= f;
+      M = bm;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (mv[j] == -INFINITY) continue;   // empty record (or past the last one)
+      const float f = exp2f(mv[j] - M);
+      L = fmaf(f, lv[j], L);
+      acc = fmaf(f, av[j], acc);
+    }
   }
   out[bh * kHeadDim + c] = acc / L;
 }

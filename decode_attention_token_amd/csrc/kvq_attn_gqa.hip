@@ -431,7 +431,12 @@ void gqa_mfma_kernel(AttnArgs a) {
 
   const int units = a.batch * a.hkv;
   const int split = (int)blockIdx.x / units;
-  const int unit = (int)blockIdx.x % units;
+  // Workgroups are dealt to the XCDs round-robin, and the first 256 take one
+  // slot per CU before the rest fill the second.  Rotating the unit by the
+  // split puts a unit's workgroups on different XCDs and in both rounds, so
+  // the shared work queue below can even out slower XCDs and the younger
+  // workgroup of each CU.
+  const int unit = ((int)blockIdx.x % units + split) % units;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, kq = lane >> 4;
@@ -439,11 +444,39 @@ void gqa_mfma_kernel(AttnArgs a) {
   const int b = unit / a.hkv, hk = unit % a.hkv;
   const int64_t cap = a.c.cap;
   const int ngroups = (int)(a.n_main / GS);
-  const int g0 = (int)((int64_t)ngroups * split / a.splits);
-  const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
-  const int wg0 = g0 + (g1 - g0) * wave / kGqaWaves;
-  const int wg1 = g0 + (g1 - g0) * (wave + 1) / kGqaWaves;
-  const int nsteps = (wg1 - wg0) * SPG;
+  // Work queue.  The unit's key groups form super-chunks of four (the last
+  // one possibly shorter).  Each wave of the unit takes its first two
+  // super-chunks by its index among the unit's nw waves (slot, nw + slot),
+  // then one at a time from the unit's ticket counter (super-chunk
+  // 2 nw + ticket), grabbed a whole super-chunk before its loads are issued.
+  // With a.dynamic == 0 the sequence stays strided (slot + k nw): the same
+  // partial sums on every run.
+  // Ids only grow along a wave's sequence, so the first id past the end ends
+  // the wave.  Every wave then adds (1 << 24) | (super-chunks it took) to
+  // the unit's second counter; the last wave checks that the unit's count is
+  // complete (else the result is poisoned with NaN: the counters did not
+  // start at zero) and returns both counters to zero for the next call.
+  const int nsc = (ngroups + 3) / 4;
+  const int nw = a.splits * kGqaWaves;
+  const int slot = split * kGqaWaves + wave;
+  uint32_t *const ticket = a.ctr + 2 * unit;
+  auto grab = [&]() -> uint32_t {   // in lane 0; read at the next super-chunk
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
+  auto live_steps = [&](uint32_t id) { return (ngroups - 4 * (int)id < 4 ? ngroups - 4 * (int)id : 4) * SPG; };
+  // ids compare unsigned, so any value past the end (however large) ends the wave
+  uint32_t idL = slot, idL1 = nw + slot;   // super-chunk of the load cursor, and the next one
+  int nsteps = 0x7fffffff;                 // known once the next super-chunk is past the end
+  uint32_t pend = 0;                       // ticket grabbed for the super-chunk after idL1
+  if (idL >= (uint32_t)nsc) {
+    nsteps = 0;
+  } else if (idL1 >= (uint32_t)nsc) {
+    nsteps = live_steps(idL);
+  } else if (a.dynamic) {
+    pend = grab();
+  }
 
   float *kmS = smem + wave * Gm::PER_WAVE;
   float *kmZ = kmS + Gm::KM;
@@ -496,7 +529,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   // 16-byte loads per lane; entries of groups past the wave's range get an
   // out-of-range lane offset, so they read zero without touching memory
   auto load_kmeta = [&](GqaKMeta &km, uint32_t gfirst) {
-    const bool kneed = gfirst + (uint32_t)(lane >> 4) < (uint32_t)wg1;
+    const bool kneed = gfirst + (uint32_t)(lane >> 4) < (uint32_t)ngroups;
     const uint32_t koff = gfirst * kHeadDim + 8u * (uint32_t)lane;
     const uint32_t so = kneed ? koff * 4 : kOutOfRange;
     km.s0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rks, so, 0, kStream));
@@ -523,11 +556,22 @@ void gqa_mfma_kernel(AttnArgs a) {
   auto load = [&](Buf &bf, int s) {
     // key metadata of the next super-chunk with the loads of a super-chunk's
     // first step; staged into LDS at its second step, after the preparation
-    if (s < nsteps && s % SPC == 0) load_kmeta(kmr, (uint32_t)(wg0 + 4 * (s / SPC + 1)));
+    if (s < nsteps && s % SPC == 0) {
+      if (s > 0) {   // the load cursor enters the next super-chunk
+        idL = idL1;
+        idL1 = a.dynamic ? 2u * nw + (uint32_t)__builtin_amdgcn_readlane(pend, 0) : idL1 + nw;
+        if (idL1 < (uint32_t)nsc) {
+          if (a.dynamic) pend = grab();
+        } else {
+          nsteps = s + live_steps(idL);
+        }
+      }
+      if (idL1 < (uint32_t)nsc) load_kmeta(kmr, 4u * idL1);
+    }
     // past the end (never processed): out-of-range lane offsets, so the
     // ring's last loads read zero instead of fetching data again
     const bool live = s < nsteps;
-    const uint32_t g = (uint32_t)(wg0 + (s >> LOG_SPG));
+    const uint32_t g = 4u * idL + (uint32_t)((s % SPC) >> LOG_SPG);
     const uint32_t t0 = live ? g * GS + (uint32_t)((s & (SPG - 1)) * 32) : 0u;
     const uint32_t cl = live ? code_lane : kOutOfRange;
     const uint32_t ml4 = live ? mflat * 4 : kOutOfRange, ml2 = live ? mflat * 2 : kOutOfRange;
@@ -739,7 +783,7 @@ void gqa_mfma_kernel(AttnArgs a) {
     // metadata of the first super-chunk
     {
       GqaKMeta km0;
-      load_kmeta(km0, (uint32_t)wg0);
+      load_kmeta(km0, 4u * idL);
       stage_kmeta(km0);
     }
     Buf A, B, C;
@@ -750,7 +794,6 @@ void gqa_mfma_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
     wave_sync();
     for (int s = 0; s < nsteps; s += 3) {
-      progress_priority(nsteps - s, nsteps);
       load(C, s + 2);
       process(A, s);
       load(A, s + 3);
@@ -759,6 +802,12 @@ void gqa_mfma_kernel(AttnArgs a) {
       if (s + 2 < nsteps) process(C, s + 2);
     }
   }
+  // every grab of this wave has been read: report the super-chunks taken
+  // (the reply is read at the end, so its latency overlaps the combine)
+  const uint32_t took = (uint32_t)((nsteps + SPC - 1) / SPC);
+  uint32_t done_old = 0;
+  if (lane == 0)
+    done_old = __hip_atomic_fetch_add(ticket + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- combine: per-wave rows [h][128] in LDS, then across waves
   float L = block_sum<4>(lsum);
@@ -849,6 +898,17 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
+  {
+    const uint32_t old = __builtin_amdgcn_readlane(done_old, 0);
+    if ((old >> 24) == (uint32_t)(nw - 1)) {   // the unit's last wave
+      if (lane == 0) {
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ticket + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if ((old & 0xffffffu) + took != (uint32_t)nsc && lane < kHpg) st.ml[2 * lane + 1] = __builtin_nanf("");
+    }
+  }
+  __syncthreads();
   finish_part<kHpg>(a, unit, split, st);
 }
 

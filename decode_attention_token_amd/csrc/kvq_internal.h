@@ -10,6 +10,9 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kMaxSplits = 64;
 constexpr int kPartialStride = kHeadDim + 4;   // acc[128], m, l, pad, pad (floats)
+// Workspace: per-unit work-queue counters (two u32 each), padded to 256
+// bytes, then the partial records.
+inline size_t counter_bytes(int64_t units) { return (size_t)((units * 8 + 255) / 256 * 256); }
 
 struct CacheView {
   uint32_t *k_codes;
@@ -72,6 +75,8 @@ struct AttnArgs {
   const uint16_t *q;     // [B][Hq][128]
   float *out;            // [B][Hq][128]
   float *partials;       // [B][Hq][nparts][kPartialStride]
+  uint32_t *ctr;         // [B*Hkv][2] work-queue counters (zero between calls)
+  int dynamic;           // 1: waves take super-chunks from the work queue; 0: fixed strided order
   int batch, hq, hkv;
   int64_t n, nq_k, nq_v;
   int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups

@@ -183,9 +183,10 @@ int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens);
 
 /* Workspace bytes kvq_decode_attention needs for `splits` splits (0 = the
  * automatic count for n_tokens; more tokens never need fewer splits, so the
- * size for max_tokens covers every call): fp32 partial (acc[head_dim], max,
- * sum) records for every query head and part.  Host only; 0 on an invalid
- * cfg. */
+ * size for max_tokens covers every call): two u32 work-queue counters per
+ * (batch, kv head), padded to 256 bytes, then fp32 partial (acc[head_dim],
+ * max, sum) records for every query head and part.  Host only; 0 on an
+ * invalid cfg. */
 size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t splits);
 
 /* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
@@ -222,8 +223,12 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
  * q.K^T and P.V products).  q fp16 device [batch][num_q_heads][head_dim];
  * out fp32 device [batch][num_q_heads][head_dim]; query head h uses key head
  * h / (num_q_heads / num_kv_heads).  workspace: device, at least
- * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, no initialization needed;
- * calls that share a workspace must be ordered on one stream.  splits: 0 =
+ * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, zero-filled once before
+ * its first use: its leading bytes hold per-(batch, kv head) work-queue
+ * counters that every call leaves at zero again (the rest is scratch for
+ * split records; a call whose counters did not start at zero returns NaN
+ * outputs instead of a wrong result); calls that share a workspace must be
+ * ordered on one stream.  splits: 0 =
  * automatic, else 1..64.  One kernel launch when every unit fits one part,
  * else a second (merge) launch.  Needs started and n_tokens >= 1. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,

@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: run the HIP path and the oracle on the
 same seeded fp16 bits and compare buffers (bit-exact) and outputs (2e-3)."""
+import contextlib
+import os
+
 import numpy as np
 import torch
 
@@ -15,6 +18,21 @@ ATOL = 2e-3   # attention max-abs bound versus the float64 oracle
 # moves an output by a few 1e-5; 1e-4 leaves margin and is still 20x below ATOL.
 SPLIT_TOL = 1e-5
 SPLIT_TOL_MFMA = 1e-4
+
+
+@contextlib.contextmanager
+def deterministic_schedule():
+    """KVQ_DETERMINISTIC=1 for the calls inside: the matrix-core kernel then
+    hands super-chunks to waves in a fixed order instead of a work queue."""
+    old = os.environ.get("KVQ_DETERMINISTIC")
+    os.environ["KVQ_DETERMINISTIC"] = "1"
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["KVQ_DETERMINISTIC"]
+        else:
+            os.environ["KVQ_DETERMINISTIC"] = old
 
 
 def split_tol(heads_per_kv):

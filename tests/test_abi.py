@@ -286,8 +286,11 @@ def test_workspace_and_split_sizing(lib):
     c = cfg()
     s = kvq.kvq_auto_splits(c, 4097)
     assert 1 <= s <= 64
-    assert kvq.kvq_workspace_bytes(c, 4097, 0) == 16 * 32 * (s + 1) * 132 * 4
-    assert kvq.kvq_workspace_bytes(c, 4097, 3) == 16 * 32 * 4 * 132 * 4
+    # per-unit work-queue counters (two u32 per (batch, kv head), padded to
+    # 256 bytes), then (splits + 1) records of 132 floats per query head
+    ctr = 16 * 32 * 8
+    assert kvq.kvq_workspace_bytes(c, 4097, 0) == ctr + 16 * 32 * (s + 1) * 132 * 4
+    assert kvq.kvq_workspace_bytes(c, 4097, 3) == ctr + 16 * 32 * 4 * 132 * 4
     assert kvq.kvq_workspace_bytes(c, 4097, 65) == 0
     # more tokens never needs fewer splits, so sizing for capacity is enough
     prev = 0
