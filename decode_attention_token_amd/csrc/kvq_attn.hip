@@ -471,49 +471,13 @@ void decode_attn_kernel(AttnArgs a) {
   finish_part<HPG>(a, unit, split, st);
 }
 
-// Merge of the part records: m = max m_i, l = sum l_i 2^(m_i - m),
-// out = sum acc_i 2^(m_i - m) / l.
-// Split records are read kMergeBatch at a time: every load of a batch is
-// issued before any is used, so a batch costs one memory round trip.  The
-// batches fold into a running (max, sum, acc) by the same rescaling rule the
-// attention kernels use inside a split.
-constexpr int kMergeBatch = 8;
-
+// Merge of the part records (one workgroup per query head, one thread per
+// channel).
 __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float *__restrict__ partials,
                                                          float *__restrict__ out, int nparts) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
-  const float *p = partials + bh * nparts * kPartialStride;
-  float M = -INFINITY, L = 0.0f, acc = 0.0f;
-  for (int i0 = 0; i0 < nparts; i0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const bool in = i0 + j < nparts;
-      const float *r = p + (int64_t)(in ? i0 + j : i0) * kPartialStride;
-      mv[j] = in ? r[kHeadDim] : -INFINITY;
-      lv[j] = r[kHeadDim + 1];
-      av[j] = r[c];
-    }
-    float bm = mv[0];
-#pragma unroll
-    for (int j = 1; j < kMergeBatch; ++j) bm = fmaxf(bm, mv[j]);
-    if (bm == -INFINITY) continue;   // no tokens in this batch's records
-    if (bm > M) {
-      const float f = (M == -INFINITY) ? 0.0f : exp2f(M - bm);
-      L *= f;
-      acc *= f;
-      M = bm;
-    }
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      if (mv[j] == -INFINITY) continue;   // empty record (or past the last one)
-      const float f = exp2f(mv[j] - M);
-      L = fmaf(f, lv[j], L);
-      acc = fmaf(f, av[j], acc);
-    }
-  }
-  out[bh * kHeadDim + c] = acc / L;
+  out[bh * kHeadDim + c] = merge_records(partials + bh * nparts * kPartialStride, nparts, c);
 }
 
 template <int BITS, int GS, int HPG, int META>
@@ -580,8 +544,8 @@ hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
     m.tail_wg = 0;
     m.resid_main = 0;
     m.nparts = m.splits;
-    if ((e = launch_gqa_mfma(m, s)) != hipSuccess) return e;
-    return launch_merge(m, s);
+    // the unit's last workgroup merges the split records itself
+    return launch_gqa_mfma(m, s);
   }
   if ((e = launch_valu(a, s)) != hipSuccess) return e;
   return launch_merge(a, s);

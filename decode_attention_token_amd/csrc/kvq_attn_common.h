@@ -205,6 +205,52 @@ __device__ void finish_part(const AttnArgs &a, int unit, int part, const Stage &
 }
 
 
+// Merge of one query head's split records (nparts records of kPartialStride
+// floats from p: acc[128], max, sum) for channel c: m = max m_i,
+// l = sum l_i 2^(m_i - m), out = sum acc_i 2^(m_i - m) / l.  Records are read
+// kMergeBatch at a time: every load of a batch is issued before any is used,
+// so a batch costs one memory round trip.  The batches fold into a running
+// (max, sum, acc) by the same rescaling rule the kernels use inside a split.
+constexpr int kMergeBatch = 8;
+
+struct PlainLoad {
+  __device__ float operator()(const float *p) const { return *p; }
+};
+
+template <class Load = PlainLoad>
+__device__ __forceinline__ float merge_records(const float *__restrict__ p, int nparts, int c, Load ld = Load()) {
+  float M = -INFINITY, L = 0.0f, acc = 0.0f;
+  for (int i0 = 0; i0 < nparts; i0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool in = i0 + j < nparts;
+      const float *r = p + (int64_t)(in ? i0 + j : i0) * kPartialStride;
+      mv[j] = in ? ld(r + kHeadDim) : -INFINITY;
+      lv[j] = ld(r + kHeadDim + 1);
+      av[j] = ld(r + c);
+    }
+    float bm = mv[0];
+#pragma unroll
+    for (int j = 1; j < kMergeBatch; ++j) bm = fmaxf(bm, mv[j]);
+    if (bm == -INFINITY) continue;   // no tokens in this batch's records
+    if (bm > M) {
+      const float f = (M == -INFINITY) ? 0.0f : exp2f(M - bm);
+      L *= f;
+      acc *= f;
+      M = bm;
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (mv[j] == -INFINITY) continue;   // empty record (or past the last one)
+      const float f = exp2f(mv[j] - M);
+      L = fmaf(f, lv[j], L);
+      acc = fmaf(f, av[j], acc);
+    }
+  }
+  return acc / L;
+}
+
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for the MHA
 // tilings, two for the grouped-query tiling that keeps 4 heads in registers.
 template <int HPG>

@@ -416,6 +416,14 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
   __syncthreads();
 }
 
+// Agent-scope atomic load: reads what another XCD wrote with an agent-scope
+// atomic store.
+struct CoherentLoad {
+  __device__ float operator()(const float *p) const {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
 template <int BITS, int GS, int META>
 __global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(kGqaWavesPerEU, kGqaWavesPerEU)))
 void gqa_mfma_kernel(AttnArgs a) {
@@ -426,6 +434,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   constexpr int LOG_SPG = SPG == 1 ? 0 : (SPG == 2 ? 1 : 2);
 
   __shared__ __attribute__((aligned(16))) float smem[Gm::SMEM];
+  __shared__ uint32_t s_took[kGqaWaves + 1];   // super-chunks per wave; then the last-part flag
   const Stage st = stage_of<kHpg>(smem, Gm::WORK + Gm::QS);
   float *qsm = smem + Gm::WORK;   // scaled query [h][128], shared by the workgroup's waves
 
@@ -452,10 +461,11 @@ void gqa_mfma_kernel(AttnArgs a) {
   // With a.dynamic == 0 the sequence stays strided (slot + k nw): the same
   // partial sums on every run.
   // Ids only grow along a wave's sequence, so the first id past the end ends
-  // the wave.  Every wave then adds (1 << 24) | (super-chunks it took) to
-  // the unit's second counter; the last wave checks that the unit's count is
-  // complete (else the result is poisoned with NaN: the counters did not
-  // start at zero) and returns both counters to zero for the next call.
+  // the wave.  At its end every workgroup adds (1 << 24) | (super-chunks its
+  // waves took) to the unit's second counter; the unit's last workgroup
+  // checks that the count is complete (else its output is NaN: the counters
+  // did not start at zero), returns both counters to zero for the next call
+  // and merges the unit's split records.
   const int nsc = (ngroups + 3) / 4;
   const int nw = a.splits * kGqaWaves;
   const int slot = split * kGqaWaves + wave;
@@ -802,12 +812,8 @@ void gqa_mfma_kernel(AttnArgs a) {
       if (s + 2 < nsteps) process(C, s + 2);
     }
   }
-  // every grab of this wave has been read: report the super-chunks taken
-  // (the reply is read at the end, so its latency overlaps the combine)
-  const uint32_t took = (uint32_t)((nsteps + SPC - 1) / SPC);
-  uint32_t done_old = 0;
-  if (lane == 0)
-    done_old = __hip_atomic_fetch_add(ticket + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every grab of this wave has been read: the super-chunks it took
+  if (lane == 0) s_took[wave] = (uint32_t)((nsteps + SPC - 1) / SPC);
 
   // ---- combine: per-wave rows [h][128] in LDS, then across waves
   float L = block_sum<4>(lsum);
@@ -898,18 +904,52 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  {
-    const uint32_t old = __builtin_amdgcn_readlane(done_old, 0);
-    if ((old >> 24) == (uint32_t)(nw - 1)) {   // the unit's last wave
-      if (lane == 0) {
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ticket + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if ((old & 0xffffffu) + took != (uint32_t)nsc && lane < kHpg) st.ml[2 * lane + 1] = __builtin_nanf("");
+  // Several parts: publish this part's record, then count the workgroup in;
+  // the unit's last workgroup merges every record.  The records cross XCDs,
+  // whose L2 caches are not kept coherent for ordinary stores, so they are
+  // written and read with agent-scope atomic accesses (through to memory),
+  // and every wave waits for its own stores to complete before the count.
+  if (a.nparts > 1) {
+    for (int i = tid; i < kHpg * (kHeadDim + 2); i += kGqaThreads) {
+      const int h = i / (kHeadDim + 2), c = i % (kHeadDim + 2);
+      const int64_t bh = (int64_t)b * a.hq + hk * kHpg + h;
+      float *rec = a.partials + (bh * a.nparts + split) * kPartialStride;
+      __hip_atomic_store(rec + c, c < kHeadDim ? st.acc[h * kHeadDim + c] : st.ml[2 * h + (c - kHeadDim)],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    uint32_t took = 0;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) took += s_took[w];
+    const uint32_t old =
+        __hip_atomic_fetch_add(ticket + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t last = 0;
+    if ((old >> 24) == (uint32_t)(a.splits - 1)) {
+      last = ((old & 0xffffffu) + took == (uint32_t)nsc) ? 1u : 2u;
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ticket + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_took[kGqaWaves] = last;
   }
   __syncthreads();
-  finish_part<kHpg>(a, unit, split, st);
+  const uint32_t last = s_took[kGqaWaves];
+  if (a.nparts == 1) {   // the only part: normalized output straight from the workgroup
+    if (last == 2 && tid < kHpg) st.ml[2 * tid + 1] = __builtin_nanf("");
+    __syncthreads();
+    finish_part<kHpg>(a, unit, split, st);
+    return;
+  }
+  if (last == 0) return;
+  for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads) {
+    const int h = i / kHeadDim, c = i % kHeadDim;
+    const int64_t bh = (int64_t)b * a.hq + hk * kHpg + h;
+    a.out[bh * kHeadDim + c] =
+        last == 2 ? __builtin_nanf("")
+                  : merge_records(a.partials + bh * a.nparts * kPartialStride, a.nparts, c, CoherentLoad());
+  }
 }
 
 template <int BITS, int GS, int META>
