@@ -169,3 +169,38 @@ def test_gqa_mfma_large_magnitudes():
     err = max_err(_attention(cache, q, "mfma"), oracle_attention(ref, host(q), 1 / math.sqrt(128)))
     print(f"  err {err:.2e}", flush=True)
     assert err <= ATOL
+
+
+def test_gqa_mfma_work_queue_counters():
+    """The work-queue counters at the start of the workspace are zero after
+    every call.  A counter that did not start at zero makes that unit's
+    output NaN (some super-chunks would be skipped) instead of a wrong
+    number, the call still returns them to zero, and the next call is right."""
+    w = _w(450, 2, 4000, 2, 32, 128, 1)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    q = gen_queries(w, 0, "cuda")[0].contiguous()
+    cache, ref = _cache(w), _ref(w)
+    cache.prefill(k, v)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    ref.prefill(host(k), host(v))
+    ref.append(host(kn[0]), host(vn[0]))
+    want = oracle_attention(ref, host(q), 1 / math.sqrt(128))
+    units = w.batch * w.num_kv_heads
+    ws = cache.workspace(splits=1)
+    ctr = ws.view(torch.int32)[: 2 * units]
+    out = _attention(cache, q, "mfma", workspace=ws, splits=1)
+    torch.cuda.synchronize()
+    assert max_err(out, want) <= ATOL
+    assert int(ctr.abs().sum()) == 0, host(ctr)
+    u = units - 1                         # unit (batch 1, kv head 1): query heads 4..7 of batch 1
+    ctr[2 * u] = 5                        # a ticket that did not start at zero
+    out = host(_attention(cache, q, "mfma", workspace=ws, splits=1))
+    b, h = divmod(u, w.num_kv_heads)
+    bad = out[b, 4 * h:4 * h + 4]
+    assert np.isnan(bad).all(), "a miscounted unit must come out NaN"
+    keep = np.ones(out.shape[:2], bool)
+    keep[b, 4 * h:4 * h + 4] = False
+    assert float(np.abs(out[keep].astype(np.float64) - want[keep]).max()) <= ATOL
+    assert int(ctr.abs().sum()) == 0, host(ctr)
+    assert max_err(_attention(cache, q, "mfma", workspace=ws, splits=1), want) <= ATOL
