@@ -251,6 +251,81 @@ __device__ __forceinline__ float merge_records(const float *__restrict__ p, int 
   return acc / L;
 }
 
+// Agent-scope atomic load: reads what another XCD wrote with an agent-scope
+// atomic store.
+struct CoherentLoad {
+  __device__ float operator()(const float *p) const {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+// Work queue of one unit: its workgroups' waves take chunks of its tokens
+// from a ticket counter (ctr[0]); ctr[1] counts finished workgroups (bits
+// 24..31) and the chunks they took (bits 0..23).
+__device__ __forceinline__ uint32_t queue_grab(uint32_t *ctr, int lane) {
+  uint32_t v = 0;
+  if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;   // in lane 0; read it (readlane) a chunk later
+}
+
+// End of a part whose waves took their chunks from the unit's queue.
+// s_flag: LDS, [NW] chunks taken per wave, then one word for the result.
+// With several parts, the part's (acc, m, l) record goes out with
+// agent-scope atomic stores (the records cross XCDs, whose L2 caches are not
+// kept coherent for ordinary stores) and every wave waits for its own stores
+// before the workgroup is counted in.  The unit's last workgroup checks the
+// chunk count (a count short of nchunks means the counters did not start at
+// zero: its outputs are NaN instead of a wrong result), returns both
+// counters to zero for the next call and merges every record of the unit;
+// a single part writes the normalized output itself.
+template <int HPG, int NW>
+__device__ void queue_finish(const AttnArgs &a, int unit, int split, const Stage &st, uint32_t *s_flag,
+                             uint32_t nchunks) {
+  const int tid = threadIdx.x, nthreads = blockDim.x;
+  const int b = unit / a.hkv, hk = unit % a.hkv;
+  uint32_t *ctr = a.ctr + 2 * unit;
+  if (a.nparts > 1) {
+    for (int i = tid; i < HPG * (kHeadDim + 2); i += nthreads) {
+      const int h = i / (kHeadDim + 2), c = i % (kHeadDim + 2);
+      const int64_t bh = (int64_t)b * a.hq + hk * HPG + h;
+      float *rec = a.partials + (bh * a.nparts + split) * kPartialStride;
+      __hip_atomic_store(rec + c, c < kHeadDim ? st.acc[h * kHeadDim + c] : st.ml[2 * h + (c - kHeadDim)],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    uint32_t took = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) took += s_flag[w];
+    const uint32_t old = __hip_atomic_fetch_add(ctr + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t last = 0;
+    if ((old >> 24) == (uint32_t)(a.splits - 1)) {
+      last = ((old & 0xffffffu) + took == nchunks) ? 1u : 2u;
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_flag[NW] = last;
+  }
+  __syncthreads();
+  const uint32_t last = s_flag[NW];
+  if (a.nparts == 1) {
+    if (last == 2 && tid < HPG) st.ml[2 * tid + 1] = __builtin_nanf("");
+    __syncthreads();
+    finish_part<HPG>(a, unit, split, st);
+    return;
+  }
+  if (last == 0) return;
+  for (int i = tid; i < HPG * kHeadDim; i += nthreads) {
+    const int h = i / kHeadDim, c = i % kHeadDim;
+    const int64_t bh = (int64_t)b * a.hq + hk * HPG + h;
+    a.out[bh * kHeadDim + c] =
+        last == 2 ? __builtin_nanf("")
+                  : merge_records(a.partials + bh * a.nparts * kPartialStride, a.nparts, c, CoherentLoad());
+  }
+}
+
 // Occupancy target: four waves per SIMD (at most 128 VGPRs) for the MHA
 // tilings, two for the grouped-query tiling that keeps 4 heads in registers.
 template <int HPG>

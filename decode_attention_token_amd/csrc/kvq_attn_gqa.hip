@@ -416,14 +416,6 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
   __syncthreads();
 }
 
-// Agent-scope atomic load: reads what another XCD wrote with an agent-scope
-// atomic store.
-struct CoherentLoad {
-  __device__ float operator()(const float *p) const {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-};
-
 template <int BITS, int GS, int META>
 __global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(kGqaWavesPerEU, kGqaWavesPerEU)))
 void gqa_mfma_kernel(AttnArgs a) {
@@ -470,11 +462,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   const int nw = a.splits * kGqaWaves;
   const int slot = split * kGqaWaves + wave;
   uint32_t *const ticket = a.ctr + 2 * unit;
-  auto grab = [&]() -> uint32_t {   // in lane 0; read at the next super-chunk
-    uint32_t v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return v;
-  };
+  auto grab = [&]() { return queue_grab(ticket, lane); };   // read at the next super-chunk
   auto live_steps = [&](uint32_t id) { return (ngroups - 4 * (int)id < 4 ? ngroups - 4 * (int)id : 4) * SPG; };
   // ids compare unsigned, so any value past the end (however large) ends the wave
   uint32_t idL = slot, idL1 = nw + slot;   // super-chunk of the load cursor, and the next one
@@ -904,52 +892,7 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  // Several parts: publish this part's record, then count the workgroup in;
-  // the unit's last workgroup merges every record.  The records cross XCDs,
-  // whose L2 caches are not kept coherent for ordinary stores, so they are
-  // written and read with agent-scope atomic accesses (through to memory),
-  // and every wave waits for its own stores to complete before the count.
-  if (a.nparts > 1) {
-    for (int i = tid; i < kHpg * (kHeadDim + 2); i += kGqaThreads) {
-      const int h = i / (kHeadDim + 2), c = i % (kHeadDim + 2);
-      const int64_t bh = (int64_t)b * a.hq + hk * kHpg + h;
-      float *rec = a.partials + (bh * a.nparts + split) * kPartialStride;
-      __hip_atomic_store(rec + c, c < kHeadDim ? st.acc[h * kHeadDim + c] : st.ml[2 * h + (c - kHeadDim)],
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  if (tid == 0) {
-    uint32_t took = 0;
-#pragma unroll
-    for (int w = 0; w < kGqaWaves; ++w) took += s_took[w];
-    const uint32_t old =
-        __hip_atomic_fetch_add(ticket + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t last = 0;
-    if ((old >> 24) == (uint32_t)(a.splits - 1)) {
-      last = ((old & 0xffffffu) + took == (uint32_t)nsc) ? 1u : 2u;
-      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ticket + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    s_took[kGqaWaves] = last;
-  }
-  __syncthreads();
-  const uint32_t last = s_took[kGqaWaves];
-  if (a.nparts == 1) {   // the only part: normalized output straight from the workgroup
-    if (last == 2 && tid < kHpg) st.ml[2 * tid + 1] = __builtin_nanf("");
-    __syncthreads();
-    finish_part<kHpg>(a, unit, split, st);
-    return;
-  }
-  if (last == 0) return;
-  for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads) {
-    const int h = i / kHeadDim, c = i % kHeadDim;
-    const int64_t bh = (int64_t)b * a.hq + hk * kHpg + h;
-    a.out[bh * kHeadDim + c] =
-        last == 2 ? __builtin_nanf("")
-                  : merge_records(a.partials + bh * a.nparts * kPartialStride, a.nparts, c, CoherentLoad());
-  }
+  queue_finish<kHpg, kGqaWaves>(a, unit, split, st, s_took, (uint32_t)nsc);
 }
 
 template <int BITS, int GS, int META>

@@ -339,6 +339,7 @@ void innerq_attn_kernel(AttnArgs a) {
   using Buf = IqBuf<WPL>;
 
   __shared__ __attribute__((aligned(16))) float smem[kRedFloats<HPG> + kStageFloats<HPG>];
+  __shared__ uint32_t s_done[kWaves + 1];   // no work queue here (zeros); then the last-part flag
   const Stage st = stage_of<HPG>(smem, kRedFloats<HPG>);
 
   const int units = a.batch * a.hkv;
@@ -469,6 +470,8 @@ void innerq_attn_kernel(AttnArgs a) {
     }
   }
 
+  if (lane == 0) s_done[wave] = 0;
+
   // fp16 tokens: sinks [0, nsink) from the sink rows, then the window
   // [nq, n) from ring slots t mod R
   if (split == a.splits - 1) {
@@ -498,7 +501,10 @@ void innerq_attn_kernel(AttnArgs a) {
   }
 
   combine_waves<HPG, LPT, 1>(o, smem, st, wave, lane, INV_U);
-  finish_part<HPG>(a, unit, split, st);
+  // each wave keeps its contiguous step range (the kernel streams HBM near
+  // its ceiling, and scattered chunks lost more than balancing gained); the
+  // unit's last workgroup merges the split records
+  queue_finish<HPG, kWaves>(a, unit, split, st, s_done, 0u);
 }
 
 template <int BITS, int GS, int HPG>
@@ -566,9 +572,8 @@ hipError_t launch_innerq_append(const CacheView &c, int units, const uint16_t *k
 }
 
 hipError_t launch_innerq_attention(const AttnArgs &a, hipStream_t s) {
-  hipError_t e = (a.c.bits == 2) ? launch_iq_by_group<2>(a, s) : launch_iq_by_group<4>(a, s);
-  if (e != hipSuccess) return e;
-  return launch_merge(a, s);
+  // the unit's last workgroup merges the split records itself
+  return (a.c.bits == 2) ? launch_iq_by_group<2>(a, s) : launch_iq_by_group<4>(a, s);
 }
 
 }  // namespace kvq
