@@ -11,6 +11,8 @@ Prints one JSON line:
   tokens_per_s batch * steps / loop time
   roofline     split-kernel bytes per launch / its average duration (HIP
                events on the library's stream), against 8 TB/s
+  fp16_equivalent  bytes an fp16 cache of the same tokens would move per
+               call / the same call time (labelled; not a roofline fraction)
   cpu_baseline the NumPy oracle's decode-attention call on a sample of units,
                timed on this host, scaled to the same byte formula
 """
@@ -330,7 +332,7 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     last = total - 1
-    calls, cb = 0, 0
+    calls, cb, fb = 0, 0, 0
     ev0.record(stream)
     for _ in range(args.reps):
         for layer in range(layers):
@@ -338,6 +340,7 @@ def main():
             c.attention(qs[layer][last], scale, outs[layer], ws, args.splits, sp)
             calls += 1
             cb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
+            fb += w.units * c.n_tokens * w.head_dim * 2 * 2 + w.batch * w.num_q_heads * w.head_dim * 6
     ev1.record(stream)
     torch.cuda.synchronize()
     call_us = ev0.elapsed_time(ev1) * 1e3 / calls
@@ -381,6 +384,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
                      "kernel": KERNELS[kernel_key(w)][0], "avg_call_us": round(call_us, 2),
                      "bytes_per_call": int(call_bytes)},
+        # what an fp16 cache of the same tokens would move per call, over the
+        # same call time: a compression view, not a roofline fraction
+        "fp16_equivalent": {"GB/s": round(fb / calls / (call_us * 1e-6) / 1e9, 1),
+                            "bytes_per_call": int(fb / calls)},
     }
     if side is not None:
         res.update(side)
