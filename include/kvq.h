@@ -230,7 +230,14 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
  * outputs instead of a wrong result); calls that share a workspace must be
  * ordered on one stream.  splits: 0 =
  * automatic, else 1..64.  One kernel launch when every unit fits one part,
- * else a second (merge) launch.  Needs started and n_tokens >= 1. */
+ * else a second (merge) launch, except for the matrix-core kernel (four query
+ * heads per kv head) and the InnerQ kernel, which merge inside their one
+ * launch.  Needs started and n_tokens >= 1.
+ * Environment (read at each call): KVQ_GQA_PATH=valu runs four query heads
+ * per kv head on the vector-ALU kernel instead of the matrix-core one;
+ * KVQ_DETERMINISTIC=1 makes the matrix-core kernel hand out its work in a
+ * fixed order (bit-identical reruns) instead of from its per-unit work queue,
+ * whose run-dependent order changes only the rounding of fp32 partial sums. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                 const uint16_t *q, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, int32_t splits,
