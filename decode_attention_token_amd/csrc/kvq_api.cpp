@@ -337,6 +337,17 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
     if (e != hipSuccess) return device_error(e, "quantize popped value");
     nq_v += 1;
   }
+  if (cfg->v_policy == KVQ_V_CHUNK && (n + 1) - nq_k == R && nq_v == nq_k) {
+    // both rings fill with this token: one launch quantizes them, reading the
+    // new token from k_new / v_new; no ring slot is live afterwards
+    e = kvq::launch_flush(cv, units, k_new, v_new, (int)(n % R), nq_k / G, nq_v, stream);
+    if (e != hipSuccess) return device_error(e, "flush");
+    cache->n_tokens = S + n + 1;
+    cache->nq_k = cache->nq_v = S + n + 1;
+    cache->flushes = flushes + 1;
+    g_err[0] = 0;
+    return KVQ_OK;
+  }
   e = kvq::launch_copy_to_residual(cv, units, k_new, v_new, 1, 0, 1, (int)(n % R), true, true, stream);
   if (e != hipSuccess) return device_error(e, "append to residual");
   n += 1;

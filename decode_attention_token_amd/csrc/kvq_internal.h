@@ -40,6 +40,13 @@ hipError_t launch_quantize_keys(const CacheView &c, int units, const uint16_t *s
 
 // Quantize `count` value rows per unit (source row src_row0 + i) into
 // destination token rows dst_row0 + i.
+// Chunked residual flush of both rings in one launch: the R ring slots in
+// token order, ring slot `slot` read from k_new / v_new ([unit][128]) instead
+// (the token the same append brings), keys into group dst_group0 and values
+// into row dst_row0 of every unit.  The ring slots are left as they are.
+hipError_t launch_flush(const CacheView &c, int units, const uint16_t *k_new, const uint16_t *v_new, int slot,
+                        int64_t dst_group0, int64_t dst_row0, hipStream_t s);
+
 hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t *src,
                                   int64_t src_rows, int64_t src_row0, int count,
                                   int64_t dst_row0, hipStream_t s);

@@ -46,17 +46,21 @@ __device__ __forceinline__ f16x2 max_over_rows(f16x2 x) {
 // wave) and hands them to the others through LDS, laid out so that each read
 // instruction touches 16 consecutive entries.  Codes are packed into
 // token rows in registers and stored as 256 contiguous bytes per instruction.
+// Block `blk` of a grid of 4-wave blocks.  ovr (null: unused) supplies
+// source row ovr_row of every unit ([unit][128] fp16) in place of the row in
+// src: a flush reads the token appended by the same call from there.
 template <int BITS, int GS>
-__global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
-                                                            int64_t src_rows, int64_t src_row0,
-                                                            int64_t dst_group0, int ngroups, int total) {
+__device__ __forceinline__ void quantize_keys_block(const CacheView &c, const uint16_t *__restrict__ src,
+                                                    int64_t src_rows, int64_t src_row0, int64_t dst_group0,
+                                                    int ngroups, int total, int blk,
+                                                    const uint16_t *__restrict__ ovr, int64_t ovr_row) {
   constexpr int RL = GS / 4;                  // rows per lane
   constexpr int PER = 32 / BITS;              // codes per word
   constexpr int W = kHeadDim / PER;           // words per token row
   constexpr float QMAX = float((1 << BITS) - 1);
   __shared__ float4 s_par[4][8][16];          // [wave][channel % 8][channel / 8]: r, z, thr, s
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gi = (int)blockIdx.x * 4 + wave;
+  const int gi = blk * 4 + wave;
   if (gi >= total) return;                    // wave-uniform
   const int unit = gi / ngroups, g = gi - unit * ngroups;
   const int cs = lane & 15, q = lane >> 4;
@@ -64,9 +68,11 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
   const uint4 *in =
       reinterpret_cast<const uint4 *>(src + ((int64_t)unit * src_rows + src_row0 + (int64_t)g * GS + q) * kHeadDim) +
       cs;
+  const int64_t srow = src_row0 + (int64_t)g * GS + q;   // source row of raw[0]
+  const uint4 *ov = ovr ? reinterpret_cast<const uint4 *>(ovr + (int64_t)unit * kHeadDim) + cs : nullptr;
   uint4 raw[RL];
 #pragma unroll
-  for (int i = 0; i < RL; ++i) raw[i] = in[i * 4 * (kHeadDim / 8)];
+  for (int i = 0; i < RL; ++i) raw[i] = (ov && srow + 4 * i == ovr_row) ? *ov : in[i * 4 * (kHeadDim / 8)];
 
   f16x2 mn[4], mx[4];
 #pragma unroll
@@ -149,9 +155,10 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const u
 // the parameter divisions and share the results through LDS; codes are
 // packed and stored as for keys.
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const uint16_t *__restrict__ src,
-                                                              int64_t src_rows, int64_t src_row0, int count,
-                                                              int64_t dst_row0, int total_rows) {
+__device__ __forceinline__ void quantize_values_block(const CacheView &c, const uint16_t *__restrict__ src,
+                                                      int64_t src_rows, int64_t src_row0, int count,
+                                                      int64_t dst_row0, int total_rows, int blk,
+                                                      const uint16_t *__restrict__ ovr, int64_t ovr_row) {
   constexpr int NR = 8;                       // rows per lane
   constexpr int LPG = G / 8;                  // lanes per value group
   constexpr int NG = kHeadDim / G;            // value groups per row
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   __shared__ float4 s_par[4][NR][4][NG];      // [wave][row][l / 16][group]: r, z, thr, s
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cs = lane & 15, q = lane >> 4, j = cs / LPG, gl = cs % LPG;
-  const int row0 = ((int)blockIdx.x * 4 + wave) * 4 * NR;
+  const int row0 = (blk * 4 + wave) * 4 * NR;
   if (row0 >= total_rows) return;             // wave-uniform
   // (unit, token) of the lane's row i, stepped from the block's first row
   // (one wave-uniform division per block)
@@ -184,7 +191,9 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
     if (valid(i)) {
       int u, t;
       locate(i, u, t);
-      raw[i] = *(reinterpret_cast<const uint4 *>(src + ((int64_t)u * src_rows + src_row0 + t) * kHeadDim) + cs);
+      raw[i] = (ovr && src_row0 + t == ovr_row)
+                   ? *(reinterpret_cast<const uint4 *>(ovr + (int64_t)u * kHeadDim) + cs)
+                   : *(reinterpret_cast<const uint4 *>(src + ((int64_t)u * src_rows + src_row0 + t) * kHeadDim) + cs);
     }
   }
 
@@ -272,6 +281,39 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const
   }
 }
 
+template <int BITS, int GS>
+__global__ __launch_bounds__(256) void quantize_keys_kernel(CacheView c, const uint16_t *__restrict__ src,
+                                                            int64_t src_rows, int64_t src_row0,
+                                                            int64_t dst_group0, int ngroups, int total) {
+  quantize_keys_block<BITS, GS>(c, src, src_rows, src_row0, dst_group0, ngroups, total, (int)blockIdx.x, nullptr, -1);
+}
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void quantize_values_kernel(CacheView c, const uint16_t *__restrict__ src,
+                                                              int64_t src_rows, int64_t src_row0, int count,
+                                                              int64_t dst_row0, int total_rows) {
+  quantize_values_block<BITS, G>(c, src, src_rows, src_row0, count, dst_row0, total_rows, (int)blockIdx.x, nullptr,
+                                 -1);
+}
+
+// Residual flush of both rings in one launch (the key groups, then the value
+// rows, of the R ring slots in token order), with the token appended by the
+// same call read from k_new / v_new at its ring slot `slot`.  The ring slot
+// itself is not written: once flushed, no ring slot is live.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void flush_kernel(CacheView c, const uint16_t *__restrict__ k_new,
+                                                    const uint16_t *__restrict__ v_new, int slot,
+                                                    int64_t dst_group0, int64_t dst_row0, int units, int kblocks) {
+  const int R = c.residual;
+  if ((int)blockIdx.x < kblocks) {
+    quantize_keys_block<BITS, G>(c, c.k_resid, R, 0, dst_group0, R / G, units * (R / G), (int)blockIdx.x, k_new,
+                                 slot);
+  } else {
+    quantize_values_block<BITS, G>(c, c.v_resid, R, 0, R, dst_row0, units * R, (int)blockIdx.x - kblocks, v_new,
+                                   slot);
+  }
+}
+
 // Copies fp16 rows into ring-indexed destination rows (the residual rings or
 // the sink rows), 16 bytes per thread; the second half of the grid (when both
 // destinations are given) copies the value rows.
@@ -343,6 +385,30 @@ hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t 
     else KVQ_QV(4, 128);
   }
 #undef KVQ_QV
+  return hipGetLastError();
+}
+
+hipError_t launch_flush(const CacheView &c, int units, const uint16_t *k_new, const uint16_t *v_new, int slot,
+                        int64_t dst_group0, int64_t dst_row0, hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  const int64_t kwaves = (int64_t)units * (c.residual / c.group);   // one key group per wave
+  const int64_t vrows = (int64_t)units * c.residual;                // 32 value rows per wave
+  if (vrows > INT32_MAX - 256) return hipErrorInvalidValue;
+  const int kblocks = (int)((kwaves + 3) / 4);
+  const int vblocks = (int)((vrows + 127) / 128);
+#define KVQ_FL(B, G)                                                                                          \
+  hipLaunchKernelGGL((flush_kernel<B, G>), dim3(kblocks + vblocks), dim3(256), 0, s, c, k_new, v_new, slot, \
+                     dst_group0, dst_row0, units, kblocks)
+  if (c.bits == 2) {
+    if (c.group == 32) KVQ_FL(2, 32);
+    else if (c.group == 64) KVQ_FL(2, 64);
+    else KVQ_FL(2, 128);
+  } else {
+    if (c.group == 32) KVQ_FL(4, 32);
+    else if (c.group == 64) KVQ_FL(4, 64);
+    else KVQ_FL(4, 128);
+  }
+#undef KVQ_FL
   return hipGetLastError();
 }
 
