@@ -13,6 +13,8 @@ Prints one JSON line:
                events on the library's stream), against 8 TB/s
   fp16_equivalent  bytes an fp16 cache of the same tokens would move per
                call / the same call time (labelled; not a roofline fraction)
+  stream_ceiling  GB/s of the library's plain streaming-read probe over
+               4 GiB, and the roofline's achieved rate as a fraction of it
   cpu_baseline the NumPy oracle's decode-attention call on a sample of units,
                timed on this host, scaled to the same byte formula
 """
@@ -52,6 +54,27 @@ def attn_bytes(w, n, nq_k, nq_v):
         per_unit = (qk * d * b // 8 + (qk // G) * d * mb + qv * d * b // 8 + qv * (d // G) * mb
                     + ((n - qk) + (n - qv)) * d * 2)
     return w.batch * w.num_kv_heads * per_unit + w.batch * w.num_q_heads * d * 6
+
+
+def stream_ceiling(dev, stream, reps=5):
+    """GB/s of kvq_stream_read_probe over a 4 GiB buffer (16x the MALL),
+    timed with HIP events on the given stream."""
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    sp = stream.cuda_stream
+    for _ in range(2):
+        kvq.kvq_stream_read_probe(buf, out, sp)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        kvq.kvq_stream_read_probe(buf, out, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, out
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def make_cfg(w, max_tokens):
@@ -348,6 +371,7 @@ def main():
     achieved = call_bytes / (call_us * 1e-6) / 1e9
 
     side = time_prefill_and_flush(w, dev, stream) if not args.no_side else None
+    ceiling = stream_ceiling(dev, stream)
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic: reads and writes 256 MiB
@@ -388,6 +412,10 @@ def main():
         # same call time: a compression view, not a roofline fraction
         "fp16_equivalent": {"GB/s": round(fb / calls / (call_us * 1e-6) / 1e9, 1),
                             "bytes_per_call": int(fb / calls)},
+        # the library's plain streaming-read kernel over 4 GiB on this device:
+        # the achievable read rate, for context beside the 8 TB/s peak
+        "stream_ceiling": {"GB/s": round(ceiling, 1), "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4),
+                           "roofline_frac_of_ceiling": round(achieved / ceiling, 4)},
     }
     if side is not None:
         res.update(side)

@@ -24,7 +24,8 @@ KVQ_META_F32, KVQ_META_F16 = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
-    "kvq_append_token", "kvq_decode_attention", "kvq_decode_step", "kvq_status_string", "kvq_last_error",
+    "kvq_append_token", "kvq_decode_attention", "kvq_decode_step", "kvq_stream_read_probe", "kvq_status_string",
+    "kvq_last_error",
 ]
 
 
@@ -86,6 +87,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_step.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, vp, ctypes.c_float, vp, vp,
                                     ctypes.c_size_t, ctypes.c_int32, vp]
     lib.kvq_decode_step.restype = ctypes.c_int
+    lib.kvq_stream_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.kvq_stream_read_probe.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_last_error.argtypes = []
@@ -282,3 +285,12 @@ def kvq_decode_step(cfg, cache: KVCache, k_new, v_new, q, softmax_scale, out, wo
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib_handle.kvq_decode_step(cache._cfg_ref, cache._c_ref, kp, vp, qp, softmax_scale, out.data_ptr(),
                                        workspace.data_ptr(), nbytes, splits, _stream_ptr(stream)))
+
+
+def kvq_stream_read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None):
+    """Streaming-read probe over a device buffer (measurement only): reads
+    every byte of `buf` once; `out` is a device int32 scratch word."""
+    if not buf.is_cuda or not out.is_cuda:
+        raise ValueError("buf and out must be device tensors")
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().kvq_stream_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), _stream_ptr(stream)))

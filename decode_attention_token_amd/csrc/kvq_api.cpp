@@ -511,6 +511,16 @@ kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16
   return KVQ_OK;
 }
 
+kvq_status kvq_stream_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream) {
+  if (!buf || !out) return fail(KVQ_ERR_ARG, "buf or out is null");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(KVQ_ERR_ARG, "probe buffer must be 16-byte aligned and a non-zero multiple of 16 bytes");
+  const hipError_t e = kvq::launch_stream_read(buf, bytes, out, stream);
+  if (e != hipSuccess) return device_error(e, "stream-read probe");
+  g_err[0] = 0;
+  return KVQ_OK;
+}
+
 const char *kvq_status_string(kvq_status s) {
   switch (s) {
     case KVQ_OK: return "ok";

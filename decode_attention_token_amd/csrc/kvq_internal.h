@@ -118,4 +118,7 @@ hipError_t launch_innerq_attention(const AttnArgs &a, hipStream_t s);
 // Second launch that merges the part records when nparts > 1 (no-op else).
 hipError_t launch_merge(const AttnArgs &a, hipStream_t s);
 
+// Streaming-read probe over `bytes` (a multiple of 16) of device memory.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
+
 }  // namespace kvq

@@ -255,6 +255,16 @@ kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16
                            const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream);
 
+/* Measurement only, not part of the attention path: reads `bytes` of device
+ * memory at buf (16-byte aligned, bytes a non-zero multiple of 16) with a
+ * plain streaming kernel, so a caller can time the device's achievable HBM
+ * read rate and compare the decode kernels' bandwidth with it as well as
+ * with the specification's peak.  out: device, one u32 the kernel writes
+ * only in a case a buffer of ones never produces (it keeps the loads live).
+ * KVQ_ERR_ARG for a null pointer, misalignment or a bad size; stream-ordered,
+ * never synchronizes. */
+kvq_status kvq_stream_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *kvq_status_string(kvq_status s);
 

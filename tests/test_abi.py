@@ -298,3 +298,15 @@ def test_workspace_and_split_sizing(lib):
         cur = kvq.kvq_auto_splits(c, n)
         assert cur >= prev
         prev = cur
+
+
+def test_stream_read_probe_rejects_bad_arguments_on_the_host(lib):
+    """Measurement probe: null pointers, a size that is not a non-zero
+    multiple of 16 and a misaligned buffer fail before any device work."""
+    P = ctypes.c_void_p
+    assert lib.kvq_stream_read_probe(None, 1024, P(64), None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_stream_read_probe(P(64), 1024, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_stream_read_probe(P(64), 0, P(64), None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_stream_read_probe(P(64), 1000, P(64), None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_stream_read_probe(P(72), 1024, P(64), None) == kvq.KVQ_ERR_ARG
+    assert b"16" in lib.kvq_last_error()
