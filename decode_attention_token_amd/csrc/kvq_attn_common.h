@@ -277,7 +277,10 @@ __device__ __forceinline__ uint32_t queue_grab(uint32_t *ctr, int lane) {
 // chunk count (a count short of nchunks means the counters did not start at
 // zero: its outputs are NaN instead of a wrong result), returns both
 // counters to zero for the next call and merges every record of the unit;
-// a single part writes the normalized output itself.
+// a single part writes the normalized output itself.  "Last" is the
+// workgroup count modulo the split count, so a count field that did not
+// start at zero still elects one workgroup, and its chunk count (which
+// cannot match then) makes the output NaN rather than leaving it unwritten.
 template <int HPG, int NW>
 __device__ void queue_finish(const AttnArgs &a, int unit, int split, const Stage &st, uint32_t *s_flag,
                              uint32_t nchunks) {
@@ -301,7 +304,7 @@ __device__ void queue_finish(const AttnArgs &a, int unit, int split, const Stage
     for (int w = 0; w < NW; ++w) took += s_flag[w];
     const uint32_t old = __hip_atomic_fetch_add(ctr + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t last = 0;
-    if ((old >> 24) == (uint32_t)(a.splits - 1)) {
+    if ((old >> 24) % (uint32_t)a.splits == (uint32_t)(a.splits - 1)) {
       last = ((old & 0xffffffu) + took == nchunks) ? 1u : 2u;
       __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -204,3 +204,16 @@ def test_gqa_mfma_work_queue_counters():
     assert float(np.abs(out[keep].astype(np.float64) - want[keep]).max()) <= ATOL
     assert int(ctr.abs().sum()) == 0, host(ctr)
     assert max_err(_attention(cache, q, "mfma", workspace=ws, splits=1), want) <= ATOL
+
+    # two splits, finished-workgroup count not starting at zero: the unit's
+    # output must come out NaN, not stale (nothing would be written if no
+    # workgroup saw itself as the last one)
+    ws2 = cache.workspace(splits=2)
+    ctr2 = ws2.view(torch.int32)[: 2 * units]
+    out2 = torch.zeros_like(torch.from_numpy(want).float()).cuda()
+    ctr2[2 * u + 1] = 1 << 24
+    _attention(cache, q, "mfma", workspace=ws2, splits=2, out=out2)
+    torch.cuda.synchronize()
+    got = host(out2)
+    assert np.isnan(got[b, 4 * h:4 * h + 4]).all(), "a miscounted unit must come out NaN"
+    assert float(np.abs(got[keep].astype(np.float64) - want[keep]).max()) <= ATOL
