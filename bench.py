@@ -2,21 +2,31 @@
 
 A step is one decode step of the whole batch through every layer of the
 workload: per layer, kvq_decode_step = kvq_append_token (residual write, eager
-flush when due) + kvq_decode_attention, one kernel launch when no flush is due.  Caches are prefilled before
-timing; inputs for every step are resident in HBM when timing starts.
+flush when due) + kvq_decode_attention, one kernel launch when no flush is
+due.  Caches are prefilled before timing; inputs for every step are resident
+in HBM when timing starts.
 
 Prints one JSON line:
   value        effective KV GB/s of the whole timed loop (algorithmic bytes of
                every attention call / loop time)
   tokens_per_s batch * steps / loop time
-  roofline     split-kernel bytes per launch / its average duration (HIP
-               events on the library's stream), against 8 TB/s
+  roofline     the decode kernel as the timed loop launches it (the fused
+               append + attention step): algorithmic bytes per launch / its
+               average duration, from HIP events on the library's stream
+               around the timed loop, against 8 TB/s
+  attention_only  the same kernel launched by kvq_decode_attention alone
+               (back-to-back passes over the layers, HIP events)
   fp16_equivalent  bytes an fp16 cache of the same tokens would move per
-               call / the same call time (labelled; not a roofline fraction)
+               call / the attention-only call time (labelled; not a roofline
+               fraction)
   stream_ceiling  GB/s of the library's plain streaming-read probe over
                4 GiB, and the roofline's achieved rate as a fraction of it
-  cpu_baseline the NumPy oracle's decode-attention call on a sample of units,
-               timed on this host, scaled to the same byte formula
+  prefill, flush  HIP-event timings of one prefill and one flushing append
+  tiny         latency of one decode step on the tiny workload
+  cpu_baseline the NumPy oracle on sampled units, timed on this host: one
+               thread and a process pool over the host cores, scaled to the
+               same byte formula; plus one oracle prefill and one flush
+  source       content digests of the sources that produced the numbers
 """
 from __future__ import annotations
 
@@ -77,13 +87,13 @@ def stream_ceiling(dev, stream, reps=5):
     return gbs
 
 
-def make_cfg(w, max_tokens):
+def make_cfg(w, max_tokens, schedule=kvq.KVQ_SCHED_FIXED, kernel=kvq.KVQ_KERNEL_AUTO):
     return kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks, w.meta)
+                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks, w.meta, schedule, kernel)
 
 
-def build_caches(w, layers, max_tokens, dev):
-    cfg = make_cfg(w, max_tokens)
+def build_caches(w, layers, max_tokens, dev, schedule=kvq.KVQ_SCHED_FIXED, kernel=kvq.KVQ_KERNEL_AUTO):
+    cfg = make_cfg(w, max_tokens, schedule, kernel)
     caches = []
     for layer in range(layers):
         k, v = gen_prefill(w, layer, dev)
@@ -96,7 +106,11 @@ def build_caches(w, layers, max_tokens, dev):
     return cfg, caches
 
 
-def sample_units(w, count=512, seed=7):
+def sample_units(w, host_bytes=512 << 20, seed=7):
+    """A seeded sample of (batch, kv head) units for the oracle, as many as
+    fit about host_bytes of fp16 prompt (at least 4, at most 64)."""
+    per_unit = w.context * w.head_dim * 2 * 2
+    count = max(4, min(64, host_bytes // max(per_unit, 1), w.units))
     return [int(u) for u in np.random.default_rng(seed).permutation(w.units)[:count]]
 
 
@@ -111,12 +125,12 @@ KERNELS = {
 }
 
 
-def kernel_key(w):
+def kernel_key(w, kernel=kvq.KVQ_KERNEL_AUTO):
     """Which decode kernel dominates the workload: the matrix-core kernel for
-    four query heads per kv head (KIVI layout, unless KVQ_GQA_PATH=valu),
-    else the scheme's vector-ALU kernel."""
+    four query heads per kv head (KIVI layout, unless the config selects the
+    vector-ALU kernel), else the scheme's vector-ALU kernel."""
     if (w.scheme == kvq.KVQ_SCHEME_KIVI and w.num_q_heads == 4 * w.num_kv_heads
-            and os.environ.get("KVQ_GQA_PATH") != "valu"):
+            and kernel == kvq.KVQ_KERNEL_AUTO):
         return "gqa4"
     return w.scheme
 
@@ -130,17 +144,18 @@ def kernel_source_digest(scheme=0):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(w):
+def measured_traffic(w, kernel=kvq.KVQ_KERNEL_AUTO):
     """HBM bytes per launch of the decode kernel from the committed counter
     summary, or None when it is missing, for another workload, or taken on a
     different kernel source."""
+    key = kernel_key(w, kernel)
     try:
-        with open(os.path.join(ROOT, "profiles", KERNELS[kernel_key(w)][2])) as f:
+        with open(os.path.join(ROOT, "profiles", KERNELS[key][2])) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("kernel_source_digest") != kernel_source_digest(kernel_key(w)) or kv.get("workload") != w.name:
+    if kv.get("kernel_source_digest") != kernel_source_digest(key) or kv.get("workload") != w.name:
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -149,84 +164,182 @@ def measured_traffic(w):
 
 
 def host_sample(w, units, dev):
-    """Host copies of the sampled units' layer-0 inputs (the same fp16 bits the GPU caches use)."""
+    """Host copies of the sampled units' layer-0 inputs (the same fp16 bits
+    the GPU caches use): prompt K, V, R new tokens and the first query."""
     k, v = gen_prefill(w, 0, dev)
-    kn, vn = gen_new_tokens(w, 0, dev, steps=1)
+    kn, vn = gen_new_tokens(w, 0, dev, steps=w.residual)
     q = gen_queries(w, 0, dev, steps=1)[0]
     hpg = w.num_q_heads // w.num_kv_heads
     out = []
     for u in units:
         b, h = divmod(u, w.num_kv_heads)
         out.append((k[b:b + 1, h:h + 1].cpu().numpy(), v[b:b + 1, h:h + 1].cpu().numpy(),
-                    kn[0][b:b + 1, h:h + 1].cpu().numpy(), vn[0][b:b + 1, h:h + 1].cpu().numpy(),
+                    kn[:, b:b + 1, h:h + 1].cpu().numpy(), vn[:, b:b + 1, h:h + 1].cpu().numpy(),
                     q[b:b + 1, h * hpg:(h + 1) * hpg].cpu().numpy()))
-    del k, v
+    del k, v, kn, vn
     return out
 
 
-def cpu_baseline(w, sample, budget_s=12.0):
-    """The oracle's decode-attention call (dequantize + float64 attention) on
-    sampled units, one host thread, scaled by the algorithmic byte formula.
-    The sampled units are swept repeatedly until about budget_s seconds of
-    timed oracle work have accumulated."""
+def _oracle_unit_cache(w):
     import oracle
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        return oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+    if w.sinks:
+        return oracle.KiviSinkCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, w.v_policy, w.meta)
+    return oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy, w.meta)
+
+
+def _unit_attn_bytes(w, ref):
     hpg = w.num_q_heads // w.num_kv_heads
     unit_w = w.scaled(batch=1, num_kv_heads=1, num_q_heads=hpg)
-    refs = []
-    for k, v, kn, vn, q in sample:
-        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
-            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
-        elif w.sinks:
-            ref = oracle.KiviSinkCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, w.v_policy, w.meta)
-        else:
-            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy, w.meta)
-        ref.prefill(k, v)
-        ref.append(kn, vn)
-        refs.append((ref, q))
-    t_total, done, nbytes = 0.0, 0, 0
-    while t_total < budget_s:
-        for ref, q in refs:
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        return attn_bytes(unit_w, ref.n, ref.nq, ref.nq)
+    return attn_bytes(unit_w, ref.n, ref.nq_k, ref.nq_v)
+
+
+def _oracle_attention_worker(w, items, budget_s):
+    """Oracle decode-attention calls (dequantize + float64 attention) on the
+    given units, one thread (BLAS included), swept until budget_s seconds of
+    timed work: (bytes, seconds, calls)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        refs = []
+        for k, v, kn, vn, q in items:
+            ref = _oracle_unit_cache(w)
+            ref.prefill(k, v)
+            ref.append(kn[0], vn[0])
+            refs.append((ref, q, _unit_attn_bytes(w, ref)))
+        t_total, done, nbytes = 0.0, 0, 0
+        while t_total < budget_s:
+            for ref, q, nb in refs:
+                t0 = time.perf_counter()
+                K, V = ref.dequantized()
+                oracle.attention(q, K, V, 1.0 / math.sqrt(w.head_dim))
+                t_total += time.perf_counter() - t0
+                done += 1
+                nbytes += nb
+                if t_total >= budget_s:
+                    break
+    return nbytes, t_total, done
+
+
+def host_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_cores(limit=16):
+    """Cores this process may run on, capped at the host share of one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, limit))
+
+
+def cpu_baseline(w, sample, budget_s=10.0, pool_budget_s=6.0):
+    """The oracle timed on this host, on sampled units of the workload:
+    decode-attention calls (dequantize + float64 attention) on one thread and
+    in a process pool over the host cores (one BLAS thread per worker), each
+    scaled by the algorithmic byte formula; and one oracle prefill and one
+    flushing append per sampled unit (one thread), scaled to all units."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    import oracle  # noqa: F401  (the oracle is the baseline being timed)
+
+    one = _oracle_attention_worker(w, sample, budget_s)
+    cores = min(host_cores(), len(sample))
+    shards = [sample[i::cores] for i in range(cores)]
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.starmap(_oracle_attention_worker, [(w, sh, pool_budget_s) for sh in shards])
+    pool_bytes = sum(r[0] for r in res)
+    pool_s = max(r[1] for r in res)
+    pool_calls = sum(r[2] for r in res)
+
+    # one prefill and one flushing append per sampled unit, one thread
+    nunits = min(len(sample), 8)
+    t_pre = t_fl = 0.0
+    with threadpool_limits(limits=1):
+        for k, v, kn, vn, q in sample[:nunits]:
+            ref = _oracle_unit_cache(w)
             t0 = time.perf_counter()
-            K, V = ref.dequantized()
-            oracle.attention(q, K, V, 1.0 / math.sqrt(w.head_dim))
-            t_total += time.perf_counter() - t0
-            done += 1
-            nq = ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_k
-            nbytes += attn_bytes(unit_w, ref.n, nq, ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_v)
-            if t_total >= budget_s:
-                break
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} unit-calls over {len(refs)} of {w.units} (batch, kv-head) units: one "
-                      f"decode-attention call each (dequantize + float64 attention) at n={w.context + 1}, "
-                      f"same fp16 inputs as the GPU caches; {t_total:.1f} s on one host thread",
-            "seconds_per_call_extrapolated": round(t_total / done * w.units, 3)}
+            ref.prefill(k, v)
+            t_pre += time.perf_counter() - t0
+            # bring the residual to R - 1 tokens, then time the append that quantizes
+            if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+                need = 0
+            else:
+                need = (w.residual - 1) - (ref.n - ref.nq_k)
+            for i in range(need):
+                ref.append(kn[i], vn[i])
+            q0 = ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_k
+            t0 = time.perf_counter()
+            ref.append(kn[-1], vn[-1])
+            t_fl += time.perf_counter() - t0
+            assert (ref.nq if w.scheme == kvq.KVQ_SCHEME_INNERQ else ref.nq_k) > q0
+    pre_s = t_pre / nunits * w.units
+    fl_s = t_fl / nunits * w.units
+    pb, fb = prefill_bytes(w, w.context), flush_bytes(w)
+    return {"value": round(pool_bytes / pool_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "host": host_model(),
+            "sample": f"decode-attention calls (dequantize + float64 attention) of the NumPy oracle on {len(sample)} "
+                      f"of {w.units} (batch, kv head) units at n={w.context + 1}, same fp16 inputs as the GPU "
+                      f"caches: {pool_calls} unit-calls in a pool of {cores} processes (one BLAS thread each) "
+                      f"over {pool_s:.1f} s, scaled by the algorithmic byte formula",
+            "single_thread": {"value": round(one[0] / one[1] / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "calls": one[2], "seconds": round(one[1], 2),
+                              "seconds_per_call_extrapolated": round(one[1] / one[2] * w.units, 3)},
+            "pool_seconds_per_call_extrapolated": round(pool_s / pool_calls * cores * w.units / cores, 3),
+            "prefill": {"seconds_extrapolated": round(pre_s, 3), "bytes": pb,
+                        "GB/s": round(pb / pre_s / 1e9, 4), "cores": 1,
+                        "sample": f"oracle prefill of {w.context} tokens on {nunits} units, scaled to {w.units}"},
+            "flush": {"seconds_extrapolated": round(fl_s, 4), "bytes": fb, "GB/s": round(fb / fl_s / 1e9, 4),
+                      "cores": 1,
+                      "sample": f"oracle append that quantizes, on {nunits} units, scaled to {w.units}"}}
 
 
 def prefill_bytes(w, L):
-    """Bytes a prefill of L tokens must move: fp16 K and V in, codes +
-    metadata + fp16 residual (or sinks and window) out."""
+    """Bytes a prefill of L tokens must move: fp16 K and V in; codes,
+    metadata and the fp16 rows kept (sinks, residual or window) out."""
     d, b, G, R = w.head_dim, w.bits, w.group, w.residual
     if w.scheme == kvq.KVQ_SCHEME_INNERQ:
         m = max(0, L - w.sinks - R)
         out = m * 2 * (d * b // 8 + (d // G) * 6) + (L - m) * d * 2 * 2
     else:
         ns = min(L, w.sinks)
-        nq = (L - ns) - (L - ns) % R    # quantized tokens after the sinks
+        inner = L - ns
+        nq_k = inner - inner % R                                   # quantized keys after the sinks
+        nq_v = nq_k if w.v_policy == kvq.KVQ_V_CHUNK else max(0, inner - R)
         mb = 4 if w.meta else 6
-        out = nq * d * b // 8 * 2 + (nq // G) * d * mb + nq * (d // G) * mb + (L - nq) * d * 2 * 2
+        out = (nq_k * d * b // 8 + (nq_k // G) * d * mb + nq_v * d * b // 8 + nq_v * (d // G) * mb
+               + ((L - nq_k) + (L - nq_v)) * d * 2)
     return w.units * (L * d * 2 * 2 + out)
 
 
 def flush_bytes(w):
-    """Bytes one quantizing append must move (the append's own token write
-    included).  KIVI: R fp16 keys and values in, their codes and metadata
-    out.  InnerQ: the token leaving the window in, its codes and metadata
-    out."""
+    """Bytes of the append that quantizes (the bench times it with the key
+    residual at R - 1 tokens).  KIVI, chunked values: the R keys and values
+    (R - 1 ring slots and the new token) in, their codes and metadata out;
+    no ring slot is written.  KIVI, FIFO values: the R keys and the popped
+    value row in, their codes and metadata out, the new value into its ring
+    slot (the new key is one of the R).  InnerQ: the token leaving the window
+    and the new token in, the old one's codes and metadata and the new one's
+    ring slot out."""
     d, b, G, R = w.head_dim, w.bits, w.group, w.residual
     if w.scheme == kvq.KVQ_SCHEME_INNERQ:
-        return w.units * (d * 2 * 2 + 2 * (d * b // 8 + (d // G) * 6) + d * 2 * 2)
+        return w.units * (2 * d * 2 + 2 * (d * b // 8 + (d // G) * 6) + 2 * d * 2 + 2 * d * 2)
     mb = 4 if w.meta else 6
-    return w.units * (R * d * 2 * 2 + R * d * b // 8 * 2 + (R // G) * d * mb + R * (d // G) * mb + d * 2 * 2)
+    keys = R * d * 2 + R * d * b // 8 + (R // G) * d * mb
+    if w.v_policy == kvq.KVQ_V_CHUNK:
+        return w.units * (keys + R * d * 2 + R * d * b // 8 + R * (d // G) * mb)
+    return w.units * (keys + d * 2 + d * b // 8 + (d // G) * mb + d * 2 + d * 2)
 
 
 def time_prefill_and_flush(w, dev, stream, reps=5):
@@ -273,6 +386,67 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
                       "per_appended_token_us": round(fl_us / (1 if w.scheme else w.residual), 3)}}
 
 
+def source_digest():
+    """Content digests of the sources behind the numbers: one sha256 over the
+    library, binding, bench and workload sources, and the git blob id (sha1 of
+    "blob <size>\\0" + content) of each kernel source, which matches
+    `git ls-tree` of the commit the tree came from."""
+    import hashlib
+    names = []
+    for sub in ("decode_attention_token_amd/csrc", "include"):
+        d = os.path.join(ROOT, sub)
+        names += [os.path.join(sub, f) for f in sorted(os.listdir(d)) if not f.startswith(".")]
+    names += ["decode_attention_token_amd/__init__.py", "bench.py", "workloads/__init__.py"]
+    h = hashlib.sha256()
+    blobs = {}
+    for n in names:
+        with open(os.path.join(ROOT, n), "rb") as f:
+            data = f.read()
+        h.update(n.encode() + b"\0" + data)
+        if n.startswith("decode_attention_token_amd/csrc"):
+            blobs[os.path.basename(n)] = hashlib.sha1(b"blob %d\0" % len(data) + data).hexdigest()
+    sha = None
+    try:
+        import subprocess
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        sha = None
+    return {"sha256": h.hexdigest()[:16], "git_head": sha, "kernel_blobs": blobs}
+
+
+def tiny_latency(dev, stream, steps=20):
+    """Per-step latency of the tiny workload (batch 1, one head, context 256):
+    decode steps timed one at a time with HIP events; launch-bound, so it is
+    reported as a latency, not against a roofline."""
+    from workloads import TINY
+    w = TINY
+    cap = ((w.context + steps + 2 + w.residual - 1) // w.residual) * w.residual
+    cfg = make_cfg(w, cap)
+    k, v = gen_prefill(w, 0, dev)
+    kn, vn = gen_new_tokens(w, 0, dev, steps=steps + 2)
+    q = gen_queries(w, 0, dev, steps=steps + 2)
+    c = kvq.KVCache(cfg, dev)
+    c.prefill(k, v, stream.cuda_stream)
+    ws = c.workspace(cap)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    sp = stream.cuda_stream
+    scale = 1.0 / math.sqrt(w.head_dim)
+    times = []
+    for i in range(steps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        c.step(kn[i], vn[i], q[i], scale, out, ws, 0, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return {"workload": w.name, "us_per_step_median": round(times[len(times) // 2], 2),
+            "us_per_step_min": round(times[0], 2), "steps": steps,
+            "note": "one kvq_decode_step per step (append + attention), HIP events around each step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,12 +458,16 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
-    ap.add_argument("--no-side", action="store_true", help="skip the prefill and flush timings")
+    ap.add_argument("--no-side", action="store_true", help="skip the prefill, flush and tiny-workload timings")
     ap.add_argument("--v-policy", choices=("chunk", "fifo"), default=None,
                     help="override the workload's value-residual policy (KIVI scheme)")
     ap.add_argument("--sinks", type=int, default=None, help="override the workload's fp16 sink tokens")
     ap.add_argument("--meta", choices=("f32", "f16"), default=None,
                     help="group metadata: fp32 scale + int16 zero, or a packed fp16 scale | zero word (KIVI)")
+    ap.add_argument("--schedule", choices=("fixed", "queue"), default="fixed",
+                    help="matrix-core kernel work order: fixed (bit-identical reruns) or the work queue")
+    ap.add_argument("--kernel", choices=("auto", "valu"), default="auto",
+                    help="four query heads per kv head: matrix cores (auto) or the vector-ALU kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -307,6 +485,8 @@ def main():
         w = w.scaled(sinks=args.sinks)
     if args.meta is not None:
         w = w.scaled(meta=0 if args.meta == "f32" else 1, name=w.name + ("-meta16" if args.meta == "f16" else ""))
+    schedule = kvq.KVQ_SCHED_QUEUE if args.schedule == "queue" else kvq.KVQ_SCHED_FIXED
+    kernel = kvq.KVQ_KERNEL_VALU if args.kernel == "valu" else kvq.KVQ_KERNEL_AUTO
     steps = w.steps if args.steps is None else args.steps
     layers = w.layers if args.layers is None else args.layers
     dev = torch.device("cuda:0")
@@ -317,7 +497,7 @@ def main():
     if not args.no_cpu:
         sample = host_sample(w, sample_units(w), dev)
     print(f"# workload {w.name}: prefill {layers} layer caches", file=sys.stderr, flush=True)
-    cfg, caches = build_caches(w, layers, max_tokens, dev)
+    cfg, caches = build_caches(w, layers, max_tokens, dev, schedule, kernel)
     total = args.warmup + steps
     news = [gen_new_tokens(w, layer, dev, steps=total) for layer in range(layers)]
     qs = [gen_queries(w, layer, dev, steps=total) for layer in range(layers)]
@@ -343,12 +523,27 @@ def main():
         step(i, False)
     torch.cuda.synchronize()
     print("# timed loop", file=sys.stderr, flush=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    flushed, step_bytes = [], []
     t0 = time.perf_counter()
     nbytes = 0
-    for i in range(args.warmup, total):
-        nbytes += step(i, True)
+    for k, i in enumerate(range(args.warmup, total)):
+        evs[k].record(stream)
+        f0 = caches[0].flushes
+        nb = step(i, True)
+        nbytes += nb
+        step_bytes.append(nb)
+        flushed.append(caches[0].flushes != f0)
+    evs[steps].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_us = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)]
+    plain = [k for k in range(steps) if not flushed[k]]
+    # the timed loop's launches: one fused append + attention launch per layer
+    # and step when no flush is due; its bytes add the new token's ring store
+    fused_us = sum(step_us[k] for k in plain) / (len(plain) * layers) if plain else None
+    fused_bytes = (sum(step_bytes[k] for k in plain) / (len(plain) * layers) + w.units * w.head_dim * 2 * 2
+                   if plain else None)
 
     # attention-only passes, timed with HIP events on the library's stream
     print("# kernel timing", file=sys.stderr, flush=True)
@@ -368,9 +563,10 @@ def main():
     torch.cuda.synchronize()
     call_us = ev0.elapsed_time(ev1) * 1e3 / calls
     call_bytes = cb / calls
-    achieved = call_bytes / (call_us * 1e-6) / 1e9
+    att_gbs = call_bytes / (call_us * 1e-6) / 1e9
 
     side = time_prefill_and_flush(w, dev, stream) if not args.no_side else None
+    tiny = tiny_latency(dev, stream) if not args.no_side else None
     ceiling = stream_ceiling(dev, stream)
 
     if args.copy_probe:
@@ -382,6 +578,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # a decode step is one launch for the KIVI scheme with chunked values
+    # (no flush due); otherwise it is an append launch plus the attention
+    # launch, and the roofline takes the attention launch alone
+    one_launch = w.scheme == kvq.KVQ_SCHEME_KIVI and w.v_policy == kvq.KVQ_V_CHUNK
+    if fused_us is not None and one_launch:
+        roof_us, roof_bytes, roof_launch = fused_us, fused_bytes, "fused decode step (kvq_decode_step)"
+    else:
+        roof_us, roof_bytes, roof_launch = call_us, call_bytes, "attention only (kvq_decode_attention)"
+    achieved = roof_bytes / (roof_us * 1e-6) / 1e9
     splits_used = args.splits or kvq.kvq_auto_splits(cfg, caches[0].n_tokens)
     res = {
         "metric": METRIC,
@@ -403,11 +608,18 @@ def main():
                    "bits": w.bits, "group": w.group, "residual": w.residual, "layers": layers,
                    "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo",
                    "scheme": "innerq" if w.scheme == kvq.KVQ_SCHEME_INNERQ else "kivi", "sinks": w.sinks,
-                   "meta": "f16-packed" if w.meta else "f32+i16"},
+                   "meta": "f16-packed" if w.meta else "f32+i16", "schedule": args.schedule,
+                   "kernel": KERNELS[kernel_key(w, kernel)][0]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
-                     "kernel": KERNELS[kernel_key(w)][0], "avg_call_us": round(call_us, 2),
-                     "bytes_per_call": int(call_bytes)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, kernel),
+                     "kernel": KERNELS[kernel_key(w, kernel)][0], "launch": roof_launch,
+                     "avg_launch_us": round(roof_us, 2), "bytes_per_launch": int(roof_bytes),
+                     "launches": (len(plain) * layers) if roof_us is fused_us else calls},
+        "attention_only": {"avg_call_us": round(call_us, 2), "bytes_per_call": int(call_bytes),
+                           "GB/s": round(att_gbs, 1), "frac": round(att_gbs / HBM_PEAK_GBS, 4), "calls": calls},
+        "loop_steps_with_flush": int(sum(flushed)),
+        "loop_step_us": {"median": round(sorted(step_us)[len(step_us) // 2], 1), "min": round(min(step_us), 1),
+                         "max": round(max(step_us), 1), "launches_per_step": layers if one_launch else None},
         # what an fp16 cache of the same tokens would move per call, over the
         # same call time: a compression view, not a roofline fraction
         "fp16_equivalent": {"GB/s": round(fb / calls / (call_us * 1e-6) / 1e9, 1),
@@ -416,9 +628,11 @@ def main():
         # the achievable read rate, for context beside the 8 TB/s peak
         "stream_ceiling": {"GB/s": round(ceiling, 1), "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4),
                            "roofline_frac_of_ceiling": round(achieved / ceiling, 4)},
+        "source": source_digest(),
     }
     if side is not None:
         res.update(side)
+        res["tiny"] = tiny
     if not args.no_cpu:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         del caches, news, qs

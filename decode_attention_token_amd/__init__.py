@@ -21,6 +21,8 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_STATE, KVQ_ERR_DEVICE, KVQ_ERR_UN
 KVQ_V_CHUNK, KVQ_V_FIFO = 0, 1
 KVQ_SCHEME_KIVI, KVQ_SCHEME_INNERQ = 0, 1
 KVQ_META_F32, KVQ_META_F16 = 0, 1
+KVQ_SCHED_FIXED, KVQ_SCHED_QUEUE = 0, 1
+KVQ_KERNEL_AUTO, KVQ_KERNEL_VALU = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
@@ -32,7 +34,7 @@ EXPORTED = [
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bits", "group", "residual", "batch", "num_q_heads", "num_kv_heads", "head_dim",
-        "max_tokens", "v_policy", "scheme", "sink_tokens", "meta_format")]
+        "max_tokens", "v_policy", "scheme", "sink_tokens", "meta_format", "schedule", "kernel")]
 
 
 class kvq_layout(ctypes.Structure):
@@ -104,9 +106,10 @@ def _check(status: int):
 
 
 def make_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0, meta_format=KVQ_META_F32) -> kvq_config:
+                v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0, meta_format=KVQ_META_F32,
+                schedule=KVQ_SCHED_FIXED, kernel=KVQ_KERNEL_AUTO) -> kvq_config:
     return kvq_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                      v_policy, scheme, sink_tokens, meta_format)
+                      v_policy, scheme, sink_tokens, meta_format, schedule, kernel)
 
 
 def make_innerq_config(bits, group, window, sink_tokens, batch, num_q_heads, num_kv_heads, head_dim,

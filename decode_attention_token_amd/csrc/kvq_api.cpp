@@ -11,6 +11,7 @@
 // InnerQ-style state machine is described at innerq_prefill below.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -56,11 +57,13 @@ kvq_status check_config(const kvq_config *c) {
   if (c->v_policy != KVQ_V_CHUNK && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "unknown v_policy");
   if (c->sink_tokens < 0) return fail(KVQ_ERR_ARG, "sink_tokens must be non-negative");
   if (c->meta_format != KVQ_META_F32 && c->meta_format != KVQ_META_F16) return fail(KVQ_ERR_ARG, "unknown meta_format");
+  if (c->schedule != KVQ_SCHED_FIXED && c->schedule != KVQ_SCHED_QUEUE) return fail(KVQ_ERR_ARG, "unknown schedule");
+  if (c->kernel != KVQ_KERNEL_AUTO && c->kernel != KVQ_KERNEL_VALU) return fail(KVQ_ERR_ARG, "unknown kernel");
   if (iq && c->meta_format != KVQ_META_F32)
     return fail(KVQ_ERR_UNSUPPORTED, "compressed metadata is implemented for the KIVI scheme only");
   if (iq && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "the InnerQ scheme keeps a FIFO window (v_policy 1)");
   if (c->sink_tokens > 512) return fail(KVQ_ERR_UNSUPPORTED, "more than 512 sink tokens is not implemented");
-  if (c->max_tokens > (1 << 25)) return fail(KVQ_ERR_UNSUPPORTED, "max_tokens above 2^25 is not implemented");
+  if (c->max_tokens > kvq::kMaxTokens) return fail(KVQ_ERR_UNSUPPORTED, "max_tokens above 2^25 is not implemented");
   if (c->head_dim != kvq::kHeadDim) return fail(KVQ_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
   if (c->group != 32 && c->group != 64 && c->group != 128)
     return fail(KVQ_ERR_UNSUPPORTED, "only group 32, 64 or 128 is implemented");
@@ -133,17 +136,25 @@ size_t workspace_for(const kvq_config *c, int32_t splits) {
          (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
 }
 
-// KVQ_DETERMINISTIC=1 (any value but "0") in the environment: the
-// matrix-core kernel hands super-chunks to waves in a fixed order, so reruns
-// are bit-identical; by default waves take them from a work queue, which
-// only changes the order of fp32 partial sums from run to run.
-bool deterministic_schedule() {
-  const char *v = getenv("KVQ_DETERMINISTIC");
-  return v != nullptr && strcmp(v, "0") != 0;
+// cfg->schedule: KVQ_SCHED_FIXED (default) makes the matrix-core kernel
+// hand super-chunks to waves in a fixed order, so reruns are bit-identical;
+// KVQ_SCHED_QUEUE lets waves take them from a work queue, which only changes
+// the order of fp32 partial sums from run to run.
+// Epoch of a launch: tags the per-unit election words, so a word an earlier
+// launch left behind never counts toward this one (zero is never used).
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (e == 0);
+  return e;
 }
 
 void set_workspace(kvq::AttnArgs &a, const kvq_config *c, void *workspace) {
-  a.dynamic = deterministic_schedule() ? 0 : 1;
+  a.epoch = next_epoch();
+  a.dynamic = c->schedule == KVQ_SCHED_QUEUE ? 1 : 0;
+  a.mfma = c->kernel == KVQ_KERNEL_AUTO ? 1 : 0;
   a.ctr = static_cast<uint32_t *>(workspace);
   a.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                          kvq::counter_bytes((int64_t)c->batch * c->num_kv_heads));

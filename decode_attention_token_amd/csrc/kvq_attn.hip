@@ -35,9 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "kvq_internal.h"
 #include "kvq_attn_common.h"
 
@@ -524,13 +521,6 @@ hipError_t launch_valu(const AttnArgs &a, hipStream_t s) {
   return (a.c.bits == 2) ? launch_by_group<2, 0>(a, s) : launch_by_group<4, 0>(a, s);
 }
 
-// The matrix-core kernel takes the quantized groups of four-heads-per-kv-head
-// layouts unless KVQ_GQA_PATH=valu is set in the environment.
-bool gqa_mfma_enabled() {
-  const char *v = getenv("KVQ_GQA_PATH");
-  return v == nullptr || strcmp(v, "valu") != 0;
-}
-
 }  // namespace
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
@@ -539,7 +529,7 @@ hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
   // takes a share of the sinks and tokens [n_main, n)
   const int64_t rest_tokens = a.nsink + (a.n - a.n_main);
   if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && a.splits >= 1 && rest_tokens <= kGqaMaxRest &&
-      gqa_mfma_enabled()) {
+      a.mfma) {
     AttnArgs m = a;
     m.tail_wg = 0;
     m.resid_main = 0;

@@ -259,34 +259,43 @@ struct CoherentLoad {
   }
 };
 
-// Work queue of one unit: its workgroups' waves take chunks of its tokens
-// from a ticket counter (ctr[0]); ctr[1] counts finished workgroups (bits
-// 24..31) and the chunks they took (bits 0..23).
+// Per-unit counters in the workspace (kCtrWords u32 per unit):
+//   word 0     ticket: waves of the work-queue schedule take chunks of the
+//              unit's tokens from it (queue_grab);
+//   words 2-3  one 64-bit election word: the call's epoch in the high half
+//              and, in the low half, the workgroups that finished (bits
+//              24..31) and the chunks they took (bits 0..23).
 __device__ __forceinline__ uint32_t queue_grab(uint32_t *ctr, int lane) {
   uint32_t v = 0;
   if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;   // in lane 0; read it (readlane) a chunk later
 }
 
-// End of a part whose waves took their chunks from the unit's queue.
+// End of a part of a unit split over a.splits workgroups.
 // s_flag: LDS, [NW] chunks taken per wave, then one word for the result.
 // With several parts, the part's (acc, m, l) record goes out with
 // agent-scope atomic stores (the records cross XCDs, whose L2 caches are not
 // kept coherent for ordinary stores) and every wave waits for its own stores
-// before the workgroup is counted in.  The unit's last workgroup checks the
-// chunk count (a count short of nchunks means the counters did not start at
-// zero: its outputs are NaN instead of a wrong result), returns both
-// counters to zero for the next call and merges every record of the unit;
-// a single part writes the normalized output itself.  "Last" is the
-// workgroup count modulo the split count, so a count field that did not
-// start at zero still elects one workgroup, and its chunk count (which
-// cannot match then) makes the output NaN rather than leaving it unwritten.
+// before the workgroup is counted in.  Counting is a compare-and-swap on the
+// unit's election word: a word whose epoch is not this call's (a.epoch, new
+// for every launch) counts as empty, so a word left over from an earlier
+// call, interrupted or never zero-filled, cannot bring the count forward.
+// Exactly one workgroup, the one whose swap completes the count, is the
+// unit's last: it checks the chunk total (a total short of nchunks means the
+// ticket did not start at zero, and its outputs are NaN instead of a wrong
+// result), returns the ticket and the word to zero for the next call and
+// merges every record of the unit; a single part writes the normalized
+// output itself.  Ordering: each record store and the swap are agent-scope
+// atomics, the stores are complete (s_waitcnt 0) before the barrier that
+// precedes the swap, and the last workgroup reads the records only after
+// its swap has returned, with agent-scope loads that go to the coherent
+// level.
 template <int HPG, int NW>
 __device__ void queue_finish(const AttnArgs &a, int unit, int split, const Stage &st, uint32_t *s_flag,
                              uint32_t nchunks) {
   const int tid = threadIdx.x, nthreads = blockDim.x;
   const int b = unit / a.hkv, hk = unit % a.hkv;
-  uint32_t *ctr = a.ctr + 2 * unit;
+  uint32_t *ctr = a.ctr + kCtrWords * unit;
   if (a.nparts > 1) {
     for (int i = tid; i < HPG * (kHeadDim + 2); i += nthreads) {
       const int h = i / (kHeadDim + 2), c = i % (kHeadDim + 2);
@@ -302,12 +311,23 @@ __device__ void queue_finish(const AttnArgs &a, int unit, int split, const Stage
     uint32_t took = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) took += s_flag[w];
-    const uint32_t old = __hip_atomic_fetch_add(ctr + 1, (1u << 24) | took, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t *word = reinterpret_cast<uint64_t *>(ctr + 2);
+    const uint64_t tag = (uint64_t)a.epoch << 32;
+    // first guess: the word is clean (every call leaves it at zero)
+    uint64_t seen = 0, base;
+    for (;;) {
+      base = (seen >> 32) == a.epoch ? (seen & 0xffffffffull) : 0ull;
+      uint64_t expect = seen;
+      if (__hip_atomic_compare_exchange_strong(word, &expect, tag | (base + ((1u << 24) | took)), __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        break;
+      seen = expect;
+    }
     uint32_t last = 0;
-    if ((old >> 24) % (uint32_t)a.splits == (uint32_t)(a.splits - 1)) {
-      last = ((old & 0xffffffu) + took == nchunks) ? 1u : 2u;
+    if ((uint32_t)(base >> 24) + 1u == (uint32_t)a.splits) {
+      last = ((uint32_t)(base & 0xffffffu) + took == nchunks) ? 1u : 2u;
       __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     s_flag[NW] = last;
   }

@@ -42,10 +42,16 @@
 // arrive with the step's loads (coalesced) and are staged through a per-wave
 // LDS area into the lanes that need them.  The online softmax (log2 units,
 // wave-uniform per-head maximum raised only past a margin) follows the
-// vector-ALU kernel.  Work split: as the vector-ALU kernel, whole key groups
-// of one unit per workgroup, contiguous group ranges per wave; the fp16 tokens
-// (sinks, residual) and the mixed FIFO tail go to the vector-ALU kernel as
-// extra parts of the same unit, merged by the merge kernel.
+// vector-ALU kernel.  Work split: a unit's key groups form super-chunks of
+// four; a unit has `splits` workgroups of four waves, rotated across the
+// XCDs, and each wave takes super-chunks in a fixed strided order or, with
+// the work-queue schedule, its first two by index and the rest from a
+// per-unit ticket counter.  After its quantized groups every workgroup takes
+// its share of the unit's fp16 tokens (sinks, the residual ring, the token of
+// a fused step, the FIFO tail whose values are still fp16) with a plain
+// dequantize-then-dot routine (gqa_fp16_part).  The unit's last workgroup, by
+// a finished-workgroup counter, merges the split records inside the same
+// launch (queue_finish).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -71,10 +77,16 @@ constexpr int kHpg = 4;   // query heads per kv head on this path
 // partial key group (< 128).
 constexpr int kMaxRest = kGqaMaxRest;
 
-// Lane byte offset past every buffer this kernel reads (resources cover at
-// most 2^31 bytes; loads that use it add at most a few KiB of uniform offset): such a load
-// returns zero and touches no memory.
-constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;
+// Lane byte offset past every buffer this kernel reads, so a load that uses
+// it returns zero and touches no memory.  The largest resource is a unit's
+// 4-bit code buffer at the largest capacity, 2^25 tokens * 64 bytes = 2^31
+// bytes; the loads that take this offset add at most 32 rows of 64 bytes of
+// uniform offset (plus a 16-byte step), and the sum stays below 2^32, so the
+// offset neither lands inside a resource nor wraps around.
+constexpr uint32_t kOutOfRange = 0xFFFFF000u;
+static_assert((uint64_t)kMaxTokens * (kHeadDim * 4 / 8) <= 0x80000000ull, "largest code resource");
+static_assert((uint64_t)kOutOfRange >= 0x80000000ull + 4096, "sentinel above every resource");
+static_assert((uint64_t)kOutOfRange + 32 * 64 + 16 < 0x100000000ull, "sentinel plus step offset fits 32 bits");
 // Four waves per workgroup, two waves per SIMD (up to 256 VGPRs: the
 // accumulators, both q' limb sets and a three-step load ring stay in
 // registers; at three waves per SIMD the kernel spills and runs slower).
@@ -461,7 +473,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   const int nsc = (ngroups + 3) / 4;
   const int nw = a.splits * kGqaWaves;
   const int slot = split * kGqaWaves + wave;
-  uint32_t *const ticket = a.ctr + 2 * unit;
+  uint32_t *const ticket = a.ctr + kCtrWords * unit;
   auto grab = [&]() { return queue_grab(ticket, lane); };   // read at the next super-chunk
   auto live_steps = [&](uint32_t id) { return (ngroups - 4 * (int)id < 4 ? ngroups - 4 * (int)id : 4) * SPG; };
   // ids compare unsigned, so any value past the end (however large) ends the wave

@@ -9,10 +9,15 @@ namespace kvq {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxSplits = 64;
+// Largest accepted max_tokens.  With 4-bit codes a unit's code buffer is then
+// 2^25 * 64 = 2^31 bytes, the largest buffer resource a kernel builds.
+constexpr int kMaxTokens = 1 << 25;
 constexpr int kPartialStride = kHeadDim + 4;   // acc[128], m, l, pad, pad (floats)
-// Workspace: per-unit work-queue counters (two u32 each), padded to 256
-// bytes, then the partial records.
-inline size_t counter_bytes(int64_t units) { return (size_t)((units * 8 + 255) / 256 * 256); }
+// Workspace: per-unit counters (kCtrWords u32 each: the work-queue ticket,
+// a pad word and a 64-bit election word), padded to 256 bytes, then the
+// partial records.
+constexpr int kCtrWords = 4;
+inline size_t counter_bytes(int64_t units) { return (size_t)((units * kCtrWords * 4 + 255) / 256 * 256); }
 
 struct CacheView {
   uint32_t *k_codes;
@@ -82,8 +87,10 @@ struct AttnArgs {
   const uint16_t *q;     // [B][Hq][128]
   float *out;            // [B][Hq][128]
   float *partials;       // [B][Hq][nparts][kPartialStride]
-  uint32_t *ctr;         // [B*Hkv][2] work-queue counters (zero between calls)
+  uint32_t *ctr;         // [B*Hkv][kCtrWords] work-queue counters (zero between calls)
+  uint32_t epoch;        // non-zero, different for consecutive launches: tags the election words
   int dynamic;           // 1: waves take super-chunks from the work queue; 0: fixed strided order
+  int mfma;              // 1: four query heads per kv head run on the matrix-core kernel
   int batch, hq, hkv;
   int64_t n, nq_k, nq_v;
   int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups

@@ -26,7 +26,8 @@
  *   - fp16 tensors are passed as uint16_t bit patterns; every pointer named
  *     "device" is HIP device memory owned by the caller.  The library never
  *     allocates or frees device memory and keeps no global state other than a
- *     thread-local error string.
+ *     thread-local error string and a process-wide launch counter (its value
+ *     tags the per-call counters in an attention workspace).
  *   - Every call is stream-ordered on the given hipStream_t and never
  *     synchronizes the device.  The host-side counters in kvq_cache are
  *     updated at enqueue time, so calls on one cache must be serialized by
@@ -118,8 +119,26 @@ typedef enum { KVQ_SCHEME_KIVI = 0, KVQ_SCHEME_INNERQ = 1 } kvq_scheme;
  *   levels.  KIVI scheme only. */
 typedef enum { KVQ_META_F32 = 0, KVQ_META_F16 = 1 } kvq_meta_format;
 
+/* Order in which the matrix-core kernel (four query heads per kv head) hands
+ * its super-chunks (four key groups) to waves.
+ * KVQ_SCHED_FIXED (default): a fixed strided order, so reruns on the same
+ *   inputs are bit-identical.
+ * KVQ_SCHED_QUEUE: each wave takes its next super-chunk from a per-unit
+ *   ticket counter in the workspace, which balances waves that run at
+ *   different speeds; the order, and so the rounding of the fp32 partial
+ *   sums, varies from run to run (results agree to about 1e-6, within 1e-4).
+ * The other kernels use a fixed order under both values. */
+typedef enum { KVQ_SCHED_FIXED = 0, KVQ_SCHED_QUEUE = 1 } kvq_schedule;
+
+/* Attention kernel family for four query heads per kv head (KIVI scheme).
+ * KVQ_KERNEL_AUTO (default): the matrix-core kernel (bf16 MFMA tiles over
+ *   the quantized groups).  KVQ_KERNEL_VALU: the vector-ALU kernel every
+ *   other head ratio uses (kept for comparison).  Ignored elsewhere. */
+typedef enum { KVQ_KERNEL_AUTO = 0, KVQ_KERNEL_VALU = 1 } kvq_kernel;
+
 /* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
- * plus the attention shape and the scheme.  Constraints: bits in {2,4};
+ * plus the attention shape, the scheme and two launch choices (schedule,
+ * kernel; zero selects the defaults).  Constraints: bits in {2,4};
  * head_dim % group == 0; group * bits % 32 == 0; num_q_heads % num_kv_heads
  * == 0; residual > 0; max_tokens > 0; sink_tokens >= 0.  KVQ_SCHEME_KIVI
  * also needs residual % group == 0 ([KIVI] how it works) and max_tokens %
@@ -138,6 +157,8 @@ typedef struct {
   int32_t scheme;       /* kvq_scheme */
   int32_t sink_tokens;  /* leading tokens kept fp16 (both schemes; 0 = none) */
   int32_t meta_format;  /* kvq_meta_format */
+  int32_t schedule;     /* kvq_schedule (0 = fixed order, bit-identical reruns) */
+  int32_t kernel;       /* kvq_kernel (0 = matrix cores for four query heads per kv head) */
 } kvq_config;
 
 /* Byte sizes of the caller-allocated device buffers of one cache (k_sink and
@@ -183,10 +204,10 @@ int32_t kvq_auto_splits(const kvq_config *cfg, int64_t n_tokens);
 
 /* Workspace bytes kvq_decode_attention needs for `splits` splits (0 = the
  * automatic count for n_tokens; more tokens never need fewer splits, so the
- * size for max_tokens covers every call): two u32 work-queue counters per
- * (batch, kv head), padded to 256 bytes, then fp32 partial (acc[head_dim],
- * max, sum) records for every query head and part.  Host only; 0 on an
- * invalid cfg. */
+ * size for max_tokens covers every call): four u32 counter words per (batch,
+ * kv head) (a work-queue ticket and a 64-bit election word tagged with the
+ * launch), padded to 256 bytes, then fp32 partial (acc[head_dim], max, sum)
+ * records for every query head and part.  Host only; 0 on an invalid cfg. */
 size_t kvq_workspace_bytes(const kvq_config *cfg, int64_t n_tokens, int32_t splits);
 
 /* Prefill ([KIVI] how it works): k, v are the prompt's keys and values, fp16
@@ -218,26 +239,38 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
                             hipStream_t stream);
 
 /* Decode attention of one query per head over the whole cache, including the
- * token appended in the same step: out = softmax(softmax_scale * q K^T) V
- * with K, V dequantized inside the kernels (fused dequantization into the
- * q.K^T and P.V products).  q fp16 device [batch][num_q_heads][head_dim];
- * out fp32 device [batch][num_q_heads][head_dim]; query head h uses key head
- * h / (num_q_heads / num_kv_heads).  workspace: device, at least
- * kvq_workspace_bytes(cfg, n_tokens, splits) bytes, zero-filled once before
- * its first use: its leading bytes hold per-(batch, kv head) work-queue
- * counters that every call leaves at zero again (the rest is scratch for
- * split records; a call whose counters did not start at zero returns NaN
- * outputs instead of a wrong result); calls that share a workspace must be
- * ordered on one stream.  splits: 0 =
- * automatic, else 1..64.  One kernel launch when every unit fits one part,
- * else a second (merge) launch, except for the matrix-core kernel (four query
- * heads per kv head) and the InnerQ kernel, which merge inside their one
- * launch.  Needs started and n_tokens >= 1.
- * Environment (read at each call): KVQ_GQA_PATH=valu runs four query heads
- * per kv head on the vector-ALU kernel instead of the matrix-core one;
- * KVQ_DETERMINISTIC=1 makes the matrix-core kernel hand out its work in a
- * fixed order (bit-identical reruns) instead of from its per-unit work queue,
- * whose run-dependent order changes only the rounding of fp32 partial sums. */
+ * token appended in the same step.
+ * Defining passages: generating a token reads every cached key and value
+ * while the arithmetic units mostly wait, so this call streams the packed
+ * cache once ([KIVI] background); the group's shared scale is loaded once and
+ * dequantization is fused into the dot products of a GEMV ([InnerQ]
+ * methodology 3); the result is the textbook attention of the dequantized
+ * cache, which none of the pages prints:
+ *     out[b][h] = sum_t p_t V^[t],  p = softmax(softmax_scale * q[b][h] . K^[t]),
+ * with K^, V^ = S * (code + Z) for quantized tokens ([HFQ] 2.1, inverted) and
+ * the stored fp16 values for sink, residual and window tokens; no mask.
+ * Arguments:
+ *   q        fp16 device [batch][num_q_heads][head_dim], read only; query head
+ *            h uses key head h / (num_q_heads / num_kv_heads).
+ *   softmax_scale  finite; 1/sqrt(head_dim) for the textbook scaling.
+ *   out      fp32 device [batch][num_q_heads][head_dim], written.
+ *   workspace  device, at least kvq_workspace_bytes(cfg, n_tokens, splits)
+ *            bytes, zero-filled once before its first use.  Its leading bytes
+ *            hold per-(batch, kv head) counters that every call leaves at
+ *            zero again; the rest is scratch for split records.  An election
+ *            word left non-zero by an earlier, interrupted call is ignored
+ *            (it carries another launch's tag); a work-queue ticket that did
+ *            not start at zero makes that call write NaN for the affected
+ *            units instead of a wrong number, and the call returns it to
+ *            zero.  Calls that share a workspace must be ordered on one
+ *            stream: overlapping calls race on it.
+ *   splits   0 = automatic (kvq_auto_splits), else 1..64 parts per unit.
+ * One kernel launch when every unit fits one part, else a second (merge)
+ * launch, except for the matrix-core kernel (four query heads per kv head)
+ * and the InnerQ kernel, which merge inside their one launch; cfg->schedule
+ * and cfg->kernel choose the matrix-core kernel's work order and whether it
+ * runs at all.  Needs started and n_tokens >= 1; KVQ_ERR_CAPACITY for a
+ * workspace below the size needed; never synchronizes. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                 const uint16_t *q, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, int32_t splits,

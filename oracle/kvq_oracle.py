@@ -74,7 +74,7 @@ import numpy as np
 
 __all__ = [
     "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
-    "attention", "kv_code_bytes_per_token", "attention_call_bytes", "flush_bytes",
+    "attention", "kv_code_bytes_per_token", "attention_call_bytes",
     "CHUNK", "FIFO", "META_F32", "META_F16", "round_up_to_fp16", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
     "InnerQCache", "innerq_attention_call_bytes", "KiviSinkCache",
 ]
@@ -697,11 +697,3 @@ def attention_call_bytes(batch, q_heads, kv_heads, head_dim, bits, group, n, nq_
                 + nq_v * d * b // 8 + nq_v * (d // G) * mb
                 + ((n - nq_k) + (n - nq_v)) * d * 2)
     return batch * kv_heads * per_unit + batch * q_heads * d * (2 + 4)
-
-
-def flush_bytes(batch, kv_heads, head_dim, bits, group, residual):
-    """Bytes of one residual flush: read R fp16 keys and values, write codes + metadata."""
-    d, b, G, R = head_dim, bits, group, residual
-    read = R * d * 2 * 2
-    write = 2 * R * d * b // 8 + (R // G) * d * 6 + R * (d // G) * 6
-    return batch * kv_heads * (read + write)

@@ -1,7 +1,6 @@
 """Shared helpers of the GPU parity tests: run the HIP path and the oracle on the
 same seeded fp16 bits and compare buffers (bit-exact) and outputs (2e-3)."""
 import contextlib
-import os
 
 import numpy as np
 import torch
@@ -21,18 +20,23 @@ SPLIT_TOL_MFMA = 1e-4
 
 
 @contextlib.contextmanager
-def deterministic_schedule():
-    """KVQ_DETERMINISTIC=1 for the calls inside: the matrix-core kernel then
-    hands super-chunks to waves in a fixed order instead of a work queue."""
-    old = os.environ.get("KVQ_DETERMINISTIC")
-    os.environ["KVQ_DETERMINISTIC"] = "1"
+def config_fields(cache, **fields):
+    """Sets launch-choice fields of the cache's own kvq_config (schedule,
+    kernel) for the calls inside, then restores them."""
+    old = {k: getattr(cache.cfg, k) for k in fields}
+    for k, v in fields.items():
+        setattr(cache.cfg, k, v)
     try:
         yield
     finally:
-        if old is None:
-            del os.environ["KVQ_DETERMINISTIC"]
-        else:
-            os.environ["KVQ_DETERMINISTIC"] = old
+        for k, v in old.items():
+            setattr(cache.cfg, k, v)
+
+
+def queue_schedule(cache):
+    """The matrix-core kernel's work-queue schedule for the calls inside
+    (the default is the fixed order with bit-identical reruns)."""
+    return config_fields(cache, schedule=kvq.KVQ_SCHED_QUEUE)
 
 
 def split_tol(heads_per_kv):

@@ -60,7 +60,7 @@ int main(void) {
   printf("kvq_config %zu\nkvq_layout %zu\nkvq_cache %zu\n", sizeof(kvq_config), sizeof(kvq_layout),
          sizeof(kvq_cache));
   F(kvq_config, scheme) F(kvq_config, sink_tokens) F(kvq_layout, k_sink) F(kvq_layout, v_sink)
-  F(kvq_config, meta_format)
+  F(kvq_config, meta_format) F(kvq_config, schedule) F(kvq_config, kernel)
   F(kvq_cache, k_sink) F(kvq_cache, v_sink) F(kvq_cache, n_tokens) F(kvq_cache, flushes)
   return 0;
 }
@@ -129,6 +129,23 @@ def test_invalid_metadata_formats_are_rejected(lib, bad, status):
     out = kvq.kvq_layout()
     assert lib.kvq_layout_bytes(ctypes.byref(bad), ctypes.byref(out)) == status
     assert "meta" in lib.kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("bad", [cfg(schedule=2), cfg(schedule=-1), cfg(kernel=2), cfg(kernel=-1)])
+def test_invalid_launch_choices_are_rejected(lib, bad):
+    out = kvq.kvq_layout()
+    assert lib.kvq_layout_bytes(ctypes.byref(bad), ctypes.byref(out)) == kvq.KVQ_ERR_ARG
+    err = lib.kvq_last_error().decode()
+    assert "schedule" in err or "kernel" in err
+
+
+def test_launch_choices_do_not_change_sizes(lib):
+    base = kvq.kvq_layout_bytes(cfg(num_q_heads=128))
+    for kw in (dict(schedule=kvq.KVQ_SCHED_QUEUE), dict(kernel=kvq.KVQ_KERNEL_VALU)):
+        lay = kvq.kvq_layout_bytes(cfg(num_q_heads=128, **kw))
+        assert all(getattr(lay, f) == getattr(base, f) for f, _ in kvq.kvq_layout._fields_), kw
+        assert kvq.kvq_workspace_bytes(cfg(num_q_heads=128, **kw), 4224) == \
+            kvq.kvq_workspace_bytes(cfg(num_q_heads=128), 4224)
 
 
 def test_packed_metadata_needs_no_zero_buffers(lib):
@@ -286,9 +303,10 @@ def test_workspace_and_split_sizing(lib):
     c = cfg()
     s = kvq.kvq_auto_splits(c, 4097)
     assert 1 <= s <= 64
-    # per-unit work-queue counters (two u32 per (batch, kv head), padded to
-    # 256 bytes), then (splits + 1) records of 132 floats per query head
-    ctr = 16 * 32 * 8
+    # per-unit counters (four u32 per (batch, kv head): ticket, pad and a
+    # 64-bit election word; padded to 256 bytes), then (splits + 1) records of
+    # 132 floats per query head
+    ctr = 16 * 32 * 16
     assert kvq.kvq_workspace_bytes(c, 4097, 0) == ctr + 16 * 32 * (s + 1) * 132 * 4
     assert kvq.kvq_workspace_bytes(c, 4097, 3) == ctr + 16 * 32 * 4 * 132 * 4
     assert kvq.kvq_workspace_bytes(c, 4097, 65) == 0

@@ -1,10 +1,9 @@
 """GPU parity of the matrix-core kernel for four query heads per kv head
 (KIVI layout): bf16 MFMA tiles with two-limb operands against the float64
 oracle, across bit widths, group sizes, value policies, sink tokens,
-metadata formats and split counts; and against the vector-ALU kernel
-(KVQ_GQA_PATH=valu) on the same cache."""
+metadata formats, split counts and both work schedules; and against the
+vector-ALU kernel (config kernel = KVQ_KERNEL_VALU) on the same cache."""
 import math
-import os
 
 import numpy as np
 import pytest
@@ -13,8 +12,8 @@ import torch
 import decode_attention_token_amd as kvq
 import oracle
 from workloads import Workload, gen_new_tokens, gen_prefill, gen_queries
-from gpu_helpers import (ATOL, SPLIT_TOL_MFMA, compare_sink_unit, deterministic_schedule, host, max_err,
-                         oracle_attention)
+from gpu_helpers import (ATOL, SPLIT_TOL_MFMA, compare_sink_unit, config_fields, host, max_err, oracle_attention,
+                         queue_schedule)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,16 +54,10 @@ def _cache(w):
 
 
 def _attention(cache, q, path, **kw):
-    old = os.environ.get("KVQ_GQA_PATH")
-    os.environ["KVQ_GQA_PATH"] = path
-    try:
+    kernel = kvq.KVQ_KERNEL_VALU if path == "valu" else kvq.KVQ_KERNEL_AUTO
+    with config_fields(cache, kernel=kernel):
         out = cache.attention(q, **kw)
         torch.cuda.synchronize()
-    finally:
-        if old is None:
-            del os.environ["KVQ_GQA_PATH"]
-        else:
-            os.environ["KVQ_GQA_PATH"] = old
     return out
 
 
@@ -119,18 +112,20 @@ def test_gqa_mfma_split_counts_and_reruns(bits, G):
         outs.append(host(o))
     for o in outs[1:]:
         assert float(np.abs(o - outs[0]).max()) <= SPLIT_TOL_MFMA
-    # One split (four waves over 31 super-chunks) runs mostly from the work
-    # queue, whose hand-out order varies between runs: reruns agree to fp32
-    # reordering.  The fixed strided schedule gives bit-identical reruns.
+    # The default fixed schedule gives bit-identical reruns.  With one split
+    # (four waves over 31 super-chunks) the work-queue schedule runs mostly
+    # from the queue, whose hand-out order varies between runs: its results
+    # agree with the fixed order to fp32 reordering.
     for s in (1, 0):
-        with deterministic_schedule():
-            a = host(_attention(cache, q, "mfma", splits=s))
-            b = host(_attention(cache, q, "mfma", splits=s))
+        a = host(_attention(cache, q, "mfma", splits=s))
+        b = host(_attention(cache, q, "mfma", splits=s))
         assert np.array_equal(a, b), f"splits {s}: reruns must be bit-identical"
         assert float(np.abs(a.astype(np.float64) - want).max()) <= ATOL
-        for _ in range(3):
-            dyn = host(_attention(cache, q, "mfma", splits=s))
-            assert float(np.abs(dyn - a).max()) <= SPLIT_TOL_MFMA
+        with queue_schedule(cache):
+            for _ in range(3):
+                dyn = host(_attention(cache, q, "mfma", splits=s))
+                assert float(np.abs(dyn - a).max()) <= SPLIT_TOL_MFMA
+                assert float(np.abs(dyn.astype(np.float64) - want).max()) <= ATOL
 
 
 def test_gqa_mfma_fused_step_matches_append_then_attention():
@@ -172,10 +167,13 @@ def test_gqa_mfma_large_magnitudes():
 
 
 def test_gqa_mfma_work_queue_counters():
-    """The work-queue counters at the start of the workspace are zero after
-    every call.  A counter that did not start at zero makes that unit's
-    output NaN (some super-chunks would be skipped) instead of a wrong
-    number, the call still returns them to zero, and the next call is right."""
+    """The per-unit counters at the start of the workspace (ticket, pad, and a
+    64-bit election word tagged with the launch) are zero after every call.
+    A ticket that did not start at zero makes that unit's output NaN under the
+    work-queue schedule (some super-chunks would be skipped) instead of a
+    wrong number; the call returns it to zero and the next call is right.  An
+    election word left over from another launch is ignored: the call is
+    right, with one split or several, and the word is zero afterwards."""
     w = _w(450, 2, 4000, 2, 32, 128, 1)
     k, v = gen_prefill(w, 0, "cuda")
     kn, vn = gen_new_tokens(w, 0, "cuda")
@@ -187,33 +185,30 @@ def test_gqa_mfma_work_queue_counters():
     ref.append(host(kn[0]), host(vn[0]))
     want = oracle_attention(ref, host(q), 1 / math.sqrt(128))
     units = w.batch * w.num_kv_heads
-    ws = cache.workspace(splits=1)
-    ctr = ws.view(torch.int32)[: 2 * units]
-    out = _attention(cache, q, "mfma", workspace=ws, splits=1)
-    torch.cuda.synchronize()
-    assert max_err(out, want) <= ATOL
-    assert int(ctr.abs().sum()) == 0, host(ctr)
     u = units - 1                         # unit (batch 1, kv head 1): query heads 4..7 of batch 1
-    ctr[2 * u] = 5                        # a ticket that did not start at zero
-    out = host(_attention(cache, q, "mfma", workspace=ws, splits=1))
     b, h = divmod(u, w.num_kv_heads)
-    bad = out[b, 4 * h:4 * h + 4]
-    assert np.isnan(bad).all(), "a miscounted unit must come out NaN"
-    keep = np.ones(out.shape[:2], bool)
+    keep = np.ones(want.shape[:2], bool)
     keep[b, 4 * h:4 * h + 4] = False
-    assert float(np.abs(out[keep].astype(np.float64) - want[keep]).max()) <= ATOL
-    assert int(ctr.abs().sum()) == 0, host(ctr)
-    assert max_err(_attention(cache, q, "mfma", workspace=ws, splits=1), want) <= ATOL
-
-    # two splits, finished-workgroup count not starting at zero: the unit's
-    # output must come out NaN, not stale (nothing would be written if no
-    # workgroup saw itself as the last one)
-    ws2 = cache.workspace(splits=2)
-    ctr2 = ws2.view(torch.int32)[: 2 * units]
-    out2 = torch.zeros_like(torch.from_numpy(want).float()).cuda()
-    ctr2[2 * u + 1] = 1 << 24
-    _attention(cache, q, "mfma", workspace=ws2, splits=2, out=out2)
-    torch.cuda.synchronize()
-    got = host(out2)
-    assert np.isnan(got[b, 4 * h:4 * h + 4]).all(), "a miscounted unit must come out NaN"
-    assert float(np.abs(got[keep].astype(np.float64) - want[keep]).max()) <= ATOL
+    for schedule in (kvq.KVQ_SCHED_FIXED, kvq.KVQ_SCHED_QUEUE):
+        with config_fields(cache, schedule=schedule):
+            for splits in (1, 2, 5):
+                print(f"  schedule {schedule} splits {splits}", flush=True)
+                ws = cache.workspace(splits=splits)
+                ctr = ws.view(torch.int32)[: 4 * units]
+                out = _attention(cache, q, "mfma", workspace=ws, splits=splits)
+                assert max_err(out, want) <= ATOL
+                assert int(ctr.abs().sum()) == 0, host(ctr)
+                # a stale election word: another launch's tag, some workgroups counted
+                # (epochs 0 and near 2^32 are never those of a launch in this process)
+                for stale in ((0xFFFFFFF0 << 32) | (1 << 24) | 7, (1 << 24), (0xFFFFFFFF << 32) | (3 << 24)):
+                    ctr.view(torch.int64)[2 * u + 1] = int(np.array(stale, np.uint64).view(np.int64))
+                    out = _attention(cache, q, "mfma", workspace=ws, splits=splits)
+                    assert max_err(out, want) <= ATOL, (schedule, splits, stale)
+                    assert int(ctr.abs().sum()) == 0, host(ctr)
+                if schedule == kvq.KVQ_SCHED_QUEUE:
+                    ctr[4 * u] = 5                # a ticket that did not start at zero
+                    got = host(_attention(cache, q, "mfma", workspace=ws, splits=splits))
+                    assert np.isnan(got[b, 4 * h:4 * h + 4]).all(), "a miscounted unit must come out NaN"
+                    assert float(np.abs(got[keep].astype(np.float64) - want[keep]).max()) <= ATOL
+                    assert int(ctr.abs().sum()) == 0, host(ctr)
+                    assert max_err(_attention(cache, q, "mfma", workspace=ws, splits=splits), want) <= ATOL

@@ -10,8 +10,8 @@ import torch
 import decode_attention_token_amd as kvq
 import oracle
 from workloads import Workload, gen_new_tokens, gen_prefill, gen_queries, TINY
-from gpu_helpers import (split_tol, ATOL, compare_all_buffers, deterministic_schedule, host, make_cache, max_err,
-                         oracle_attention)
+from gpu_helpers import (split_tol, ATOL, compare_all_buffers, host, make_cache, max_err, oracle_attention,
+                         queue_schedule)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,11 +89,13 @@ def test_split_count_invariance_and_determinism(bits, G, hpg):
         outs.append(host(o))
     for o in outs[1:]:
         assert float(np.abs(o - outs[0]).max()) <= split_tol(hpg)
-    with deterministic_schedule():
-        again = host(cache.attention(q, splits=0))
-        twice = host(cache.attention(q, splits=0))
+    again = host(cache.attention(q, splits=0))
+    twice = host(cache.attention(q, splits=0))
     assert np.array_equal(again, twice), "reruns must be bit-identical"
-    assert float(np.abs(again - outs[-1]).max()) <= split_tol(hpg)
+    assert np.array_equal(again, outs[-1]), "reruns must be bit-identical"
+    with queue_schedule(cache):
+        dyn = host(cache.attention(q, splits=0))
+    assert float(np.abs(dyn - again).max()) <= split_tol(hpg)
 
 
 def test_empty_prefill_then_single_token():
