@@ -206,9 +206,17 @@ def test_gqa_mfma_work_queue_counters():
                     assert max_err(out, want) <= ATOL, (schedule, splits, stale)
                     assert int(ctr.abs().sum()) == 0, host(ctr)
                 if schedule == kvq.KVQ_SCHED_QUEUE:
+                    # each of the 4 * splits waves takes its first two super-chunks
+                    # (four key groups each) by index; the ticket is read only
+                    # when more super-chunks remain
+                    nsc = -(-(min(ref.nq_k, ref.nq_v) // 32) // 4)
+                    queued = 2 * 4 * splits < nsc
                     ctr[4 * u] = 5                # a ticket that did not start at zero
                     got = host(_attention(cache, q, "mfma", workspace=ws, splits=splits))
-                    assert np.isnan(got[b, 4 * h:4 * h + 4]).all(), "a miscounted unit must come out NaN"
-                    assert float(np.abs(got[keep].astype(np.float64) - want[keep]).max()) <= ATOL
+                    if queued:
+                        assert np.isnan(got[b, 4 * h:4 * h + 4]).all(), "a miscounted unit must come out NaN"
+                        assert float(np.abs(got[keep].astype(np.float64) - want[keep]).max()) <= ATOL
+                    else:
+                        assert float(np.abs(got.astype(np.float64) - want).max()) <= ATOL
                     assert int(ctr.abs().sum()) == 0, host(ctr)
                     assert max_err(_attention(cache, q, "mfma", workspace=ws, splits=splits), want) <= ATOL
