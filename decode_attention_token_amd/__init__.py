@@ -26,9 +26,10 @@ KVQ_KERNEL_AUTO, KVQ_KERNEL_VALU = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
-    "kvq_append_token", "kvq_decode_attention", "kvq_decode_step", "kvq_stream_read_probe", "kvq_status_string",
-    "kvq_last_error",
+    "kvq_append_token", "kvq_decode_attention", "kvq_decode_attention_static", "kvq_decode_step",
+    "kvq_stream_read_probe", "kvq_status_string", "kvq_last_error",
 ]
+KVQ_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class kvq_config(ctypes.Structure):
@@ -86,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_float, vp, vp,
                                          ctypes.c_size_t, ctypes.c_int32, vp]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_decode_attention_static.argtypes = [P(kvq_config), P(kvq_cache), vp, ctypes.c_float, vp,
+                                                ctypes.c_int32, vp]
+    lib.kvq_decode_attention_static.restype = ctypes.c_int
     lib.kvq_decode_step.argtypes = [P(kvq_config), P(kvq_cache), vp, vp, vp, ctypes.c_float, vp, vp,
                                     ctypes.c_size_t, ctypes.c_int32, vp]
     lib.kvq_decode_step.restype = ctypes.c_int
@@ -232,6 +236,16 @@ class KVCache:
         kvq_decode_step(cfg, self, k_new, v_new, q, softmax_scale, out, workspace, splits, stream)
         return out
 
+    def attention_static(self, q, softmax_scale=None, out=None, splits=0, stream=None):
+        """Attention without a workspace: the library's static device scratch."""
+        cfg = self.cfg
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(cfg.head_dim)
+        if out is None:
+            out = torch.empty(cfg.batch, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+        kvq_decode_attention_static(cfg, self, q, softmax_scale, out, splits, stream)
+        return out
+
     def attention(self, q, softmax_scale=None, out=None, workspace=None, splits=0, stream=None):
         cfg = self.cfg
         if softmax_scale is None:
@@ -272,6 +286,18 @@ def kvq_decode_attention(cfg, cache: KVCache, q, softmax_scale, out, workspace, 
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib_handle.kvq_decode_attention(cache._cfg_ref, cache._c_ref, qp, softmax_scale, out.data_ptr(),
                                             workspace.data_ptr(), nbytes, splits, _stream_ptr(stream)))
+
+
+def kvq_decode_attention_static(cfg, cache: KVCache, q, softmax_scale, out, splits=0, stream=None):
+    """kvq_decode_attention with the library's static device scratch in place
+    of a workspace (for callers that cannot allocate)."""
+    if cfg is not cache.cfg:
+        raise ValueError("cfg must be the cache's own config")
+    qp = _f16_ptr(q, cache._q_shape, "q")
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.shape != cache._q_shape:
+        raise ValueError("out must be a contiguous fp32 CUDA tensor [batch][num_q_heads][head_dim]")
+    _check(load_library().kvq_decode_attention_static(cache._cfg_ref, cache._c_ref, qp, softmax_scale,
+                                                      out.data_ptr(), splits, _stream_ptr(stream)))
 
 
 def kvq_decode_step(cfg, cache: KVCache, k_new, v_new, q, softmax_scale, out, workspace, splits=0, stream=None):

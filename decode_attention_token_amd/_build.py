@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_gqa.hip", "kvq_innerq.hip", "kvq_probe.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_attn.hip", "kvq_attn_gqa.hip", "kvq_innerq.hip", "kvq_probe.hip",
+           "kvq_noalloc.hip"]
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 arithmetic;
 # correctly rounded fp32 division (the hipcc default) is required for the

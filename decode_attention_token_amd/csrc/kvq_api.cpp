@@ -20,6 +20,7 @@
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
+#include "kvq_api_internal.h"
 
 namespace {
 
@@ -480,11 +481,13 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
 
 }  // namespace
 
-extern "C" {
+namespace kvq {
 
-kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
-                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-                                int32_t splits, hipStream_t stream) {
+kvq_status report(kvq_status s, const char *msg) { return fail(s, "%s", msg); }
+
+kvq_status decode_attention_into(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                 float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                 int32_t splits, hipStream_t stream) {
   kvq_status s = check_attention_args(cfg, cache, q, out, workspace, splits, softmax_scale);
   if (s != KVQ_OK) return s;
   if (cache->n_tokens < 1) return fail(KVQ_ERR_STATE, "attention over an empty cache");
@@ -492,6 +495,16 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, c
                        workspace_bytes, splits, stream);
   if (s == KVQ_OK) g_err[0] = 0;
   return s;
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                int32_t splits, hipStream_t stream) {
+  return kvq::decode_attention_into(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
 }
 
 kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new, const uint16_t *v_new,

@@ -276,6 +276,29 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const kvq_cache *cache,
                                 void *workspace, size_t workspace_bytes, int32_t splits,
                                 hipStream_t stream);
 
+/* Size in bytes of the device array kvq_decode_attention_static uses in place
+ * of a workspace (one copy per GPU, held until the process ends). */
+#define KVQ_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* kvq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the per-unit counters and split records
+ * live in a file-scope device array of KVQ_STATIC_SCRATCH_BYTES bytes that the
+ * library's code object carries; nothing is allocated or freed at run time.
+ * Same arguments, results and requirements as kvq_decode_attention, except:
+ * the matrix-core kernel always runs the fixed schedule (cfg->schedule is
+ * ignored), so results equal kvq_decode_attention's with KVQ_SCHED_FIXED bit
+ * for bit; `stream` must belong to the current device (KVQ_ERR_ARG
+ * otherwise); a call whose workspace size (kvq_workspace_bytes for its splits
+ * and n_tokens) exceeds KVQ_STATIC_SCRATCH_BYTES returns KVQ_ERR_CAPACITY and
+ * enqueues nothing.  Every call on a GPU shares that GPU's array, which keeps
+ * the last call's contents; no part of it needs to start at zero.  Calls that
+ * overlap on one GPU (other streams, other host threads) race on the array
+ * and must be ordered by the caller.  The first call on a device looks up the
+ * array's device address (KVQ_ERR_DEVICE if that fails). */
+kvq_status kvq_decode_attention_static(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
+                                       float softmax_scale, float *out, int32_t splits, hipStream_t stream);
+
 /* One decode step: kvq_append_token(k_new, v_new) followed by
  * kvq_decode_attention(q) with the same results, but as a single kernel
  * launch whenever a KIVI append needs no flush, the new token is not a sink

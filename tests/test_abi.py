@@ -31,6 +31,11 @@ def test_header_declares_the_binding_surface():
     assert _declared() == sorted(kvq.EXPORTED)
 
 
+def test_static_scratch_size_matches_the_header():
+    m = re.search(r"#define\s+KVQ_STATIC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.KVQ_STATIC_SCRATCH_BYTES
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
