@@ -458,6 +458,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--reps", type=int, default=4, help="attention-only passes for kernel timing")
+    ap.add_argument("--settle", type=float, default=0.1,
+                    help="seconds of untimed back-to-back attention calls before timing")
     ap.add_argument("--no-side", action="store_true", help="skip the prefill, flush and tiny-workload timings")
     ap.add_argument("--v-policy", choices=("chunk", "fifo"), default=None,
                     help="override the workload's value-residual policy (KIVI scheme)")
@@ -518,6 +520,46 @@ def main():
                 nb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
         return nb
 
+    # Steady state: the device's memory and compute clocks ramp under
+    # sustained load, so before anything is timed the attention kernel runs
+    # back to back (untimed) for at least settle_s.
+    last = total - 1
+
+    def attention_pass():
+        calls, cb, fb = 0, 0, 0
+        for layer in range(layers):
+            c = caches[layer]
+            c.attention(qs[layer][last], scale, outs[layer], ws, args.splits, sp)
+            calls += 1
+            cb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
+            fb += w.units * c.n_tokens * w.head_dim * 2 * 2 + w.batch * w.num_q_heads * w.head_dim * 6
+        return calls, cb, fb
+
+    print("# settle", file=sys.stderr, flush=True)
+    t_settle = time.perf_counter()
+    settle_calls = 0
+    while time.perf_counter() - t_settle < args.settle:
+        settle_calls += attention_pass()[0]
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
+
+    def timed_attention(reps):
+        """Attention-only passes over the layers, HIP events on the library's stream."""
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        calls, cb, fb = 0, 0, 0
+        ev0.record(stream)
+        for _ in range(reps):
+            c_, b_, f_ = attention_pass()
+            calls, cb, fb = calls + c_, cb + b_, fb + f_
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / calls, cb / calls, fb / calls, calls
+
+    print("# kernel timing", file=sys.stderr, flush=True)
+    n_before = caches[0].n_tokens
+    call_us, call_bytes, fp16_bytes, calls = timed_attention(args.reps)
+
     print("# warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i, False)
@@ -535,6 +577,7 @@ def main():
         step_bytes.append(nb)
         flushed.append(caches[0].flushes != f0)
     evs[steps].record(stream)
+    t_enq = time.perf_counter() - t0   # host time to enqueue the loop
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     step_us = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)]
@@ -545,24 +588,8 @@ def main():
     fused_bytes = (sum(step_bytes[k] for k in plain) / (len(plain) * layers) + w.units * w.head_dim * 2 * 2
                    if plain else None)
 
-    # attention-only passes, timed with HIP events on the library's stream
-    print("# kernel timing", file=sys.stderr, flush=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    last = total - 1
-    calls, cb, fb = 0, 0, 0
-    ev0.record(stream)
-    for _ in range(args.reps):
-        for layer in range(layers):
-            c = caches[layer]
-            c.attention(qs[layer][last], scale, outs[layer], ws, args.splits, sp)
-            calls += 1
-            cb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
-            fb += w.units * c.n_tokens * w.head_dim * 2 * 2 + w.batch * w.num_q_heads * w.head_dim * 6
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    call_us = ev0.elapsed_time(ev1) * 1e3 / calls
-    call_bytes = cb / calls
+    # the same attention-only passes again after the loop (drift check)
+    after_us, after_bytes, _, _ = timed_attention(args.reps)
     att_gbs = call_bytes / (call_us * 1e-6) / 1e9
 
     side = time_prefill_and_flush(w, dev, stream) if not args.no_side else None
@@ -616,14 +643,21 @@ def main():
                      "avg_launch_us": round(roof_us, 2), "bytes_per_launch": int(roof_bytes),
                      "launches": (len(plain) * layers) if roof_us is fused_us else calls},
         "attention_only": {"avg_call_us": round(call_us, 2), "bytes_per_call": int(call_bytes),
-                           "GB/s": round(att_gbs, 1), "frac": round(att_gbs / HBM_PEAK_GBS, 4), "calls": calls},
+                           "GB/s": round(att_gbs, 1), "frac": round(att_gbs / HBM_PEAK_GBS, 4), "calls": calls,
+                           "n_tokens": n_before,
+                           "after_loop": {"avg_call_us": round(after_us, 2), "bytes_per_call": int(after_bytes),
+                                          "n_tokens": caches[0].n_tokens}},
+        "settle": {"seconds": round(settle_s, 3), "attention_calls": settle_calls,
+                   "note": "untimed back-to-back attention calls before any timing (clocks reach steady state)"},
+        "host_enqueue_us_per_launch": round(t_enq / (steps * layers) * 1e6, 2),
         "loop_steps_with_flush": int(sum(flushed)),
         "loop_step_us": {"median": round(sorted(step_us)[len(step_us) // 2], 1), "min": round(min(step_us), 1),
-                         "max": round(max(step_us), 1), "launches_per_step": layers if one_launch else None},
+                         "max": round(max(step_us), 1), "first": [round(t, 1) for t in step_us[:8]],
+                         "launches_per_step": layers if one_launch else None},
         # what an fp16 cache of the same tokens would move per call, over the
         # same call time: a compression view, not a roofline fraction
-        "fp16_equivalent": {"GB/s": round(fb / calls / (call_us * 1e-6) / 1e9, 1),
-                            "bytes_per_call": int(fb / calls)},
+        "fp16_equivalent": {"GB/s": round(fp16_bytes / (call_us * 1e-6) / 1e9, 1),
+                            "bytes_per_call": int(fp16_bytes)},
         # the library's plain streaming-read kernel over 4 GiB on this device:
         # the achievable read rate, for context beside the 8 TB/s peak
         "stream_ceiling": {"GB/s": round(ceiling, 1), "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4),

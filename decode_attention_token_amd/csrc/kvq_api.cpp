@@ -422,6 +422,7 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.nq_k = a.nq_v = cache->nq_k;
   a.n_main = cache->nq_k;
   a.splits = splits;
+  a.interleave = 0;
   a.tail_wg = 0;
   a.resid_main = 1;
   a.nparts = splits;
@@ -471,6 +472,13 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.tail_wg = (has_rest && !all_fp16) ? 1 : 0;
   a.splits = n_main > 0 ? splits : ((a.resid_main || ns > 0) ? 1 : 0);
   a.nparts = a.splits + a.tail_wg;
+  // Wave order of the vector-ALU kernel: when a wave's contiguous share of
+  // its split would span more than 32 KiB of key codes, its waves take
+  // every eighth key group instead (measured: 3.6% faster on a 4-bit cache
+  // of 8192 tokens, 64 KiB per wave; 1.5% slower on a 2-bit cache of 4096
+  // tokens, 16 KiB per wave).
+  const int64_t wave_span = (a.splits > 0 ? n_main / a.splits : 0) / 8 * (cfg->head_dim * cfg->bits / 8);
+  a.interleave = wave_span > 32 * 1024 ? 1 : 0;
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.k_new = k_new;
   a.v_new = v_new;

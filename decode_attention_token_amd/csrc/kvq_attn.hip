@@ -228,9 +228,14 @@ void decode_attn_kernel(AttnArgs a) {
   const int ngroups = (int)(a.n_main / GS);
   const int g0 = (int)((int64_t)ngroups * split / a.splits);
   const int g1 = (int)((int64_t)ngroups * (split + 1) / a.splits);
-  const int wg0 = g0 + (g1 - g0) * wave / kWaves;
-  const int wg1 = g0 + (g1 - g0) * (wave + 1) / kWaves;
-  const int nsteps = (wg1 - wg0) * SPG;
+  // a wave's key groups: a contiguous eighth of the split, or (a.interleave,
+  // chosen on the host for long splits) every eighth group, so the
+  // workgroup's waves read neighbouring groups at any one time
+  const int wg0 = a.interleave ? g0 + wave : g0 + (g1 - g0) * wave / kWaves;
+  const int wstride = a.interleave ? kWaves : 1;
+  const int wgroups = a.interleave ? (g1 - g0 - wave + kWaves - 1) / kWaves
+                                   : (g1 - g0) * (wave + 1) / kWaves - (g1 - g0) * wave / kWaves;
+  const int nsteps = wgroups * SPG;
 
   // query (log2 units, divided by the unpack scale) for channels 2*lane,
   // 2*lane+1, used to fold key scales
@@ -273,7 +278,7 @@ void decode_attn_kernel(AttnArgs a) {
 
   auto load = [&](Buf &bf, int s) {
     s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
-    const uint32_t g = (uint32_t)(wg0 + s / SPG);
+    const uint32_t g = (uint32_t)(wg0 + wstride * (s / SPG));
     const uint32_t tb = g * GS + (uint32_t)((s % SPG) * TPS);   // first token of the step (uniform)
     bload_words<WPL>(rkc, code_lane, tb * (W * 4), bf.kw);
     bload_words<WPL>(rvc, code_lane, tb * (W * 4), bf.vw);

@@ -95,6 +95,8 @@ struct AttnArgs {
   int64_t n, nq_k, nq_v;
   int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups
   int splits;            // workgroups per unit over [0, n_main) (>= 1 when resid_main)
+  int interleave;        // KIVI vector-ALU kernel: waves take every eighth key group of their
+                         // split instead of a contiguous eighth
   int tail_wg;           // 1: an extra workgroup per unit runs the mixed tail [n_main, n)
   int resid_main;        // 1: [n_main, n) is all-fp16 and the last split takes it
   int nparts;            // splits + tail_wg; 1 means the kernel writes out directly

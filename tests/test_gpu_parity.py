@@ -251,3 +251,32 @@ def test_kivi_sink_decode_step_matches_append_then_attention():
     for b in range(2):
         for h in range(2):
             compare_sink_unit(fused, ref, b, h)
+
+
+@pytest.mark.parametrize("bits,G,L", [(4, 64, 9000), (2, 32, 17000)])
+def test_wave_orders_agree(bits, G, L):
+    """One split per unit spans more than 32 KiB of key codes per wave, so its
+    waves take every eighth key group; with 4 or 16 splits each wave keeps a
+    contiguous range.  Both orders match the oracle and each other."""
+    w = _w(130 + bits, 1, 2, 2, L, bits, G, 128, 1)
+    print(f"case {w.name}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    q = gen_queries(w, 0, "cuda")[0].contiguous()
+    cfg, cache = make_cache(bits, G, 128, 1, 2, 2, w.max_tokens)
+    cache.prefill(k, v)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    ref = oracle.QuantizedKVCache(bits, G, 128, 1, 2, 128)
+    ref.prefill(host(k), host(v))
+    ref.append(host(kn[0]), host(vn[0]))
+    want = oracle_attention(ref, host(q), 1 / math.sqrt(128))
+    outs = {}
+    for s in (1, 4, 16):
+        o = cache.attention(q, workspace=cache.workspace(splits=s), splits=s)
+        torch.cuda.synchronize()
+        err = max_err(o, want)
+        print(f"  splits {s}: err {err:.2e}", flush=True)
+        assert err <= ATOL
+        outs[s] = host(o)
+    assert float(np.abs(outs[1] - outs[4]).max()) <= split_tol(1)
+    assert float(np.abs(outs[1] - outs[16]).max()) <= split_tol(1)
