@@ -114,14 +114,11 @@ def sample_units(w, host_bytes=512 << 20, seed=7):
     return [int(u) for u in np.random.default_rng(seed).permutation(w.units)[:count]]
 
 
-# decode kernel, its source files and its committed counter summary per scheme
+# decode kernel and its source files per kind
 KERNELS = {
-    0: ("decode_attn_kernel", ("kvq_attn.hip", "kvq_attn_common.h", "kvq_internal.h"),
-        "decode_attn_llama2_7b_2bit_traffic.txt"),
-    1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_internal.h"),
-        "innerq_attn_b4_h32_L131072_4bit_traffic.txt"),
-    "gqa4": ("gqa_mfma_kernel", ("kvq_attn_gqa.hip", "kvq_attn_common.h", "kvq_internal.h"),
-             "gqa_mfma_b8_q32_kv8_L32768_2bit_traffic.txt"),
+    0: ("decode_attn_kernel", ("kvq_attn.hip", "kvq_attn_common.h", "kvq_internal.h")),
+    1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_internal.h")),
+    "gqa4": ("gqa_mfma_kernel", ("kvq_attn_gqa.hip", "kvq_attn_common.h", "kvq_internal.h")),
 }
 
 
@@ -146,21 +143,27 @@ def kernel_source_digest(scheme=0):
 
 def measured_traffic(w, kernel=kvq.KVQ_KERNEL_AUTO):
     """HBM bytes per launch of the decode kernel from the committed counter
-    summary, or None when it is missing, for another workload, or taken on a
-    different kernel source."""
+    summaries (profiles/*_traffic.txt) for this workload, or None when none
+    exists or it was taken on a different kernel source."""
     key = kernel_key(w, kernel)
+    pdir = os.path.join(ROOT, "profiles")
     try:
-        with open(os.path.join(ROOT, "profiles", KERNELS[key][2])) as f:
-            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        names = sorted(f for f in os.listdir(pdir) if f.endswith("_traffic.txt"))
     except OSError:
         return None
-    kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("kernel_source_digest") != kernel_source_digest(key) or kv.get("workload") != w.name:
-        return None
-    try:
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+    for name in names:
+        with open(os.path.join(pdir, name)) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("workload") != w.name or not kv.get("kernel", "").startswith(KERNELS[key][0]):
+            continue
+        if kv.get("kernel_source_digest") != kernel_source_digest(key):
+            return None
+        try:
+            return int(float(kv["hbm_bytes_per_launch"]))
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def host_sample(w, units, dev):
