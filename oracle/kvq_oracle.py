@@ -58,6 +58,15 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                          min(R, n - sinks) tokens, prefill(L)+appends ==
                          prefill(L+m), all-fp16 cache reduces to plain
                          attention.
+  key_channel_normalizer / normalize_keys / InnerQCache(key_norm=True)
+                         pinned: scales are the smallest powers of two >=
+                         max(1, max-abs) (brute-force scan of powers of two),
+                         prompt keys land in [-1, 1], scales never change on
+                         append, keys all within [-1, 1] give the plain cache
+                         byte for byte, a common power-of-two scale leaves
+                         codes and attention bit-identical to the plain cache,
+                         the fold-into-query form equals dequantize-then-scale,
+                         |k - k_hat| <= lambda * S / 2.
 
 Sources for the InnerQ-style variant:
   [InnerQ] euno.news, "【论文】InnerQ：硬件感知免调优KV缓存量化用于大语言模型",
@@ -65,7 +74,8 @@ Sources for the InnerQ-style variant:
            group statistics min, max, mean, variance; symmetric quantization
            when the group is centred on zero, asymmetric otherwise, one
            shared scale per group), 4 (recent and attention-sink tokens kept
-           in fp16).
+           in fp16; keys scaled once per channel at prefill, the scale folded
+           into the query).
   [HFQ] 2.1 defines symmetric quantization as a range symmetric about zero.
 """
 from __future__ import annotations
@@ -76,7 +86,7 @@ __all__ = [
     "quantize_groups", "dequantize", "pack_rows", "unpack_rows", "QuantizedKVCache",
     "attention", "kv_code_bytes_per_token", "attention_call_bytes",
     "CHUNK", "FIFO", "META_F32", "META_F16", "round_up_to_fp16", "hybrid_is_symmetric", "quantize_groups_symmetric", "quantize_groups_hybrid",
-    "InnerQCache", "innerq_attention_call_bytes", "KiviSinkCache",
+    "InnerQCache", "innerq_attention_call_bytes", "KiviSinkCache", "key_channel_normalizer", "normalize_keys",
 ]
 
 CHUNK = 0   # value residual flushed as a block of R tokens, like the keys ([HFQ] 3.1)
@@ -507,6 +517,29 @@ def quantize_groups_hybrid(x, bits: int):
     return codes, np.where(sym, ss, sa).astype(_F32), np.where(sym, zs, za).astype(np.int16)
 
 
+def key_channel_normalizer(k):
+    """[InnerQ] methodology 4: one scale per key channel, computed once from
+    the prompt's keys.  Reading: the per-channel normalization into [-1, 1]
+    (as the KVQuant part of the juejin.cn page normalizes each channel),
+    with the scale rounded up to a power of two and at least 1:
+        lambda_c = smallest power of two >= max(1, max_t |k[t, c]|)
+    so dividing a key by it and multiplying the query by it are exact.
+    k: float16 [B, H, L, d] (L may be 0)  ->  float32 [B, H, d]."""
+    k = np.asarray(k, np.float16).astype(np.float64)
+    B, H, L, d = k.shape
+    amax = np.abs(k).max(axis=2) if L else np.zeros((B, H, d))
+    m, e = np.frexp(amax)                      # amax = m * 2^e, m in [0.5, 1)
+    lam = np.where(m == 0.5, amax, np.ldexp(1.0, e))
+    return np.where(amax <= 1.0, 1.0, lam).astype(_F32)
+
+
+def normalize_keys(k, lam):
+    """Keys divided by their channel scale (a power of two, exact in float32),
+    rounded to float16 (round to nearest even; only values that fall below the
+    float16 normal range round).  k [..., d] float16, lam broadcastable."""
+    return (np.asarray(k, np.float16).astype(_F32) / np.asarray(lam, _F32)).astype(np.float16)
+
+
 class InnerQCache:
     """InnerQ-style cache: keys and values both grouped along the hidden
     dimension (per token, groups of G channels, [InnerQ] methodology 1) with
@@ -516,9 +549,17 @@ class InnerQCache:
     Token t < sinks is a sink.  Later tokens enter a FIFO window; once a push
     makes the window exceed `window` tokens, the oldest one is quantized and
     appended to the quantized part [sinks, nq).
+
+    key_norm ([InnerQ] methodology 4, per-channel key scaling at prefill):
+    the prompt's keys give one scale per (unit, channel) (key_channel_normalizer),
+    fixed for the life of the cache; every key that is quantized, at prefill
+    or when it leaves the window, is divided by it first (normalize_keys).
+    The fp16 sinks and window keep the original keys.  Dequantized keys are
+    returned in the original units (lambda * S * (code + Z)), which equals
+    folding lambda into the query.
     """
 
-    def __init__(self, bits, group, window, sinks, batch, kv_heads, head_dim):
+    def __init__(self, bits, group, window, sinks, batch, kv_heads, head_dim, key_norm=False):
         if head_dim % group:
             raise ValueError("head_dim must be a multiple of G")
         if window <= 0 or sinks < 0:
@@ -536,6 +577,8 @@ class InnerQCache:
         self.qv_z = np.zeros((B, H, 0, d // G), np.int16)
         self.rk = np.zeros((B, H, 0, d), np.float16)
         self.rv = np.zeros((B, H, 0, d), np.float16)
+        self.key_norm = bool(key_norm)
+        self.k_norm = np.ones((B, H, d), _F32)
         self.n = 0
         self.started = False
 
@@ -551,6 +594,8 @@ class InnerQCache:
         return c.reshape(B, H, m, d), s, z
 
     def _push_quantized(self, k, v):
+        if self.key_norm:
+            k = normalize_keys(k, self.k_norm[:, :, None, :])
         c, s, z = self._quantize_rows(k)
         self.qk = np.concatenate([self.qk, c], axis=2)
         self.qk_s = np.concatenate([self.qk_s, s], axis=2)
@@ -566,6 +611,8 @@ class InnerQCache:
         k = np.asarray(k, np.float16)
         v = np.asarray(v, np.float16)
         L = k.shape[2]
+        if self.key_norm:
+            self.k_norm = key_channel_normalizer(k)
         ns = min(L, self.S)
         self.sink_k, self.sink_v = k[:, :, :ns].copy(), v[:, :, :ns].copy()
         if L > self.S:
@@ -595,6 +642,7 @@ class InnerQCache:
         B, H, d, G = self.B, self.H, self.d, self.G
         m = self.qk.shape[2]
         kh = dequantize(self.qk.reshape(B, H, m, d // G, G), self.qk_s, self.qk_z).reshape(B, H, m, d)
+        kh = (kh * self.k_norm[:, :, None, :]).astype(_F32)   # exact: powers of two
         vh = dequantize(self.qv.reshape(B, H, m, d // G, G), self.qv_s, self.qv_z).reshape(B, H, m, d)
         K = np.concatenate([self.sink_k.astype(_F32), kh, self.rk.astype(_F32)], axis=2)
         V = np.concatenate([self.sink_v.astype(_F32), vh, self.rv.astype(_F32)], axis=2)
@@ -633,6 +681,8 @@ class InnerQCache:
         for i in range(self.rk.shape[2]):
             out["k_resid"][:, :, (nq + i) % R] = self.rk[:, :, i]
             out["v_resid"][:, :, (nq + i) % R] = self.rv[:, :, i]
+        if self.key_norm:
+            out["k_norm"] = self.k_norm.copy()     # f32 [B,H,d], channel scales
         return out
 
     def live_resid_slots(self):
