@@ -87,9 +87,13 @@ def stream_ceiling(dev, stream, reps=5):
     return gbs
 
 
+KEY_NORM = {"on": False}   # --key-norm: InnerQ caches scale keys per channel at prefill
+
+
 def make_cfg(w, max_tokens, schedule=kvq.KVQ_SCHED_FIXED, kernel=kvq.KVQ_KERNEL_AUTO):
+    key_norm = kvq.KVQ_KEYNORM_PROMPT if KEY_NORM["on"] and w.scheme == kvq.KVQ_SCHEME_INNERQ else 0
     return kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks, w.meta, schedule, kernel)
+                           w.head_dim, max_tokens, w.v_policy, w.scheme, w.sinks, w.meta, schedule, kernel, key_norm)
 
 
 def build_caches(w, layers, max_tokens, dev, schedule=kvq.KVQ_SCHED_FIXED, kernel=kvq.KVQ_KERNEL_AUTO):
@@ -183,10 +187,10 @@ def host_sample(w, units, dev):
     return out
 
 
-def _oracle_unit_cache(w):
+def _oracle_unit_cache(w, key_norm=False):
     import oracle
     if w.scheme == kvq.KVQ_SCHEME_INNERQ:
-        return oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+        return oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, key_norm=key_norm)
     if w.sinks:
         return oracle.KiviSinkCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, w.v_policy, w.meta)
     return oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy, w.meta)
@@ -200,7 +204,7 @@ def _unit_attn_bytes(w, ref):
     return attn_bytes(unit_w, ref.n, ref.nq_k, ref.nq_v)
 
 
-def _oracle_attention_worker(w, items, budget_s):
+def _oracle_attention_worker(w, items, budget_s, key_norm=False):
     """Oracle decode-attention calls (dequantize + float64 attention) on the
     given units, one thread (BLAS included), swept until budget_s seconds of
     timed work: (bytes, seconds, calls)."""
@@ -209,7 +213,7 @@ def _oracle_attention_worker(w, items, budget_s):
     with threadpool_limits(limits=1):
         refs = []
         for k, v, kn, vn, q in items:
-            ref = _oracle_unit_cache(w)
+            ref = _oracle_unit_cache(w, key_norm)
             ref.prefill(k, v)
             ref.append(kn[0], vn[0])
             refs.append((ref, q, _unit_attn_bytes(w, ref)))
@@ -257,11 +261,12 @@ def cpu_baseline(w, sample, budget_s=10.0, pool_budget_s=6.0):
     from threadpoolctl import threadpool_limits
     import oracle  # noqa: F401  (the oracle is the baseline being timed)
 
-    one = _oracle_attention_worker(w, sample, budget_s)
+    key_norm = KEY_NORM["on"] and w.scheme == kvq.KVQ_SCHEME_INNERQ
+    one = _oracle_attention_worker(w, sample, budget_s, key_norm)
     cores = min(host_cores(), len(sample))
     shards = [sample[i::cores] for i in range(cores)]
     with mp.get_context("spawn").Pool(cores) as pool:
-        res = pool.starmap(_oracle_attention_worker, [(w, sh, pool_budget_s) for sh in shards])
+        res = pool.starmap(_oracle_attention_worker, [(w, sh, pool_budget_s, key_norm) for sh in shards])
     pool_bytes = sum(r[0] for r in res)
     pool_s = max(r[1] for r in res)
     pool_calls = sum(r[2] for r in res)
@@ -271,7 +276,7 @@ def cpu_baseline(w, sample, budget_s=10.0, pool_budget_s=6.0):
     t_pre = t_fl = 0.0
     with threadpool_limits(limits=1):
         for k, v, kn, vn, q in sample[:nunits]:
-            ref = _oracle_unit_cache(w)
+            ref = _oracle_unit_cache(w, key_norm)
             t0 = time.perf_counter()
             ref.prefill(k, v)
             t_pre += time.perf_counter() - t0
@@ -473,6 +478,8 @@ def main():
                     help="matrix-core kernel work order: fixed (bit-identical reruns) or the work queue")
     ap.add_argument("--kernel", choices=("auto", "valu"), default="auto",
                     help="four query heads per kv head: matrix cores (auto) or the vector-ALU kernel")
+    ap.add_argument("--key-norm", action="store_true",
+                    help="InnerQ scheme: scale keys once per channel at prefill, folded into the query")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -490,6 +497,9 @@ def main():
         w = w.scaled(sinks=args.sinks)
     if args.meta is not None:
         w = w.scaled(meta=0 if args.meta == "f32" else 1, name=w.name + ("-meta16" if args.meta == "f16" else ""))
+    if args.key_norm and w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        KEY_NORM["on"] = True
+        w = w.scaled(name=w.name + "-keynorm")
     schedule = kvq.KVQ_SCHED_QUEUE if args.schedule == "queue" else kvq.KVQ_SCHED_FIXED
     kernel = kvq.KVQ_KERNEL_VALU if args.kernel == "valu" else kvq.KVQ_KERNEL_AUTO
     steps = w.steps if args.steps is None else args.steps
@@ -639,6 +649,7 @@ def main():
                    "splits": splits_used, "codes": f"u{w.bits}", "v_policy": "chunk" if w.v_policy == 0 else "fifo",
                    "scheme": "innerq" if w.scheme == kvq.KVQ_SCHEME_INNERQ else "kivi", "sinks": w.sinks,
                    "meta": "f16-packed" if w.meta else "f32+i16", "schedule": args.schedule,
+                   "key_norm": bool(KEY_NORM["on"]),
                    "kernel": KERNELS[kernel_key(w, kernel)][0]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, kernel),

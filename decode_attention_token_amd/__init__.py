@@ -23,6 +23,7 @@ KVQ_SCHEME_KIVI, KVQ_SCHEME_INNERQ = 0, 1
 KVQ_META_F32, KVQ_META_F16 = 0, 1
 KVQ_SCHED_FIXED, KVQ_SCHED_QUEUE = 0, 1
 KVQ_KERNEL_AUTO, KVQ_KERNEL_VALU = 0, 1
+KVQ_KEYNORM_NONE, KVQ_KEYNORM_PROMPT = 0, 1
 
 EXPORTED = [
     "kvq_layout_bytes", "kvq_auto_splits", "kvq_workspace_bytes", "kvq_quantize_prefill",
@@ -35,13 +36,13 @@ KVQ_STATIC_SCRATCH_BYTES = 16 << 20
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bits", "group", "residual", "batch", "num_q_heads", "num_kv_heads", "head_dim",
-        "max_tokens", "v_policy", "scheme", "sink_tokens", "meta_format", "schedule", "kernel")]
+        "max_tokens", "v_policy", "scheme", "sink_tokens", "meta_format", "schedule", "kernel", "key_norm")]
 
 
 class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid", "k_sink",
-        "v_sink")]
+        "v_sink", "k_norm")]
 
 
 class kvq_cache(ctypes.Structure):
@@ -51,7 +52,7 @@ class kvq_cache(ctypes.Structure):
         ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
         ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
         ("n_tokens", ctypes.c_int64), ("nq_k", ctypes.c_int64), ("nq_v", ctypes.c_int64),
-        ("started", ctypes.c_int32), ("flushes", ctypes.c_int32),
+        ("started", ctypes.c_int32), ("flushes", ctypes.c_int32), ("k_norm", ctypes.c_void_p),
     ]
 
 
@@ -111,17 +112,18 @@ def _check(status: int):
 
 def make_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
                 v_policy=KVQ_V_CHUNK, scheme=KVQ_SCHEME_KIVI, sink_tokens=0, meta_format=KVQ_META_F32,
-                schedule=KVQ_SCHED_FIXED, kernel=KVQ_KERNEL_AUTO) -> kvq_config:
+                schedule=KVQ_SCHED_FIXED, kernel=KVQ_KERNEL_AUTO, key_norm=KVQ_KEYNORM_NONE) -> kvq_config:
     return kvq_config(bits, group, residual, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                      v_policy, scheme, sink_tokens, meta_format, schedule, kernel)
+                      v_policy, scheme, sink_tokens, meta_format, schedule, kernel, key_norm)
 
 
 def make_innerq_config(bits, group, window, sink_tokens, batch, num_q_heads, num_kv_heads, head_dim,
-                       max_tokens) -> kvq_config:
+                       max_tokens, key_norm=KVQ_KEYNORM_NONE) -> kvq_config:
     """InnerQ-style cache: hybrid groups of `group` channels per token for keys
-    and values, `sink_tokens` leading and `window` recent tokens in fp16."""
+    and values, `sink_tokens` leading and `window` recent tokens in fp16;
+    key_norm=KVQ_KEYNORM_PROMPT scales keys once per channel at prefill."""
     return make_config(bits, group, window, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
-                       KVQ_V_FIFO, KVQ_SCHEME_INNERQ, sink_tokens)
+                       KVQ_V_FIFO, KVQ_SCHEME_INNERQ, sink_tokens, key_norm=key_norm)
 
 
 def kvq_layout_bytes(cfg: kvq_config) -> kvq_layout:
@@ -162,7 +164,7 @@ class KVCache:
     _DT = {"k_codes": torch.int32, "k_scale": torch.float32, "k_zero": torch.int16,
            "v_codes": torch.int32, "v_scale": torch.float32, "v_zero": torch.int16,
            "k_resid": torch.float16, "v_resid": torch.float16, "k_sink": torch.float16,
-           "v_sink": torch.float16}
+           "v_sink": torch.float16, "k_norm": torch.float32}
 
     def __init__(self, cfg: kvq_config, device="cuda"):
         self.cfg = cfg
@@ -178,7 +180,8 @@ class KVCache:
         shapes = {"k_codes": (B, H, cap, W), "k_scale": kmeta, "k_zero": none(kmeta) if packed else kmeta,
                   "v_codes": (B, H, cap, W), "v_scale": vmeta, "v_zero": none(vmeta) if packed else vmeta,
                   "k_resid": (B, H, R, d), "v_resid": (B, H, R, d),
-                  "k_sink": (B, H, S, d), "v_sink": (B, H, S, d)}
+                  "k_sink": (B, H, S, d), "v_sink": (B, H, S, d),
+                  "k_norm": (B, H, d if cfg.key_norm else 0)}
         self.tensors = {}
         for name, shp in shapes.items():
             dt = torch.int32 if packed and name in ("k_scale", "v_scale") else self._DT[name]

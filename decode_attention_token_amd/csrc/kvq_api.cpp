@@ -60,6 +60,9 @@ kvq_status check_config(const kvq_config *c) {
   if (c->meta_format != KVQ_META_F32 && c->meta_format != KVQ_META_F16) return fail(KVQ_ERR_ARG, "unknown meta_format");
   if (c->schedule != KVQ_SCHED_FIXED && c->schedule != KVQ_SCHED_QUEUE) return fail(KVQ_ERR_ARG, "unknown schedule");
   if (c->kernel != KVQ_KERNEL_AUTO && c->kernel != KVQ_KERNEL_VALU) return fail(KVQ_ERR_ARG, "unknown kernel");
+  if (c->key_norm != KVQ_KEYNORM_NONE && c->key_norm != KVQ_KEYNORM_PROMPT) return fail(KVQ_ERR_ARG, "unknown key_norm");
+  if (!iq && c->key_norm != KVQ_KEYNORM_NONE)
+    return fail(KVQ_ERR_UNSUPPORTED, "key normalization is implemented for the InnerQ scheme only");
   if (iq && c->meta_format != KVQ_META_F32)
     return fail(KVQ_ERR_UNSUPPORTED, "compressed metadata is implemented for the KIVI scheme only");
   if (iq && c->v_policy != KVQ_V_FIFO) return fail(KVQ_ERR_ARG, "the InnerQ scheme keeps a FIFO window (v_policy 1)");
@@ -84,6 +87,7 @@ kvq_status check_cache(const kvq_config *c, const kvq_cache *k) {
       (zeros && (!k->k_zero || !k->v_zero)))
     return fail(KVQ_ERR_ARG, "a cache buffer pointer is null");
   if (c->sink_tokens > 0 && (!k->k_sink || !k->v_sink)) return fail(KVQ_ERR_ARG, "a sink buffer pointer is null");
+  if (c->key_norm != KVQ_KEYNORM_NONE && !k->k_norm) return fail(KVQ_ERR_ARG, "the k_norm buffer pointer is null");
   return KVQ_OK;
 }
 
@@ -105,6 +109,7 @@ kvq::CacheView view_of(const kvq_config *c, const kvq_cache *k) {
   v.residual = c->residual;
   v.sinks = c->sink_tokens;
   v.meta = c->meta_format;
+  v.k_norm = c->key_norm != KVQ_KEYNORM_NONE ? k->k_norm : nullptr;
   return v;
 }
 
@@ -174,7 +179,13 @@ kvq_status innerq_prefill(const kvq_config *cfg, kvq_cache *cache, const uint16_
   const int64_t ns = len < S ? len : S;
   const int64_t r = len > S ? (len - S < R ? len - S : R) : 0;
   const int64_t nq = len - r;
-  hipError_t e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, S, k, v, len, 0, (int)ns, 0, units, stream);
+  hipError_t e;
+  if (cv.k_norm != nullptr) {
+    // the per-channel key scales from every prompt token, before any key is quantized
+    e = kvq::launch_key_norm(cache->k_norm, units, k, len, stream);
+    if (e != hipSuccess) return device_error(e, "key channel scales");
+  }
+  e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, S, k, v, len, 0, (int)ns, 0, units, stream);
   if (e != hipSuccess) return device_error(e, "copy sink tokens");
   if (nq > ns) {
     e = kvq::launch_innerq_quantize(cv, units, k, v, len, ns, (int)(nq - ns), ns, stream);
@@ -238,6 +249,7 @@ kvq_status kvq_layout_bytes(const kvq_config *cfg, kvq_layout *out) {
   out->v_resid = out->k_resid;
   out->k_sink = units * (size_t)cfg->sink_tokens * d * 2;
   out->v_sink = out->k_sink;
+  out->k_norm = cfg->key_norm != KVQ_KEYNORM_NONE ? units * d * 4 : 0;
   g_err[0] = 0;
   return KVQ_OK;
 }
@@ -423,7 +435,6 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.n_main = cache->nq_k;
   a.splits = splits;
   a.interleave = 0;
-  a.tail_wg = 0;
   a.resid_main = 1;
   a.nparts = splits;
   a.qscale = softmax_scale * 1.4426950408889634f;
@@ -463,15 +474,13 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.nq_v = nq_v;
   a.n_main = n_main;
   a.nsink = (int)ns;
-  // tokens [n_main, n): all fp16 (chunked residual) -> the last split takes
-  // them; keys quantized but values fp16 (FIFO queue) -> a tail workgroup.
-  // The sink tokens always go to the last split.
+  // tokens [n_main, n) and the sink tokens go to the last split, which reads
+  // each token's key and value quantized or fp16 (a FIFO value queue leaves
+  // keys quantized whose values are still fp16)
   const bool has_rest = n_tokens > n_main;
-  const bool all_fp16 = nq_k == n_main && nq_v == n_main;
-  a.resid_main = (has_rest && all_fp16) ? 1 : 0;
-  a.tail_wg = (has_rest && !all_fp16) ? 1 : 0;
+  a.resid_main = has_rest ? 1 : 0;
   a.splits = n_main > 0 ? splits : ((a.resid_main || ns > 0) ? 1 : 0);
-  a.nparts = a.splits + a.tail_wg;
+  a.nparts = a.splits;
   // Wave order of the vector-ALU kernel: when a wave's contiguous share of
   // its split would span more than 32 KiB of key codes, its waves take
   // every eighth key group instead (measured: 3.6% faster on a 4-bit cache

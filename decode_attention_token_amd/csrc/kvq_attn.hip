@@ -20,10 +20,10 @@
 //
 // Work split.  A workgroup of 8 waves handles one split of one unit (batch,
 // kv head): a contiguous range of the unit's whole key groups.  The last
-// split also takes the fp16 residual tokens when both their keys and values
-// are fp16 (the chunked residual); otherwise (a FIFO value queue leaves keys
-// quantized whose values are still fp16) one extra workgroup per unit runs a
-// plain dequantize-then-dot tail path.  Within a wave, LPT lanes share a
+// split also takes the tokens after the whole groups and the sink tokens,
+// reading each token's key and value either dequantized or fp16 (with a FIFO
+// value queue, keys may be quantized while their values are still fp16).
+// Within a wave, LPT lanes share a
 // token and each owns 128 / LPT channels, so a wave step reads contiguous key
 // and value rows with 8- or 16-byte loads; loads run two steps ahead of the
 // arithmetic through a ring of three register buffers.  Each wave keeps its
@@ -41,8 +41,6 @@
 namespace kvq {
 namespace {
 
-constexpr int kMaxTail = 512 + 127;  // residual <= 512, group <= 128
-
 // ---------------------------------------------------------------- geometry
 template <int BITS, int GS, int HPG, int LPT>
 struct Geo {
@@ -57,16 +55,15 @@ struct Geo {
   static constexpr int RED = kRedFloats<HPG>;
   static constexpr int QPW = HPG * (kHeadDim + 8);                // per wave: q'[HPG][128], beta[HPG][8]
   static constexpr int QP = kWaves * QPW;
-  static constexpr int TAIL = HPG * kMaxTail + kParts * HPG * kHeadDim;
-  static constexpr int WORK = RED > QP ? (RED > TAIL ? RED : TAIL) : (QP > TAIL ? QP : TAIL);
+  static constexpr int WORK = RED > QP ? RED : QP;
   static constexpr int SMEM = WORK + kStageFloats<HPG>;  // floats
 };
 
 // One group's (S, Z) at index idx of a scale / zero-point pair of arrays, in
 // either metadata format.
-__device__ __forceinline__ void group_meta(const float *scale, const int16_t *zero, int64_t idx, int meta,
-                                           float &S, float &Z) {
-  if (meta) {
+template <int META>
+__device__ __forceinline__ void group_meta(const float *scale, const int16_t *zero, int64_t idx, float &S, float &Z) {
+  if constexpr (META) {
     const uint32_t w = reinterpret_cast<const uint32_t *>(scale)[idx];
     S = h2f((uint16_t)(w & 0xffffu));
     Z = (float)(int16_t)(w >> 16);
@@ -76,107 +73,30 @@ __device__ __forceinline__ void group_meta(const float *scale, const int16_t *ze
   }
 }
 
-// ---------------------------------------------------------------- tail path
-// Tokens [n_main, n): keys and values may each be quantized or fp16 per token.
-// Plain dequantize-then-dot: a wave per token for scores, a thread per
-// channel for P.V.
-template <int BITS, int HPG>
-__device__ void decode_tail(const AttnArgs &a, int unit, float *smem, const Stage &st) {
-  constexpr int PER = 32 / BITS;
-  constexpr int W = kHeadDim / PER;
+// ---------------------------------------------------------------- rest tokens
+// Channels c0 .. c0 + CPL - 1 of one token row of the cache, dequantized:
+// x = S * (code + Z) with the (S, Z) of the channel's group.  Keys carry one
+// (S, Z) per (group of GS tokens, channel), values one per (token, group of
+// GS channels).
+template <int BITS, int GS, int CPL, int META>
+__device__ __forceinline__ void dequant_row(const CacheView &c, bool values, int unit, int64_t t, int c0, float *x) {
+  constexpr int PER = 32 / BITS, W = kHeadDim / PER, VGR = kHeadDim / GS;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
-  const int G = a.c.group;
-  const int VGR = kHeadDim / G;
-  const int R = a.c.residual;
-  const int64_t cap = a.c.cap;
-  const int64_t t0 = a.n_main;
-  const int nt = (int)(a.n - a.n_main);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = unit / a.hkv, hk = unit % a.hkv;
-  float *s_sc = smem;                    // [HPG][nt] scores, then weights
-  float *s_half = smem + HPG * nt;       // [kParts][HPG][128]
-
-  float qa[HPG], qb[HPG];
+  const int64_t cap = c.cap;
+  const uint32_t *row = (values ? c.v_codes : c.k_codes) + ((int64_t)unit * cap + t) * W + c0 / PER;
 #pragma unroll
-  for (int h = 0; h < HPG; ++h) {
-    const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * HPG + h)) * kHeadDim + 2 * lane;
-    qa[h] = h2f(qp[0]) * a.qscale;
-    qb[h] = h2f(qp[1]) * a.qscale;
-  }
-  const int c0 = 2 * lane;
-  for (int i = wave; i < nt; i += kWaves) {
-    const int64_t t = t0 + i;
-    float k0, k1;
-    if (t < a.nq_k) {
-      const int64_t g = t / G;
-      const uint32_t word = a.c.k_codes[((int64_t)unit * cap + t) * W + c0 / PER];
-      const int sh = (c0 % PER) * BITS;
-      const int64_t gi = ((int64_t)unit * (cap / G) + g) * kHeadDim + c0;
-      float S0, Z0, S1, Z1;
-      group_meta(a.c.k_scale, a.c.k_zero, gi, a.c.meta, S0, Z0);
-      group_meta(a.c.k_scale, a.c.k_zero, gi + 1, a.c.meta, S1, Z1);
-      k0 = ((float)((word >> sh) & MASK) + Z0) * S0;
-      k1 = ((float)((word >> (sh + BITS)) & MASK) + Z1) * S1;
-    } else {
-      const uint16_t *r = a.c.k_resid + ((int64_t)unit * R + (t % R)) * kHeadDim + c0;
-      k0 = h2f(r[0]);
-      k1 = h2f(r[1]);
-    }
+  for (int w = 0; w < CPL / PER; ++w) {
+    const uint32_t word = row[w];
 #pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      const float d = wave_sum(fmaf(qa[h], k0, qb[h] * k1));
-      if (lane == 0) s_sc[h * nt + i] = d;
-    }
-  }
-  __syncthreads();
-  if (wave < HPG) {
-    const int h = wave;
-    float mx = -INFINITY;
-    for (int i = lane; i < nt; i += kWave) mx = fmaxf(mx, s_sc[h * nt + i]);
-    mx = wave_max(mx);
-    float l = 0.0f;
-    for (int i = lane; i < nt; i += kWave) {
-      const float p = exp2f(s_sc[h * nt + i] - mx);
-      s_sc[h * nt + i] = p;
-      l += p;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      st.ml[2 * h] = nt > 0 ? mx : -INFINITY;
-      st.ml[2 * h + 1] = l;
-    }
-  }
-  __syncthreads();
-  const int c = tid & (kHeadDim - 1);
-  const int half = tid >> 7;
-  float acc[HPG];
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) acc[h] = 0.0f;
-  for (int i = half; i < nt; i += kParts) {
-    const int64_t t = t0 + i;
-    float v;
-    if (t < a.nq_v) {
-      const uint32_t word = a.c.v_codes[((int64_t)unit * cap + t) * W + c / PER];
-      const int64_t gi = ((int64_t)unit * cap + t) * VGR + c / G;
+    for (int e = 0; e < PER; ++e) {
+      const int ch = c0 + w * PER + e;
+      const int64_t idx = values ? ((int64_t)unit * cap + t) * VGR + ch / GS
+                                 : ((int64_t)unit * (cap / GS) + t / GS) * kHeadDim + ch;
       float S, Z;
-      group_meta(a.c.v_scale, a.c.v_zero, gi, a.c.meta, S, Z);
-      v = ((float)((word >> ((c % PER) * BITS)) & MASK) + Z) * S;
-    } else {
-      v = h2f(a.c.v_resid[((int64_t)unit * R + (t % R)) * kHeadDim + c]);
+      group_meta<META>(values ? c.v_scale : c.k_scale, values ? c.v_zero : c.k_zero, idx, S, Z);
+      x[w * PER + e] = S * ((float)((word >> (e * BITS)) & MASK) + Z);
     }
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) acc[h] = fmaf(s_sc[h * nt + i], v, acc[h]);
   }
-#pragma unroll
-  for (int h = 0; h < HPG; ++h) s_half[(half * HPG + h) * kHeadDim + c] = acc[h];
-  __syncthreads();
-  for (int i = tid; i < HPG * kHeadDim; i += blockDim.x) {
-    float t = 0.0f;
-#pragma unroll
-    for (int p = 0; p < kParts; ++p) t += s_half[p * HPG * kHeadDim + i];
-    st.acc[i] = t;
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------- main path
@@ -191,7 +111,10 @@ struct StepBuf {
 };
 
 // META = 1: group metadata as packed words (fp16 S | Z << 16) in *_scale.
-template <int BITS, int GS, int HPG, int LPT, int META>
+// MIXED = 1: some of the tokens after the whole key groups have a quantized
+// key or value (a FIFO value queue), so the rest phase can dequantize rows;
+// the instance without it keeps the registers of the all-fp16 rest phase.
+template <int BITS, int GS, int HPG, int LPT, int META, int MIXED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<HPG>, 8)))
 void decode_attn_kernel(AttnArgs a) {
   using Gm = Geo<BITS, GS, HPG, LPT>;
@@ -208,17 +131,8 @@ void decode_attn_kernel(AttnArgs a) {
   const Stage st = stage_of<HPG>(smem, Gm::WORK);
 
   const int units = a.batch * a.hkv;
-  int blk = blockIdx.x;
-  if (a.tail_wg) {
-    if (blk < units) {
-      decode_tail<BITS, HPG>(a, blk, smem, st);
-      finish_part<HPG>(a, blk, a.splits, st);
-      return;
-    }
-    blk -= units;
-  }
-  const int split = blk / units;
-  const int unit = blk % units;
+  const int split = (int)blockIdx.x / units;
+  const int unit = (int)blockIdx.x % units;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -425,9 +339,12 @@ void decode_attn_kernel(AttnArgs a) {
     }
   }
 
-  // fp16 tokens, in the last split: the sink tokens (rows of k_sink) and,
-  // with the chunked residual, tokens [n_main, n) from the ring.  Same lane
-  // layout, plain query, weights p * U so the final 1/U scaling applies.
+  // The rest of the tokens, in the last split: the sink tokens (rows of
+  // k_sink) and tokens [n_main, n) after the whole key groups, whose keys and
+  // values are each quantized (t < nq_k, t < nq_v: a FIFO value queue leaves
+  // keys quantized whose values are still fp16) or fp16 in the ring.  Same
+  // lane layout, plain query, the keys and values of each token dequantized
+  // or read as fp16, weights p * U so the final 1/U scaling applies.
   const int rcount = a.resid_main ? (int)(a.n - a.n_main) : 0;
   const int nf = a.nsink + rcount;
   if (nf > 0 && split == a.splits - 1) {
@@ -453,19 +370,45 @@ void decode_attn_kernel(AttnArgs a) {
       const int i = rs * TPS + tl;
       const bool valid = i < nf;
       const int ii = valid ? i : 0;
-      const uint16_t *krow, *vrow;
-      if (ii < a.nsink) {
-        const int64_t off = ((int64_t)unit * S + ii) * kHeadDim + j * CPL;
-        krow = a.c.k_sink + off;
-        vrow = a.c.v_sink + off;
-      } else {
-        const int64_t t = a.n_main + (ii - a.nsink);
-        const bool fresh = a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
-        const int64_t slot = t % R;
-        krow = fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + slot * kHeadDim;
-        vrow = fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + slot * kHeadDim;
+      const bool sink = ii < a.nsink;
+      const int64_t t = a.n_main + (ii - a.nsink);             // when not a sink
+      const bool fresh = !sink && a.k_new != nullptr && t == a.n - 1;   // not in the ring yet
+      const int64_t sink_off = ((int64_t)unit * S + ii) * kHeadDim + j * CPL;
+      const int64_t slot = sink ? 0 : t % R;
+      if constexpr (!MIXED) {
+        // all fp16: both rows load together
+        const uint16_t *krow = sink ? a.c.k_sink + sink_off
+                                    : (fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + slot * kHeadDim);
+        const uint16_t *vrow = sink ? a.c.v_sink + sink_off
+                                    : (fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + slot * kHeadDim);
+        fp16_token<HPG, CPL, NVG, LPT>(o, qf, krow, vrow, valid, U);
+        continue;
       }
-      fp16_token<HPG, CPL, NVG, LPT>(o, qf, krow, vrow, valid, U);
+      // keys first, then values, so only one of the rows is live at a time
+      float wt[HPG];
+      {
+        float kf[CPL];
+        if (sink) {
+          fp16_row<CPL>(a.c.k_sink + sink_off, kf);
+        } else if (MIXED && t < a.nq_k) {
+          dequant_row<BITS, GS, CPL, META>(a.c, false, unit, t, j * CPL, kf);
+        } else {
+          fp16_row<CPL>(fresh ? a.k_new + (int64_t)unit * kHeadDim + j * CPL : kr + slot * kHeadDim, kf);
+        }
+        token_weights<HPG, CPL, NVG, LPT>(o, qf, kf, valid, U, wt);
+      }
+      asm volatile("" ::: "memory");
+      {
+        float vf[CPL];
+        if (sink) {
+          fp16_row<CPL>(a.c.v_sink + sink_off, vf);
+        } else if (MIXED && t < a.nq_v) {
+          dequant_row<BITS, GS, CPL, META>(a.c, true, unit, t, j * CPL, vf);
+        } else {
+          fp16_row<CPL>(fresh ? a.v_new + (int64_t)unit * kHeadDim + j * CPL : vr + slot * kHeadDim, vf);
+        }
+        token_values<HPG, CPL, NVG>(o, wt, vf);
+      }
     }
   }
 
@@ -486,8 +429,15 @@ template <int BITS, int GS, int HPG, int META>
 hipError_t launch_kernel(const AttnArgs &a, hipStream_t s) {
   constexpr int LPT = (HPG == 1) ? 4 : (HPG == 2 ? 4 : 8);
   const int units = a.batch * a.hkv;
-  hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META>), dim3(units * (a.splits + a.tail_wg)),
-                     dim3(kThreads), 0, s, a);
+  // tokens after the whole key groups with a quantized key or value
+  const bool mixed = a.resid_main && (a.nq_k > a.n_main || a.nq_v > a.n_main);
+  if (mixed) {
+    hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META, 1>), dim3(units * a.splits), dim3(kThreads), 0,
+                       s, a);
+  } else {
+    hipLaunchKernelGGL((decode_attn_kernel<BITS, GS, HPG, LPT, META, 0>), dim3(units * a.splits), dim3(kThreads), 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 
@@ -536,7 +486,6 @@ hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s) {
   if (a.hq == 4 * a.hkv && a.n_main >= a.c.group && a.splits >= 1 && rest_tokens <= kGqaMaxRest &&
       a.mfma) {
     AttnArgs m = a;
-    m.tail_wg = 0;
     m.resid_main = 0;
     m.nparts = m.splits;
     // the unit's last workgroup merges the split records itself

@@ -406,30 +406,31 @@ struct Online {
   }
 };
 
-// One fp16 token per group of LPT lanes: each lane reads its CPL channels of
-// the key and value rows (16 bytes at a time), scores them against the plain
-// query qf = q * qscale, and adds weight * U * v so that the 1/U scaling of
-// the quantized codes applies to these tokens too.  Lanes of an invalid
-// token score -inf.
-template <int HPG, int CPL, int NVG, int LPT>
-__device__ __forceinline__ void fp16_token(Online<HPG, CPL, NVG> &o, const float (&qf)[HPG][CPL],
-                                           const uint16_t *krow, const uint16_t *vrow, bool valid, float U) {
+// CPL consecutive fp16 values (16 bytes at a time) as floats.
+template <int CPL>
+__device__ __forceinline__ void fp16_row(const uint16_t *row, float *x) {
   static_assert(CPL % 8 == 0, "fp16 rows are read 16 bytes at a time");
-  float kf[CPL], vf[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; i += 8) {
-    const uint4 kk = *reinterpret_cast<const uint4 *>(krow + i);
-    const uint4 vv = *reinterpret_cast<const uint4 *>(vrow + i);
-    const uint32_t kw4[4] = {kk.x, kk.y, kk.z, kk.w};
-    const uint32_t vw4[4] = {vv.x, vv.y, vv.z, vv.w};
+    const uint4 w = *reinterpret_cast<const uint4 *>(row + i);
+    const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kf[i + 2 * e] = h2f((uint16_t)(kw4[e] & 0xffffu));
-      kf[i + 2 * e + 1] = h2f((uint16_t)(kw4[e] >> 16));
-      vf[i + 2 * e] = h2f((uint16_t)(vw4[e] & 0xffffu));
-      vf[i + 2 * e + 1] = h2f((uint16_t)(vw4[e] >> 16));
+      x[i + 2 * e] = h2f((uint16_t)(w4[e] & 0xffffu));
+      x[i + 2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
     }
   }
+}
+
+// One token per group of LPT lanes whose keys and values each lane holds as
+// floats for its CPL channels: scores them against the plain query
+// qf = q * qscale and adds weight * U * v, so that the 1/U scaling of the
+// quantized codes applies to these tokens too.  Lanes of an invalid token
+// score -inf.
+// The weights, wt[h] = weight * U, of one token from its key floats.
+template <int HPG, int CPL, int NVG, int LPT>
+__device__ __forceinline__ void token_weights(Online<HPG, CPL, NVG> &o, const float (&qf)[HPG][CPL], const float *kf,
+                                              bool valid, float U, float *wt) {
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
     float d0 = 0.0f, d1 = 0.0f;
@@ -440,10 +441,36 @@ __device__ __forceinline__ void fp16_token(Online<HPG, CPL, NVG> &o, const float
     }
     float sv = block_sum<LPT>(d0 + d1);
     sv = valid ? sv : -INFINITY;
-    const float wt = o.weight(h, sv) * U;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) o.acc[h][i] = fmaf(wt, vf[i], o.acc[h][i]);
+    wt[h] = o.weight(h, sv) * U;
   }
+}
+
+template <int HPG, int CPL, int NVG>
+__device__ __forceinline__ void token_values(Online<HPG, CPL, NVG> &o, const float *wt, const float *vf) {
+#pragma unroll
+  for (int h = 0; h < HPG; ++h) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) o.acc[h][i] = fmaf(wt[h], vf[i], o.acc[h][i]);
+  }
+}
+
+template <int HPG, int CPL, int NVG, int LPT>
+__device__ __forceinline__ void token_update(Online<HPG, CPL, NVG> &o, const float (&qf)[HPG][CPL], const float *kf,
+                                             const float *vf, bool valid, float U) {
+  float wt[HPG];
+  token_weights<HPG, CPL, NVG, LPT>(o, qf, kf, valid, U, wt);
+  token_values<HPG, CPL, NVG>(o, wt, vf);
+}
+
+// One fp16 token per group of LPT lanes (rows krow, vrow: this lane's CPL
+// channels).
+template <int HPG, int CPL, int NVG, int LPT>
+__device__ __forceinline__ void fp16_token(Online<HPG, CPL, NVG> &o, const float (&qf)[HPG][CPL],
+                                           const uint16_t *krow, const uint16_t *vrow, bool valid, float U) {
+  float kf[CPL], vf[CPL];
+  fp16_row<CPL>(krow, kf);
+  fp16_row<CPL>(vrow, vf);
+  token_update<HPG, CPL, NVG, LPT>(o, qf, kf, vf, valid, U);
 }
 
 // Sum over the token lanes of one 16-lane row that share channel slice j

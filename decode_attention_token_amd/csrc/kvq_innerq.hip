@@ -35,9 +35,18 @@ namespace {
 // float64 in channel order (|mean| < std / 10, population std).  Symmetric:
 // S = max|x| / (2^(b-1) - 1) (1 for an all-zero group), Z = -2^(b-1), codes
 // clamp(rint(x / S) - Z, 1, 2^b - 1).  Asymmetric: the KIVI group map.
+// A key divided by its channel scale and rounded to fp16 (round to nearest
+// even), returned as a float.  The scale is a power of two 2^e, so the
+// quotient is the exact product with 2^-e, whose bits are those of the scale
+// subtracted from 0x7F000000 (biased exponent 254 - (e + 127)).
+__device__ __forceinline__ float normalized_key(float x, float lam) {
+  return __half2float(__float2half_rn(x * __uint_as_float(0x7F000000u - __float_as_uint(lam))));
+}
+
+// lam: the G channels' key scales, or null (no normalization).
 template <int BITS>
 __device__ __forceinline__ void quantize_group_hybrid(const uint16_t *x, int G, uint32_t *codes, float *scale,
-                                                      int16_t *zero) {
+                                                      int16_t *zero, const float *lam) {
   constexpr int PER = 32 / BITS;
   constexpr float QMAX = float((1 << BITS) - 1);
   constexpr float QM = float((1 << (BITS - 1)) - 1);
@@ -48,6 +57,10 @@ __device__ __forceinline__ void quantize_group_hybrid(const uint16_t *x, int G, 
     float v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+    if (lam != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] = normalized_key(v[k], lam[k0 + k]);
+    }
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       mn = fminf(mn, v[k]);
@@ -75,6 +88,10 @@ __device__ __forceinline__ void quantize_group_hybrid(const uint16_t *x, int G, 
     float v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) load8(x + k0 + 8 * q, v + 8 * q);
+    if (lam != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] = normalized_key(v[k], lam[k0 + k]);
+    }
     uint32_t cd[32];
     codes_of<32>(v, p, lo, QMAX, cd);
     uint32_t words[32 / PER];
@@ -103,7 +120,8 @@ __device__ __forceinline__ void quantize_into(const CacheView &c, bool values, c
   uint32_t *codes = (values ? c.v_codes : c.k_codes) + row * W + j * (G / PER);
   float *scale = (values ? c.v_scale : c.k_scale) + row * NG + j;
   int16_t *zero = (values ? c.v_zero : c.k_zero) + row * NG + j;
-  quantize_group_hybrid<BITS>(x, G, codes, scale, zero);
+  const float *lam = (!values && c.k_norm != nullptr) ? c.k_norm + (row / c.cap) * kHeadDim + j * G : nullptr;
+  quantize_group_hybrid<BITS>(x, G, codes, scale, zero, lam);
 }
 
 // One wave quantizes a block of 32 consecutive rows of the flattened
@@ -166,6 +184,20 @@ __global__ __launch_bounds__(256) void innerq_quantize_kernel(CacheView c, const
       int u, t;
       locate(r, u, t);
       raw[i] = *(reinterpret_cast<const uint4 *>(src + ((int64_t)u * src_rows + src_row0 + t) * kHeadDim) + cs);
+      if (!values && c.k_norm != nullptr) {
+        // keys of normalized caches: times 1 / scale of their channels (a
+        // power of two, exact in fp16 down to 2^-16; its bits as in
+        // normalized_key), one fp16 rounding
+        const float4 l0 = reinterpret_cast<const float4 *>(c.k_norm + (int64_t)u * kHeadDim + 8 * cs)[0];
+        const float4 l1 = reinterpret_cast<const float4 *>(c.k_norm + (int64_t)u * kHeadDim + 8 * cs)[1];
+        auto inv = [](float l) { return (_Float16)__uint_as_float(0x7F000000u - __float_as_uint(l)); };
+        const f16x2 f0 = {inv(l0.x), inv(l0.y)};
+        const f16x2 f1 = {inv(l0.z), inv(l0.w)};
+        const f16x2 f2 = {inv(l1.x), inv(l1.y)};
+        const f16x2 f3 = {inv(l1.z), inv(l1.w)};
+        raw[i] = make_uint4(as_u32(as_h2(raw[i].x) * f0), as_u32(as_h2(raw[i].y) * f1), as_u32(as_h2(raw[i].z) * f2),
+                            as_u32(as_h2(raw[i].w) * f3));
+      }
     }
   }
   uint16_t *tile = s_tile[wave];
@@ -279,6 +311,57 @@ __global__ __launch_bounds__(256) void innerq_quantize_kernel(CacheView c, const
   }
 }
 
+// Key channel scales.  norm is first filled with 1; then each workgroup
+// takes kNormRows rows of one unit's prompt keys: thread t owns channels
+// 8 (t % 16) .. + 7 of rows t / 16 + 16 i and keeps their largest magnitude
+// as an fp16 bit pattern (the order of non-negative fp16 patterns is that of
+// their values), the 16 row-threads of a channel combine through LDS, and
+// the channel's scale, the smallest power of two >= max(1, max-abs), goes to
+// norm with an atomic maximum on its bit pattern (an order-preserving map for
+// positive floats), so the chunks of a unit combine in any order.
+constexpr int kNormRows = 1024;
+
+__global__ __launch_bounds__(256) void fill_ones_kernel(float *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 1.0f;
+}
+
+__global__ __launch_bounds__(256) void key_norm_kernel(float *__restrict__ norm, const uint16_t *__restrict__ k,
+                                                       int64_t len) {
+  __shared__ uint32_t s_max[16][kHeadDim];
+  const int u = blockIdx.y, ch = blockIdx.x;
+  const int t = threadIdx.x, cs = t & 15, r0 = t >> 4;
+  const int64_t rb = (int64_t)ch * kNormRows;
+  const int64_t re = len < rb + kNormRows ? len : rb + kNormRows;
+  const uint16_t *base = k + (int64_t)u * len * kHeadDim + 8 * cs;
+  uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  for (int64_t r = rb + r0; r < re; r += 16) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(base + r * kHeadDim);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = ws[e] & 0x7fffu, hi = (ws[e] >> 16) & 0x7fffu;
+      m[2 * e] = m[2 * e] > lo ? m[2 * e] : lo;
+      m[2 * e + 1] = m[2 * e + 1] > hi ? m[2 * e + 1] : hi;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_max[r0][8 * cs + e] = m[e];
+  __syncthreads();
+  if (t < kHeadDim) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mb = mb > s_max[r][t] ? mb : s_max[r][t];
+    const float amax = h2f((uint16_t)mb);
+    float lam = 1.0f;
+    if (amax > 1.0f) {
+      const uint32_t bits = __float_as_uint(amax);
+      lam = (bits & 0x7fffffu) == 0 ? amax : __uint_as_float((bits & 0x7f800000u) + 0x00800000u);
+    }
+    atomicMax(reinterpret_cast<unsigned int *>(norm) + (int64_t)u * kHeadDim + t, __float_as_uint(lam));
+  }
+}
+
 // One workgroup (one wave) per unit.  When pop_row >= 0 the window is full:
 // the oldest window token (ring slot pop_row mod R) is quantized into cache
 // row pop_row first.  Then the new key and value rows are written into row
@@ -365,14 +448,29 @@ void innerq_attn_kernel(AttnArgs a) {
 
   // query slice of this lane, in log2 units and divided by the unpack scale,
   // and its plain sum (the zero-point term of the lane's group)
+  // With key scales (normalized keys) the query carries them: q_c * lambda_c
+  // (powers of two, so exact), for the quantized keys only.
   float qf[HPG][CPL], qsum[HPG];
+  float lam[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) lam[i] = 1.0f;
+  if (a.c.k_norm != nullptr) {
+#pragma unroll
+    for (int i = 0; i < CPL; i += 4) {
+      const float4 l4 = *reinterpret_cast<const float4 *>(a.c.k_norm + (int64_t)unit * kHeadDim + j * CPL + i);
+      lam[i] = l4.x;
+      lam[i + 1] = l4.y;
+      lam[i + 2] = l4.z;
+      lam[i + 3] = l4.w;
+    }
+  }
 #pragma unroll
   for (int h = 0; h < HPG; ++h) {
     const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * HPG + h)) * kHeadDim + j * CPL;
     qsum[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const float qv = h2f(qp[i]) * a.qscale;
+      const float qv = h2f(qp[i]) * a.qscale * lam[i];
       qsum[h] += qv;
       qf[h][i] = qv * INV_U;
     }
@@ -479,8 +577,10 @@ void innerq_attn_kernel(AttnArgs a) {
     const int nf = (int)(nsink + (a.n - nq));
 #pragma unroll
     for (int h = 0; h < HPG; ++h) {
+      // plain query: the fp16 keys keep their original units
+      const uint16_t *qp = a.q + ((int64_t)(b * a.hq + hk * HPG + h)) * kHeadDim + j * CPL;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) qf[h][i] *= U;   // back to q * qscale
+      for (int i = 0; i < CPL; ++i) qf[h][i] = h2f(qp[i]) * a.qscale;
     }
     for (int rs = wave; rs * TPS < nf; rs += kWaves) {
       const int i = rs * TPS + tl;
@@ -557,6 +657,16 @@ hipError_t launch_innerq_quantize(const CacheView &c, int units, const uint16_t 
     else KVQ_IQQ(4, 128);
   }
 #undef KVQ_IQQ
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norm(float *norm, int units, const uint16_t *k, int64_t len, hipStream_t s) {
+  const int n = units * kHeadDim;
+  hipLaunchKernelGGL(fill_ones_kernel, dim3((n + 255) / 256), dim3(256), 0, s, norm, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || len == 0) return e;
+  const int chunks = (int)((len + kNormRows - 1) / kNormRows);
+  hipLaunchKernelGGL(key_norm_kernel, dim3(chunks, units), dim3(256), 0, s, norm, k, len);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct CacheView {
   int bits, group, residual;
   int sinks;        // sink tokens kept fp16 (0 = none)
   int meta;         // 0: fp32 scale + int16 zero; 1: packed fp16 scale | zero << 16 in *_scale
+  const float *k_norm;   // InnerQ key channel scales [unit][128] (powers of two), or null
 };
 
 // Quantize `ngroups` key groups per unit.  Source rows: src + (unit * src_rows
@@ -76,6 +77,11 @@ hipError_t launch_innerq_quantize(const CacheView &c, int units, const uint16_t 
                                   int64_t src_rows, int64_t src_row0, int count, int64_t dst_row0,
                                   hipStream_t s);
 
+// Key channel scales of the prompt: norm[u][c] = smallest power of two
+// >= max(1, max over rows [0, len) of |k[u][row][c]|) (two launches: a fill
+// with 1, then an atomic maximum per (unit, channel) over row chunks).
+hipError_t launch_key_norm(float *norm, int units, const uint16_t *k, int64_t len, hipStream_t s);
+
 // InnerQ-style append: if pop_row >= 0, quantize ring slot pop_row mod R into
 // cache row pop_row; then store k_new / v_new ([unit][128]) into row `slot`
 // of the sink rows (to_sink) or of the ring.
@@ -94,12 +100,12 @@ struct AttnArgs {
   int batch, hq, hkv;
   int64_t n, nq_k, nq_v;
   int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups
-  int splits;            // workgroups per unit over [0, n_main) (>= 1 when resid_main)
+  int splits;            // workgroups per unit over [0, n_main) (>= 1 when resid_main or sinks)
   int interleave;        // KIVI vector-ALU kernel: waves take every eighth key group of their
                          // split instead of a contiguous eighth
-  int tail_wg;           // 1: an extra workgroup per unit runs the mixed tail [n_main, n)
-  int resid_main;        // 1: [n_main, n) is all-fp16 and the last split takes it
-  int nparts;            // splits + tail_wg; 1 means the kernel writes out directly
+  int resid_main;        // 1: the last split takes tokens [n_main, n) (keys and values each
+                         // quantized or fp16 per token)
+  int nparts;            // parts per unit (== splits); 1 means the kernel writes out directly
   int nsink;             // KIVI: fp16 sink tokens present (rows of c.k_sink); counters above
                          // then count the tokens after them
   float qscale;          // softmax_scale * log2(e)

@@ -66,6 +66,7 @@
  *   k_resid, v_resid f16 [U][R][head_dim]  recent-token window, token t in
  *                                  slot t mod R
  *   k_sink, v_sink   f16 [U][sink_tokens][head_dim]  token t < sink_tokens
+ *   k_norm  f32 [U][head_dim]      per-channel key scale (KVQ_KEYNORM_PROMPT)
  *   Quantized tokens are those in [sink_tokens, nq); a symmetric group stores
  *   the signed level k as code k + 2^(bits-1) with Z = -2^(bits-1), so
  *   S * (code + Z) dequantizes both modes.
@@ -136,6 +137,20 @@ typedef enum { KVQ_SCHED_FIXED = 0, KVQ_SCHED_QUEUE = 1 } kvq_schedule;
  *   other head ratio uses (kept for comparison).  Ignored elsewhere. */
 typedef enum { KVQ_KERNEL_AUTO = 0, KVQ_KERNEL_VALU = 1 } kvq_kernel;
 
+/* One-time per-channel key normalization ([InnerQ] methodology 4: the key
+ * matrix is scaled once per channel at prefill and the scale folded into the
+ * query).  KVQ_KEYNORM_NONE (default): keys are quantized as they are.
+ * KVQ_KEYNORM_PROMPT (InnerQ scheme only): prefill sets
+ *     k_norm[u][c] = smallest power of two >= max(1, max over the prompt's
+ *                    keys of unit u of |k[c]|)
+ * (one scale per (batch, kv head) and channel, fixed for the life of the
+ * cache); every key that is quantized, at prefill or when it leaves the
+ * window, is first multiplied by 1 / k_norm and rounded to fp16 (round to
+ * nearest even); sink and window keys stay as they are; attention multiplies
+ * the query by k_norm for the quantized keys, so the scores are those of the
+ * keys in their original units. */
+typedef enum { KVQ_KEYNORM_NONE = 0, KVQ_KEYNORM_PROMPT = 1 } kvq_key_norm;
+
 /* Cache configuration: nbits / group_size / residual_length of [HFQ] 4.1
  * plus the attention shape, the scheme and two launch choices (schedule,
  * kernel; zero selects the defaults).  Constraints: bits in {2,4};
@@ -159,13 +174,14 @@ typedef struct {
   int32_t meta_format;  /* kvq_meta_format */
   int32_t schedule;     /* kvq_schedule (0 = fixed order, bit-identical reruns) */
   int32_t kernel;       /* kvq_kernel (0 = matrix cores for four query heads per kv head) */
+  int32_t key_norm;     /* kvq_key_norm (0 = none) */
 } kvq_config;
 
 /* Byte sizes of the caller-allocated device buffers of one cache (k_sink and
  * v_sink are 0 unless sink_tokens > 0; k_zero and v_zero are 0 with
- * KVQ_META_F16). */
+ * KVQ_META_F16; k_norm is 0 unless key_norm is set). */
 typedef struct {
-  size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, k_sink, v_sink;
+  size_t k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, k_sink, v_sink, k_norm;
 } kvq_layout;
 
 /* One layer's cache: caller-owned device buffers (sized by kvq_layout_bytes)
@@ -193,6 +209,8 @@ typedef struct {
   int32_t started;
   int32_t flushes;      /* KIVI: key-residual flushes since prefill; InnerQ:
                            appends that quantized a token leaving the window */
+  float *k_norm;        /* device f32 [U][head_dim], written by prefill; only
+                           with key_norm (may be null otherwise) */
 } kvq_cache;
 
 /* Validates cfg and fills *out with the buffer sizes.  Host only. */

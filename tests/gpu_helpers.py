@@ -56,8 +56,8 @@ def make_cache(bits, G, R, B, Hq, Hkv, cap, policy=kvq.KVQ_V_CHUNK, d=128, sinks
     return cfg, kvq.KVCache(cfg, "cuda")
 
 
-def make_innerq_cache(bits, G, R, S, B, Hq, Hkv, cap, d=128):
-    cfg = kvq.make_innerq_config(bits, G, R, S, B, Hq, Hkv, d, cap)
+def make_innerq_cache(bits, G, R, S, B, Hq, Hkv, cap, d=128, key_norm=kvq.KVQ_KEYNORM_NONE):
+    cfg = kvq.make_innerq_config(bits, G, R, S, B, Hq, Hkv, d, cap, key_norm)
     return cfg, kvq.KVCache(cfg, "cuda")
 
 
@@ -93,6 +93,9 @@ def compare_innerq_unit(cache, ref, b, h, rb=None, rh=None):
         if slots:
             got = host(T[name][b, h][slots]).view(np.uint16)
             assert np.array_equal(got, bufs[name][rb, rh][slots].view(np.uint16)), name
+    if "k_norm" in bufs:
+        got = host(T["k_norm"][b, h])
+        assert np.array_equal(got, bufs["k_norm"][rb, rh]), f"k_norm unit ({b},{h}): {got} vs {bufs['k_norm'][rb, rh]}"
 
 
 def compare_innerq_buffers(cache, ref):

@@ -65,7 +65,8 @@ int main(void) {
   printf("kvq_config %zu\nkvq_layout %zu\nkvq_cache %zu\n", sizeof(kvq_config), sizeof(kvq_layout),
          sizeof(kvq_cache));
   F(kvq_config, scheme) F(kvq_config, sink_tokens) F(kvq_layout, k_sink) F(kvq_layout, v_sink)
-  F(kvq_config, meta_format) F(kvq_config, schedule) F(kvq_config, kernel)
+  F(kvq_config, meta_format) F(kvq_config, schedule) F(kvq_config, kernel) F(kvq_config, key_norm)
+  F(kvq_layout, k_norm) F(kvq_cache, k_norm)
   F(kvq_cache, k_sink) F(kvq_cache, v_sink) F(kvq_cache, n_tokens) F(kvq_cache, flushes)
   return 0;
 }

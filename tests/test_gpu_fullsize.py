@@ -22,14 +22,16 @@ def _sample_units(w, k=6, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("w", [LLAMA7B_2BIT, LLAMA7B_4BIT, GQA_LONG, LONG_4BIT], ids=lambda w: w.name)
-def test_fullsize_sampled_parity(w):
-    print(f"workload {w.name}", flush=True)
+@pytest.mark.parametrize("w,key_norm", [(LLAMA7B_2BIT, 0), (LLAMA7B_4BIT, 0), (GQA_LONG, 0), (LONG_4BIT, 0),
+                                        (LONG_4BIT, 1)],
+                         ids=lambda x: x.name if hasattr(x, "name") else ("key-norm" if x else "plain"))
+def test_fullsize_sampled_parity(w, key_norm):
+    print(f"workload {w.name} key_norm={key_norm}", flush=True)
     k, v = gen_prefill(w, 0, "cuda")
     kn, vn = gen_new_tokens(w, 0, "cuda", steps=1)
     q = gen_queries(w, 0, "cuda", steps=1)[0].contiguous()
     cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim, w.max_tokens, w.v_policy, w.scheme, w.sinks)
+                          w.head_dim, w.max_tokens, w.v_policy, w.scheme, w.sinks, key_norm=key_norm)
     cache = kvq.KVCache(cfg, "cuda")
     cache.prefill(k, v)
     cache.append(kn[0].contiguous(), vn[0].contiguous())
@@ -41,7 +43,7 @@ def test_fullsize_sampled_parity(w):
     for u in _sample_units(w):
         b, h = divmod(u, w.num_kv_heads)
         if w.scheme == kvq.KVQ_SCHEME_INNERQ:
-            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, key_norm=bool(key_norm))
         else:
             ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
         ref.prefill(host(k[b:b + 1, h:h + 1]), host(v[b:b + 1, h:h + 1]))

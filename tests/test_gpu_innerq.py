@@ -155,3 +155,47 @@ def test_innerq_decode_step_matches_append_then_attention():
         assert torch.equal(oa, ob), i
     assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
     compare_innerq_buffers(a, ref)
+
+
+# One-time per-channel key scales (KVQ_KEYNORM_PROMPT): the scales, the
+# normalized quantized keys and the window are bit-exact, attention within
+# 2e-3.  Case 204 takes its scales from a 2-token prompt and quantizes later
+# keys with them; 209 appends keys 50x beyond the prompt's range.
+NORM_CASES = [
+    (CASES[0][0], [1, 2, 40]),
+    (CASES[1][0], [1, 20]),
+    (CASES[3][0], [1, 2, 3, 10, 11, 20]),
+    (CASES[7][0], [1, 2]),
+    (_w(209, 2, 4, 4, 300, 4, 64, 32, 4, 40, 4, 3.0), [1, 40]),
+]
+
+
+@pytest.mark.parametrize("w,checks", NORM_CASES, ids=[c[0].name + "-norm" for c in NORM_CASES])
+def test_innerq_key_norm_parity(w, checks):
+    print(f"case {w.name} with key scales", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    if w.config_id == 209:
+        kn = (kn.float() * 50).clamp(-60000, 60000).half()
+    qs = gen_queries(w, 0, "cuda")
+    cfg, cache = make_innerq_cache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_q_heads, w.num_kv_heads,
+                                   w.max_tokens, key_norm=kvq.KVQ_KEYNORM_PROMPT)
+    ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_kv_heads, 128, key_norm=True)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    torch.cuda.synchronize()
+    compare_innerq_buffers(cache, ref)
+    assert float(ref.k_norm.max()) > 1.0 or w.context <= w.sinks, "the scales must matter on this input"
+    scale = 1.0 / math.sqrt(128)
+    ws = cache.workspace()
+    for step in range(1, w.steps + 1):
+        cache.append(kn[step - 1].contiguous(), vn[step - 1].contiguous())
+        ref.append(host(kn[step - 1]), host(vn[step - 1]))
+        if step in checks:
+            q = qs[step - 1].contiguous()
+            out = cache.attention(q, scale, workspace=ws)
+            torch.cuda.synchronize()
+            compare_innerq_buffers(cache, ref)
+            err = max_err(out, oracle_attention(ref, host(q), scale))
+            print(f"  step {step}: n={ref.n} nq={ref.nq} err={err:.2e}", flush=True)
+            assert err <= ATOL

@@ -114,16 +114,17 @@ def test_kivi_quantizer_edge_groups(bits, G, policy, meta):
     assert ref.flushes == 2
 
 
+@pytest.mark.parametrize("key_norm", [0, 1])
 @pytest.mark.parametrize("bits,G", [(4, 64), (2, 32)])
-def test_innerq_quantizer_edge_groups(bits, G):
+def test_innerq_quantizer_edge_groups(bits, G, key_norm):
     H, S, R, L, A = 2, 4, 16, 100, 40
-    print(f"case InnerQ bits={bits} G={G}", flush=True)
+    print(f"case InnerQ bits={bits} G={G} key_norm={key_norm}", flush=True)
     T = L + A
     K = _planted(bits, G, H, T, 300 + bits, False)
     V = _planted(bits, G, H, T, 400 + bits, False)
-    cfg = kvq.make_innerq_config(bits, G, R, S, 1, H, H, D, T + 8)
+    cfg = kvq.make_innerq_config(bits, G, R, S, 1, H, H, D, T + 8, key_norm)
     cache = kvq.KVCache(cfg, "cuda")
-    ref = oracle.InnerQCache(bits, G, R, S, 1, H, D)
+    ref = oracle.InnerQCache(bits, G, R, S, 1, H, D, key_norm=bool(key_norm))
     cache.prefill(_dev(K[:, :, :L]), _dev(V[:, :, :L]))
     ref.prefill(K[:, :, :L], V[:, :, :L])
     torch.cuda.synchronize()
