@@ -619,8 +619,9 @@ def main():
         del src, dst
 
     # a decode step is one launch for the KIVI scheme with chunked values
-    # (no flush due); otherwise it is an append launch plus the attention
-    # launch, and the roofline takes the attention launch alone
+    # (no flush due); a FIFO value queue adds the small launch that quantizes
+    # the popped value, and InnerQ appends in a launch of its own: there the
+    # roofline takes the attention launch alone
     one_launch = w.scheme == kvq.KVQ_SCHEME_KIVI and w.v_policy == kvq.KVQ_V_CHUNK
     if fused_us is not None and one_launch:
         roof_us, roof_bytes, roof_launch = fused_us, fused_bytes, "fused decode step (kvq_decode_step)"

@@ -53,6 +53,7 @@ class kvq_cache(ctypes.Structure):
         ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
         ("n_tokens", ctypes.c_int64), ("nq_k", ctypes.c_int64), ("nq_v", ctypes.c_int64),
         ("started", ctypes.c_int32), ("flushes", ctypes.c_int32), ("k_norm", ctypes.c_void_p),
+        ("prequant", ctypes.c_int64),
     ]
 
 

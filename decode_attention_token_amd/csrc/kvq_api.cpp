@@ -197,6 +197,7 @@ kvq_status innerq_prefill(const kvq_config *cfg, kvq_cache *cache, const uint16_
   cache->nq_k = cache->nq_v = nq;
   cache->started = 1;
   cache->flushes = 0;
+  cache->prequant = 0;
   return KVQ_OK;
 }
 
@@ -207,10 +208,14 @@ kvq_status innerq_append(const kvq_config *cfg, kvq_cache *cache, const uint16_t
   const int64_t n = cache->n_tokens, nq = cache->nq_k;
   const bool to_sink = n < S;
   const bool pop = !to_sink && n - nq == R;
-  const hipError_t e = kvq::launch_innerq_append(view_of(cfg, cache), units, k_new, v_new, pop ? nq : -1, to_sink,
-                                                 (int)(to_sink ? n : n % R), stream);
+  // a decode step may have quantized the leaving token's rows already
+  const bool ready = cache->prequant == nq + 1;
+  const hipError_t e = kvq::launch_innerq_append(view_of(cfg, cache), units, k_new, v_new,
+                                                 (pop && !ready) ? nq : -1, to_sink, (int)(to_sink ? n : n % R),
+                                                 stream);
   if (e != hipSuccess) return device_error(e, "append");
   cache->n_tokens = n + 1;
+  cache->prequant = 0;
   if (to_sink) {
     cache->nq_k = cache->nq_v = n + 1;
   } else if (pop) {
@@ -320,6 +325,7 @@ kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache, const u
   cache->nq_v = ns + nq_v;
   cache->started = 1;
   cache->flushes = 0;
+  cache->prequant = 0;
   g_err[0] = 0;
   return KVQ_OK;
 }
@@ -357,10 +363,14 @@ kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache, const uint1
   // FIFO: the value queue would exceed R, so quantize its oldest entry before
   // its ring slot (the same slot the new token takes) is overwritten
   if (cfg->v_policy == KVQ_V_FIFO && (n + 1) - nq_v > R) {
-    e = kvq::launch_quantize_values(cv, units, cache->v_resid, R, nq_v % R, 1, nq_v, stream);
-    if (e != hipSuccess) return device_error(e, "quantize popped value");
+    // (unless a decode step has quantized that row already)
+    if (cache->prequant != S + nq_v + 1) {
+      e = kvq::launch_quantize_values(cv, units, cache->v_resid, R, nq_v % R, 1, nq_v, stream);
+      if (e != hipSuccess) return device_error(e, "quantize popped value");
+    }
     nq_v += 1;
   }
+  cache->prequant = 0;
   if (cfg->v_policy == KVQ_V_CHUNK && (n + 1) - nq_k == R && nq_v == nq_k) {
     // both rings fill with this token: one launch quantizes them, reading the
     // new token from k_new / v_new; no ring slot is live afterwards
@@ -413,9 +423,10 @@ kvq_status check_attention_args(const kvq_config *cfg, const kvq_cache *cache, c
 
 // Enqueues attention over a cache of n_tokens tokens; with k_new/v_new the
 // last token is taken from them and stored into its residual slot.
-kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *q,
-                                   float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-                                   int32_t splits, hipStream_t stream) {
+kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache, const uint16_t *k_new,
+                                   const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
+                                   void *workspace, size_t workspace_bytes, int32_t splits, int64_t prequant,
+                                   hipStream_t stream) {
   const int64_t n = cache->n_tokens;
   const int64_t first = n < cfg->sink_tokens ? n : cfg->sink_tokens;
   if (splits == 0) splits = auto_splits_for(cfg, cache->nq_k - first);
@@ -438,18 +449,24 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.resid_main = 1;
   a.nparts = splits;
   a.qscale = softmax_scale * 1.4426950408889634f;
-  a.k_new = a.v_new = nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.prequant = prequant;
   a.nsink = 0;   // the InnerQ kernel derives its sinks from n and the config
   const hipError_t e = kvq::launch_innerq_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
   return KVQ_OK;
 }
 
+// prequant: token (whole-stream index) whose quantized row(s) the launch
+// writes ahead of its pop, or -1.
 kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64_t n_tokens, const uint16_t *k_new,
                             const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
-                            void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream) {
+                            void *workspace, size_t workspace_bytes, int32_t splits, int64_t prequant,
+                            hipStream_t stream) {
   if (is_innerq(cfg))
-    return launch_innerq_attention(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
+    return launch_innerq_attention(cfg, cache, k_new, v_new, q, softmax_scale, out, workspace, workspace_bytes,
+                                   splits, prequant, stream);
   // sink tokens [0, ns) are fp16; everything else is indexed from the first
   // token after them
   const int64_t ns = n_tokens < cfg->sink_tokens ? n_tokens : cfg->sink_tokens;
@@ -491,6 +508,7 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.prequant = prequant >= 0 ? prequant - ns : -1;
   hipError_t e = kvq::launch_decode_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
   return KVQ_OK;
@@ -509,7 +527,7 @@ kvq_status decode_attention_into(const kvq_config *cfg, const kvq_cache *cache, 
   if (s != KVQ_OK) return s;
   if (cache->n_tokens < 1) return fail(KVQ_ERR_STATE, "attention over an empty cache");
   s = launch_attention(cfg, cache, cache->n_tokens, nullptr, nullptr, q, softmax_scale, out, workspace,
-                       workspace_bytes, splits, stream);
+                       workspace_bytes, splits, -1, stream);
   if (s == KVQ_OK) g_err[0] = 0;
   return s;
 }
@@ -531,22 +549,60 @@ kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16
   if (s != KVQ_OK) return s;
   if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new or v_new is null");
   if (cache->n_tokens >= cfg->max_tokens) return fail(KVQ_ERR_CAPACITY, "cache is full (%d tokens)", cfg->max_tokens);
-  const int R = cfg->residual;
+  const int R = cfg->residual, S = cfg->sink_tokens;
   const int64_t n1 = cache->n_tokens + 1;
-  // one launch when the append needs no flush or queue pop and the residual
-  // is the chunked all-fp16 kind; otherwise the two calls in sequence
-  const bool fused = !is_innerq(cfg) && cfg->v_policy == KVQ_V_CHUNK && cache->n_tokens >= cfg->sink_tokens &&
-                     cache->nq_k == cache->nq_v && n1 - cache->nq_k < R;
+  const size_t need = workspace_for(cfg, splits == 0 ? kvq_auto_splits(cfg, n1) : splits);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  // The attention launch also takes the new token from k_new / v_new and
+  // stores it into its ring slots when the new token is not a sink and (KIVI)
+  // the append quantizes no key group.  A token that leaves a FIFO value
+  // queue or the InnerQ window is quantized ahead: the step that fills the
+  // queue or window has its attention launch write the oldest token's
+  // quantized rows (cache->prequant records which), so in steady state a
+  // step is one launch.  Without that, one small launch quantizes it first.
+  // Otherwise the two calls in sequence.
+  const bool iq = is_innerq(cfg);
+  const bool fifo = iq || cfg->v_policy == KVQ_V_FIFO;
+  const bool fused = cache->n_tokens >= S &&
+                     (iq || ((fifo || cache->nq_k == cache->nq_v) && n1 - cache->nq_k < R));
   if (!fused) {
-    const size_t need = workspace_for(cfg, splits == 0 ? kvq_auto_splits(cfg, n1) : splits);
-    if (workspace_bytes < need)
-      return fail(KVQ_ERR_CAPACITY, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
     s = kvq_append_token(cfg, cache, k_new, v_new, stream);
     if (s != KVQ_OK) return s;
     return kvq_decode_attention(cfg, cache, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
   }
-  s = launch_attention(cfg, cache, n1, k_new, v_new, q, softmax_scale, out, workspace, workspace_bytes, splits, stream);
+  const int units = cfg->batch * cfg->num_kv_heads;
+  const kvq::CacheView cv = view_of(cfg, cache);
+  int64_t nq_k = cache->nq_k, nq_v = cache->nq_v;
+  int32_t flushes = cache->flushes;
+  if (fifo && n1 - nq_v > R) {
+    // the oldest fp16 value (InnerQ: token) leaves
+    if (cache->prequant != nq_v + 1) {
+      const hipError_t e = iq ? kvq::launch_innerq_append(cv, units, nullptr, nullptr, nq_v, false, 0, stream)
+                              : kvq::launch_quantize_values(cv, units, cache->v_resid, R, (nq_v - S) % R, 1, nq_v - S,
+                                                            stream);
+      if (e != hipSuccess) return device_error(e, "quantize the token leaving the residual");
+    }
+    nq_v += 1;
+    if (iq) {
+      nq_k = nq_v;
+      flushes += 1;
+    }
+  }
+  // after this step the queue or window is full: its oldest token leaves at
+  // the next append (the ring slot differs from the new token's, R >= 2)
+  const int64_t pre = (fifo && R >= 2 && n1 - nq_v == R) ? nq_v : -1;
+  kvq_cache next = *cache;
+  next.n_tokens = n1;
+  next.nq_k = nq_k;
+  next.nq_v = nq_v;
+  s = launch_attention(cfg, &next, n1, k_new, v_new, q, softmax_scale, out, workspace, workspace_bytes, splits, pre,
+                       stream);
   if (s != KVQ_OK) return s;
+  cache->nq_k = nq_k;
+  cache->nq_v = nq_v;
+  cache->flushes = flushes;
+  cache->prequant = pre >= 0 ? pre + 1 : 0;
   cache->n_tokens = n1;
   g_err[0] = 0;
   return KVQ_OK;

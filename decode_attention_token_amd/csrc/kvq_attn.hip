@@ -37,6 +37,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_attn_common.h"
+#include "kvq_quant_common.h"
 
 namespace kvq {
 namespace {
@@ -414,6 +415,13 @@ void decode_attn_kernel(AttnArgs a) {
 
   combine_waves<HPG, LPT, NVG>(o, smem, st, wave, lane, INV_U);
   finish_part<HPG>(a, unit, split, st);
+  if (a.prequant >= 0 && split == 0 && wave == kWaves - 1) {
+    // a full FIFO queue: its oldest value row is quantized now, ahead of the
+    // next append's pop
+    const int R = a.c.residual;
+    quantize_value_row<BITS, GS>(a.c, a.c.v_resid + ((int64_t)unit * R + a.prequant % R) * kHeadDim,
+                                 (int64_t)unit * cap + a.prequant);
+  }
 }
 
 // Merge of the part records (one workgroup per query head, one thread per

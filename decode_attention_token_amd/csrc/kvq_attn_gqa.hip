@@ -59,6 +59,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_attn_common.h"
+#include "kvq_quant_common.h"
 
 namespace kvq {
 namespace {
@@ -903,6 +904,13 @@ void gqa_mfma_kernel(AttnArgs a) {
       st.ml[2 * h + 1] = L;
     }
     __syncthreads();
+  }
+  if (a.prequant >= 0 && split == a.splits - 1 && wave == 0) {
+    // a full FIFO queue: its oldest value row is quantized now, ahead of the
+    // next append's pop
+    const int R = a.c.residual;
+    quantize_value_row<BITS, GS>(a.c, a.c.v_resid + ((int64_t)unit * R + a.prequant % R) * kHeadDim,
+                                 (int64_t)unit * cap + a.prequant);
   }
   queue_finish<kHpg, kGqaWaves>(a, unit, split, st, s_took, (uint32_t)nsc);
 }

@@ -364,7 +364,8 @@ __global__ __launch_bounds__(256) void key_norm_kernel(float *__restrict__ norm,
 
 // One workgroup (one wave) per unit.  When pop_row >= 0 the window is full:
 // the oldest window token (ring slot pop_row mod R) is quantized into cache
-// row pop_row first.  Then the new key and value rows are written into row
+// row pop_row first.  Then the new key and value rows, unless k_new is null
+// (a fused step's attention launch stores them), are written into row
 // `slot` of the sink rows (to_sink) or of the ring.
 template <int BITS>
 __global__ __launch_bounds__(64) void innerq_append_kernel(CacheView c, const uint16_t *__restrict__ k_new,
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(64) void innerq_append_kernel(CacheView c, const ui
     __syncthreads();   // the popped slot is read before the new token overwrites it
   }
   constexpr int CH = kHeadDim * 2 / 16;   // 16-byte chunks per row
-  if (tid < 2 * CH) {
+  if (k_new != nullptr && tid < 2 * CH) {
     const bool values = tid >= CH;
     const int ch = tid % CH;
     const uint4 *src = reinterpret_cast<const uint4 *>((values ? v_new : k_new) + (int64_t)unit * kHeadDim);
@@ -591,6 +592,11 @@ void innerq_attn_kernel(AttnArgs a) {
         const int64_t off = ((int64_t)unit * S + ii) * kHeadDim + j * CPL;
         krow = a.c.k_sink + off;
         vrow = a.c.v_sink + off;
+      } else if (a.k_new != nullptr && nq + (ii - nsink) == a.n - 1) {
+        // fused step: the new token, not in the ring yet
+        const int64_t off = (int64_t)unit * kHeadDim + j * CPL;
+        krow = a.k_new + off;
+        vrow = a.v_new + off;
       } else {
         const int64_t off = ((int64_t)unit * R + (nq + (ii - nsink)) % R) * kHeadDim + j * CPL;
         krow = a.c.k_resid + off;
@@ -598,6 +604,25 @@ void innerq_attn_kernel(AttnArgs a) {
       }
       fp16_token<HPG, CPL, 1, LPT>(o, qf, krow, vrow, valid, U);
     }
+    if (a.k_new != nullptr && tid < 2 * (kHeadDim * 2 / 16)) {
+      // fused step: the new token goes into its window slot, the slot of the
+      // token that left the window (read quantized by this launch)
+      constexpr int CH = kHeadDim * 2 / 16;
+      const int which = tid / CH, ch = tid % CH;
+      const uint4 *src = reinterpret_cast<const uint4 *>((which ? a.v_new : a.k_new) + (int64_t)unit * kHeadDim);
+      uint4 *dst = reinterpret_cast<uint4 *>((which ? a.c.v_resid : a.c.k_resid) +
+                                             ((int64_t)unit * R + (a.n - 1) % R) * kHeadDim);
+      dst[ch] = src[ch];
+    }
+  }
+  if (a.prequant >= 0 && split == 0 && wave == 0 && lane < 2 * NG) {
+    // a full window: its oldest token's key and value rows are quantized
+    // now, ahead of the next append's pop (one lane per group)
+    const bool values = lane >= NG;
+    const int g = lane % NG;
+    const uint16_t *ring = values ? a.c.v_resid : a.c.k_resid;
+    const uint16_t *x = ring + ((int64_t)unit * a.c.residual + a.prequant % a.c.residual) * kHeadDim + g * GS;
+    quantize_into<BITS>(a.c, values, x, (int64_t)unit * cap + a.prequant, g);
   }
 
   combine_waves<HPG, LPT, 1>(o, smem, st, wave, lane, INV_U);

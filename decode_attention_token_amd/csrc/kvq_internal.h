@@ -114,6 +114,12 @@ struct AttnArgs {
   // slot.  Null when the token was appended beforehand.
   const uint16_t *k_new;
   const uint16_t *v_new;
+  // Token whose quantized row(s) the launch writes ahead of its pop (same
+  // counting as n), or -1: KIVI, the value of a full FIFO queue's oldest
+  // token (ring slot prequant mod R); InnerQ, the key and value of a full
+  // window's oldest token.  Nothing in the launch reads that row or writes
+  // that ring slot.
+  int64_t prequant;
 };
 
 hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t s);

@@ -1,7 +1,8 @@
-// Device-side quantizer pieces shared by kvq_quant.hip (KIVI layout) and
-// kvq_innerq.hip (InnerQ-style layout): group scale and zero-point, the
-// exactly rounded code map with its fast path, 16-byte fp16 loads and the
-// 8-channel tile coder.
+// Device-side quantizer pieces shared by kvq_quant.hip (KIVI layout),
+// kvq_innerq.hip (InnerQ-style layout) and the KIVI attention kernels (which
+// quantize one value row ahead of a FIFO pop): group scale and zero-point,
+// the exactly rounded code map with its fast path, 16-byte fp16 loads and
+// the 8-channel tile coder.
 // Private to the HIP sources.
 //
 // Bit-exactness: every arithmetic step is one IEEE fp32 operation with round
@@ -13,6 +14,7 @@
 #include <hip/hip_fp16.h>
 
 #include "kvq_device_util.h"
+#include "kvq_internal.h"
 
 namespace kvq {
 namespace {
@@ -177,6 +179,69 @@ __device__ __forceinline__ uint32_t pair_words(uint32_t ua, uint32_t ub, bool od
   const uint32_t send = odd ? ua : ub;
   const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
   return odd ? (recv | (ub << 16)) : (ua | (recv << 16));
+}
+
+// One value row of the KIVI layout (128 fp16 channels of one token at src)
+// quantized into cache row `row` (unit * cap + token) by a whole wave, with
+// the arithmetic of the value quantizer kernel: groups of G channels, the
+// group minimum and maximum as one packed (min, -max) fp16 pair reduced over
+// the group's lanes, group_params, and the tile coder with its exact
+// fallback, so the codes and metadata are those the quantizer kernel writes
+// for the same row.  Lane l takes channels 8 (l % 16) .. + 7; the four
+// 16-lane rows of the wave repeat the work and the first one stores.  Every
+// lane of the wave must call it (cross-lane moves and a wave vote).
+template <int BITS, int G>
+__device__ __forceinline__ void quantize_value_row(const CacheView &c, const uint16_t *__restrict__ src,
+                                                   int64_t row) {
+  constexpr int LPG = G / 8;                  // lanes per value group
+  constexpr int NG = kHeadDim / G;
+  constexpr int W = kHeadDim * BITS / 32;     // code words per row
+  constexpr float QMAX = float((1 << BITS) - 1);
+  const int lane = threadIdx.x & 63, cs = lane & 15, j = cs / LPG;
+  const uint4 raw = reinterpret_cast<const uint4 *>(src)[cs];
+  const f16x2 h0 = as_h2(raw.x), h1 = as_h2(raw.y), h2 = as_h2(raw.z), h3 = as_h2(raw.w);
+  const f16x2 lo = hmin(hmin(h0, h1), hmin(h2, h3)), hi = hmax(hmax(h0, h1), hmax(h2, h3));
+  const f16x2 lo2 = hmin(lo, lo.yx), hi2 = hmax(hi, hi.yx);
+  f16x2 v = {lo2.x, -hi2.x};
+  v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0xB1, 0xF, 0xF, true)));   // lane ^ 1
+  v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x4E, 0xF, 0xF, true)));   // lane ^ 2
+  if constexpr (LPG >= 8)
+    v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x141, 0xF, 0xF, true)));  // other quad of 8
+  if constexpr (LPG >= 16)
+    v = hmin(v, as_h2((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), 0x140, 0xF, 0xF, true)));  // other half of 16
+  const float mn = (float)v.x, mx = -(float)v.y;
+  const GroupParams p = group_params(mn, mx, QMAX, c.meta != 0);
+  const float thr1 = tie_threshold(fmaxf(fabsf(mn), fabsf(mx)), p.r);
+  float r[8], z[8], thr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    r[k] = p.r;
+    z[k] = p.z;
+    thr[k] = thr1;
+  }
+  bool near = false;
+  uint32_t u = code8_fast<BITS>(raw, r, z, thr, 0.0f, near);
+  if (__any(near)) {
+    float sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sv[k] = p.s;
+    u = code8_exact<BITS>(raw, sv, z, 0.0f);
+  }
+  if (lane < 16 && cs % LPG == 0) {
+    if (c.meta) {
+      reinterpret_cast<uint32_t *>(c.v_scale)[row * NG + j] = pack_meta(p.s, p.z);
+    } else {
+      c.v_scale[row * NG + j] = p.s;
+      c.v_zero[row * NG + j] = static_cast<int16_t>(p.z);
+    }
+  }
+  if constexpr (BITS == 2) {
+    // a word holds the 8 codes of an even lane and then those of the odd one
+    const uint32_t odd = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true);   // lane ^ 1
+    if (lane < 16 && (cs & 1) == 0) c.v_codes[row * W + (cs >> 1)] = u | (odd << 16);
+  } else {
+    if (lane < 16) c.v_codes[row * W + cs] = u;
+  }
 }
 
 }  // namespace

@@ -211,6 +211,10 @@ typedef struct {
                            appends that quantized a token leaving the window */
   float *k_norm;        /* device f32 [U][head_dim], written by prefill; only
                            with key_norm (may be null otherwise) */
+  int64_t prequant;     /* library-owned: 1 + the token whose quantized rows a
+                           decode step has already written ahead of its leaving
+                           the FIFO value queue (KIVI) or the window (InnerQ);
+                           0 = none */
 } kvq_cache;
 
 /* Validates cfg and fills *out with the buffer sizes.  Host only. */
@@ -248,9 +252,10 @@ kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache,
  * residual reaches R tokens it is quantized and appended to the grouped part
  * in the same call (eager flush, [KIVI] how it works; [HFQ] 3.1); values
  * follow the cache's kvq_v_policy.  InnerQ, otherwise: when the window
- * already holds R tokens its oldest
- * token (ring slot nq mod R) is quantized into row nq first, and the new
- * token takes ring slot n mod R; one kernel launch.  Needs started and
+ * already holds R tokens its oldest token (ring slot nq mod R) is quantized
+ * into row nq first, and the new token takes ring slot n mod R; one kernel
+ * launch.  A value or window token that a decode step has already quantized
+ * (cache->prequant) is not quantized again.  Needs started and
  * n < max_tokens. */
 kvq_status kvq_append_token(const kvq_config *cfg, kvq_cache *cache,
                             const uint16_t *k_new, const uint16_t *v_new,
@@ -318,13 +323,19 @@ kvq_status kvq_decode_attention_static(const kvq_config *cfg, const kvq_cache *c
                                        float softmax_scale, float *out, int32_t splits, hipStream_t stream);
 
 /* One decode step: kvq_append_token(k_new, v_new) followed by
- * kvq_decode_attention(q) with the same results, but as a single kernel
- * launch whenever a KIVI append needs no flush, the new token is not a sink
- * and the cache uses the chunked value residual: the attention kernel reads
- * the new token from k_new/v_new
- * and stores it into its residual slot.  Otherwise (and always for InnerQ)
- * it runs the two calls in sequence.  Arguments and requirements are those of the two calls; on a
- * validation failure nothing is enqueued and the cache is unchanged. */
+ * kvq_decode_attention(q), with the same cache bytes and bit-identical
+ * output.  When the new token is not a sink and (KIVI) the append quantizes
+ * no key group, the attention kernel reads the new token from k_new/v_new
+ * and stores it into its residual slots: one launch.  A token that leaves a
+ * FIFO value queue or the InnerQ window at this append is quantized by that
+ * same launch one step ahead: a step after which the queue or window is
+ * full also writes the quantized rows of its oldest token (recorded in
+ * cache->prequant), so the next step, or the next kvq_append_token, only
+ * advances the counters; without that record one small launch quantizes it
+ * first.  Otherwise the two calls run in sequence.  Arguments and
+ * requirements are those of the two calls; on a validation failure
+ * (including a workspace below kvq_workspace_bytes for the split count used)
+ * nothing is enqueued and the cache is unchanged. */
 kvq_status kvq_decode_step(const kvq_config *cfg, kvq_cache *cache, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes, int32_t splits, hipStream_t stream);

@@ -66,7 +66,7 @@ int main(void) {
          sizeof(kvq_cache));
   F(kvq_config, scheme) F(kvq_config, sink_tokens) F(kvq_layout, k_sink) F(kvq_layout, v_sink)
   F(kvq_config, meta_format) F(kvq_config, schedule) F(kvq_config, kernel) F(kvq_config, key_norm)
-  F(kvq_layout, k_norm) F(kvq_cache, k_norm)
+  F(kvq_layout, k_norm) F(kvq_cache, k_norm) F(kvq_cache, prequant)
   F(kvq_cache, k_sink) F(kvq_cache, v_sink) F(kvq_cache, n_tokens) F(kvq_cache, flushes)
   return 0;
 }

@@ -12,7 +12,7 @@ import torch
 import decode_attention_token_amd as kvq
 import oracle
 from workloads import Workload, gen_new_tokens, gen_prefill, gen_queries
-from gpu_helpers import (ATOL, SPLIT_TOL_MFMA, compare_sink_unit, config_fields, host, max_err, oracle_attention,
+from gpu_helpers import (ATOL, SPLIT_TOL_MFMA, compare_all_buffers, compare_sink_unit, config_fields, host, max_err, oracle_attention,
                          queue_schedule)
 
 pytestmark = pytest.mark.gpu
@@ -128,8 +128,10 @@ def test_gqa_mfma_split_counts_and_reruns(bits, G):
                 assert float(np.abs(dyn.astype(np.float64) - want).max()) <= ATOL
 
 
-def test_gqa_mfma_fused_step_matches_append_then_attention():
-    w = _w(430, 2, 300, 2, 32, 64, 40)
+@pytest.mark.parametrize("policy,sinks", [(CHUNK, 0), (FIFO, 0), (FIFO, 4)], ids=["chunk", "fifo", "fifo-sinks"])
+def test_gqa_mfma_fused_step_matches_append_then_attention(policy, sinks):
+    w = _w(430, 2, 300, 2, 32, 64, 40, policy, sinks)
+    print(f"case {w.name} policy {policy} sinks {sinks}", flush=True)
     k, v = gen_prefill(w, 0, "cuda")
     kn, vn = gen_new_tokens(w, 0, "cuda")
     qs = gen_queries(w, 0, "cuda")
@@ -143,9 +145,16 @@ def test_gqa_mfma_fused_step_matches_append_then_attention():
         b.append(kn[i].contiguous(), vn[i].contiguous())
         ob = b.attention(q)
         ref.append(host(kn[i]), host(vn[i]))
+        assert (a.n_tokens, a.nq_k, a.nq_v) == (ref.n, ref.nq_k, ref.nq_v)
         torch.cuda.synchronize()
         assert torch.equal(oa, ob), i
     assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
+    if sinks:
+        for bb in range(w.batch):
+            for h in range(w.num_kv_heads):
+                compare_sink_unit(a, ref, bb, h)
+    else:
+        compare_all_buffers(a, ref)
 
 
 def test_gqa_mfma_large_magnitudes():

@@ -34,10 +34,11 @@ CASES = [
 ]
 
 
-def _cache_and_ref(w):
+def _cache_and_ref(w, key_norm=0):
     cfg, cache = make_innerq_cache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_q_heads,
-                                   w.num_kv_heads, w.max_tokens)
-    ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_kv_heads, 128)
+                                   w.num_kv_heads, w.max_tokens, key_norm=key_norm)
+    ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, w.batch, w.num_kv_heads, 128,
+                             key_norm=bool(key_norm))
     return cfg, cache, ref
 
 
@@ -134,13 +135,18 @@ def test_innerq_empty_prefill_single_token_and_capacity():
     assert e.value.status == kvq.KVQ_ERR_CAPACITY
 
 
-def test_innerq_decode_step_matches_append_then_attention():
+@pytest.mark.parametrize("key_norm", [0, 1], ids=["plain", "key-norm"])
+def test_innerq_decode_step_matches_append_then_attention(key_norm):
+    """The window is full after the prompt, so every step pops: the first one
+    with a small quantize launch, later ones from the rows the previous
+    step's attention launch quantized ahead."""
     w = _w(230, 2, 4, 2, 100, 4, 64, 32, 4, 20)
+    print(f"case {w.name} key_norm={key_norm}", flush=True)
     k, v = gen_prefill(w, 0, "cuda")
     kn, vn = gen_new_tokens(w, 0, "cuda")
     qs = gen_queries(w, 0, "cuda")
-    _, a, ref = _cache_and_ref(w)
-    _, b, _ = _cache_and_ref(w)
+    _, a, ref = _cache_and_ref(w, key_norm)
+    _, b, _ = _cache_and_ref(w, key_norm)
     a.prefill(k, v)
     b.prefill(k, v)
     ref.prefill(host(k), host(v))
@@ -151,10 +157,44 @@ def test_innerq_decode_step_matches_append_then_attention():
         b.append(kn[i].contiguous(), vn[i].contiguous())
         ob = b.attention(q, workspace=wb)
         ref.append(host(kn[i]), host(vn[i]))
+        assert (a.n_tokens, a.nq_k) == (ref.n, ref.nq)
+        assert a.c.prequant == ref.nq + 1, "a full window: its oldest token is quantized ahead"
         torch.cuda.synchronize()
         assert torch.equal(oa, ob), i
     assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
     compare_innerq_buffers(a, ref)
+
+
+def test_innerq_steps_and_appends_interleaved():
+    """Fused steps, plain appends and attention calls in a seeded random
+    order, from a prompt shorter than the window (the window fills during the
+    run): the rows quantized ahead by a step are used by the next append or
+    step, and every state matches the oracle."""
+    w = _w(231, 1, 2, 2, 20, 2, 32, 16, 2, 60)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    _, cache, ref = _cache_and_ref(w)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    ws = cache.workspace()
+    scale = 1 / math.sqrt(128)
+    order = np.random.default_rng(231).integers(0, 3, size=w.steps)
+    for i in range(w.steps):
+        q = qs[i].contiguous()
+        if order[i] == 0:
+            out = cache.step(kn[i].contiguous(), vn[i].contiguous(), q, workspace=ws)
+        else:
+            cache.append(kn[i].contiguous(), vn[i].contiguous())
+            out = cache.attention(q, workspace=ws) if order[i] == 1 else None
+        ref.append(host(kn[i]), host(vn[i]))
+        assert (cache.n_tokens, cache.nq_k) == (ref.n, ref.nq), i
+        if out is not None:
+            torch.cuda.synchronize()
+            assert max_err(out, oracle_attention(ref, host(q), scale)) <= ATOL, i
+        if i % 10 == 9:
+            compare_innerq_buffers(cache, ref)
+    compare_innerq_buffers(cache, ref)
 
 
 # One-time per-channel key scales (KVQ_KEYNORM_PROMPT): the scales, the

@@ -185,6 +185,47 @@ def test_decode_step_matches_append_then_attention(policy):
     compare_all_buffers(fused, ref)
 
 
+@pytest.mark.parametrize("sinks", [0, 4])
+def test_fifo_steps_and_appends_interleaved(sinks):
+    """KIVI with a FIFO value queue: fused steps, plain appends and attention
+    calls in a seeded random order across key flushes.  A step after which
+    the queue is full quantizes its oldest value ahead; the next step or
+    append must use that row, and every state matches the oracle."""
+    from gpu_helpers import compare_sink_unit
+    w = _w(150 + sinks, 2, 4, 2, 100, 2, 32, 64, 150, FIFO)
+    print(f"case {w.name} sinks {sinks}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    cfg = kvq.make_config(2, 32, 64, 2, 4, 2, 128, 320, FIFO, kvq.KVQ_SCHEME_KIVI, sinks)
+    cache = kvq.KVCache(cfg, "cuda")
+    ref = oracle.KiviSinkCache(2, 32, 64, sinks, 2, 2, 128, FIFO)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    ws = cache.workspace()
+    scale = 1 / math.sqrt(128)
+    order = np.random.default_rng(150 + sinks).integers(0, 3, size=w.steps)
+    ahead = 0
+    for i in range(w.steps):
+        q = qs[i].contiguous()
+        if order[i] == 0:
+            out = cache.step(kn[i].contiguous(), vn[i].contiguous(), q, workspace=ws)
+            ahead += cache.c.prequant != 0
+        else:
+            cache.append(kn[i].contiguous(), vn[i].contiguous())
+            out = cache.attention(q, workspace=ws) if order[i] == 1 else None
+        ref.append(host(kn[i]), host(vn[i]))
+        assert (cache.n_tokens, cache.nq_k, cache.nq_v) == (ref.n, ref.nq_k, ref.nq_v), i
+        if out is not None:
+            torch.cuda.synchronize()
+            assert max_err(out, oracle_attention(ref, host(q), scale)) <= ATOL, i
+        if i % 25 == 24 or i == w.steps - 1:
+            for b in range(2):
+                for h in range(2):
+                    compare_sink_unit(cache, ref, b, h)
+    assert ahead > 10
+
+
 # KIVI with fp16 sink tokens: (workload, sinks, steps at which attention is checked)
 SINK_CASES = [
     (_w(140, 2, 4, 4, 300, 2, 32, 64, 70), 4, [1, 20, 21, 70]),            # flush at step 20
@@ -225,16 +266,20 @@ def test_kivi_sink_tokens_parity(w, S, checks):
             assert err <= ATOL
 
 
-def test_kivi_sink_decode_step_matches_append_then_attention():
+@pytest.mark.parametrize("policy", [CHUNK, FIFO])
+def test_kivi_sink_decode_step_matches_append_then_attention(policy):
+    """The first steps fill the sink tokens (two calls), the later ones take
+    the fused path (one launch, or the value pop and one launch for FIFO)."""
     from gpu_helpers import compare_sink_unit
-    w = _w(144, 2, 4, 2, 2, 2, 32, 64, 80)
+    w = _w(144, 2, 4, 2, 2, 2, 32, 64, 80, policy)
     S = 4
+    print(f"case {w.name} sinks {S}", flush=True)
     kn, vn = gen_new_tokens(w, 0, "cuda")
     k, v = gen_prefill(w, 0, "cuda")
     qs = gen_queries(w, 0, "cuda")
-    mk = lambda: kvq.KVCache(kvq.make_config(2, 32, 64, 2, 4, 2, 128, 192, CHUNK, kvq.KVQ_SCHEME_KIVI, S), "cuda")
+    mk = lambda: kvq.KVCache(kvq.make_config(2, 32, 64, 2, 4, 2, 128, 192, policy, kvq.KVQ_SCHEME_KIVI, S), "cuda")
     fused, plain = mk(), mk()
-    ref = oracle.KiviSinkCache(2, 32, 64, S, 2, 2, 128)
+    ref = oracle.KiviSinkCache(2, 32, 64, S, 2, 2, 128, policy)
     fused.prefill(k, v)
     plain.prefill(k, v)
     ref.prefill(host(k), host(v))
@@ -245,6 +290,7 @@ def test_kivi_sink_decode_step_matches_append_then_attention():
         plain.append(kn[i].contiguous(), vn[i].contiguous())
         ob = plain.attention(q, workspace=wb)
         ref.append(host(kn[i]), host(vn[i]))
+        assert (fused.n_tokens, fused.nq_k, fused.nq_v) == (ref.n, ref.nq_k, ref.nq_v)
         torch.cuda.synchronize()
         assert torch.equal(oa, ob), i
     assert max_err(oa, oracle_attention(ref, host(q), 1 / math.sqrt(128))) <= ATOL
