@@ -136,10 +136,10 @@ int32_t auto_splits_for(const kvq_config *c, int64_t nq) {
 }
 
 // Workspace: per-unit work-queue counters (zero between calls), then fp32
-// partial (acc[128], max, sum) records, (splits + 1) per query head.
+// partial (acc[128], max, sum) records, one per query head and split.
 size_t workspace_for(const kvq_config *c, int32_t splits) {
   return kvq::counter_bytes((int64_t)c->batch * c->num_kv_heads) +
-         (size_t)c->batch * c->num_q_heads * (size_t)(splits + 1) * kvq::kPartialStride * sizeof(float);
+         (size_t)c->batch * c->num_q_heads * (size_t)splits * kvq::kPartialStride * sizeof(float);
 }
 
 // cfg->schedule: KVQ_SCHED_FIXED (default) makes the matrix-core kernel

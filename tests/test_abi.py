@@ -310,11 +310,11 @@ def test_workspace_and_split_sizing(lib):
     s = kvq.kvq_auto_splits(c, 4097)
     assert 1 <= s <= 64
     # per-unit counters (four u32 per (batch, kv head): ticket, pad and a
-    # 64-bit election word; padded to 256 bytes), then (splits + 1) records of
-    # 132 floats per query head
+    # 64-bit election word; padded to 256 bytes), then one record of 132
+    # floats per query head and split
     ctr = 16 * 32 * 16
-    assert kvq.kvq_workspace_bytes(c, 4097, 0) == ctr + 16 * 32 * (s + 1) * 132 * 4
-    assert kvq.kvq_workspace_bytes(c, 4097, 3) == ctr + 16 * 32 * 4 * 132 * 4
+    assert kvq.kvq_workspace_bytes(c, 4097, 0) == ctr + 16 * 32 * s * 132 * 4
+    assert kvq.kvq_workspace_bytes(c, 4097, 3) == ctr + 16 * 32 * 3 * 132 * 4
     assert kvq.kvq_workspace_bytes(c, 4097, 65) == 0
     # more tokens never needs fewer splits, so sizing for capacity is enough
     prev = 0
