@@ -7,8 +7,11 @@ exact .5 ties of x / S, and a lone outlier.  The patterns are planted in
 key groups (G tokens of one channel) and value groups (G channels of one
 token), then run through every GPU path that quantizes: prefill, the chunked
 flush append, the FIFO value pop with its key flush, both metadata formats,
-and the InnerQ-style prefill and window pop.  Every cache byte must match the
-oracle bit for bit.
+and the InnerQ-style prefill and window pop, each through kvq_append_token
+and through kvq_decode_step (whose attention launch quantizes the next
+leaving FIFO value or window token ahead; for KIVI values with a one-wave
+routine of its own).
+Every cache byte must match the oracle bit for bit.
 """
 import numpy as np
 import pytest
@@ -85,10 +88,20 @@ def _dev(x):
 KIVI_CASES = [(bits, G, policy, meta) for bits, G in ((2, 32), (4, 64)) for policy in (0, 1) for meta in (0, 1)]
 
 
+def _push(cache, k, v, via):
+    if via == "append":
+        cache.append(k, v)
+    else:
+        H = cache.cfg.num_q_heads
+        q = torch.ones(1, H, D, dtype=torch.float16, device="cuda")
+        cache.step(k, v, q)
+
+
+@pytest.mark.parametrize("via", ["append", "step"])
 @pytest.mark.parametrize("bits,G,policy,meta", KIVI_CASES)
-def test_kivi_quantizer_edge_groups(bits, G, policy, meta):
+def test_kivi_quantizer_edge_groups(bits, G, policy, meta, via):
     H, R, L, A = 2, 64, 256, 2 * 64 + 3
-    print(f"case KIVI bits={bits} G={G} policy={policy} meta={meta}", flush=True)
+    print(f"case KIVI bits={bits} G={G} policy={policy} meta={meta} via {via}", flush=True)
     T = L + A
     K = _planted(bits, G, H, T + G, 100 + bits, True)[:, :, :T]
     V = _planted(bits, G, H, T, 200 + bits, False)
@@ -102,7 +115,7 @@ def test_kivi_quantizer_edge_groups(bits, G, policy, meta):
     compare_all_buffers(cache, ref)
     for i in range(L, T):
         f0 = ref.flushes
-        cache.append(_dev(K[:, :, i]), _dev(V[:, :, i]))
+        _push(cache, _dev(K[:, :, i]), _dev(V[:, :, i]), via)
         ref.append(K[:, :, i], V[:, :, i])
         if ref.flushes != f0 or policy == 1 or i == T - 1:
             torch.cuda.synchronize()
@@ -114,11 +127,12 @@ def test_kivi_quantizer_edge_groups(bits, G, policy, meta):
     assert ref.flushes == 2
 
 
+@pytest.mark.parametrize("via", ["append", "step"])
 @pytest.mark.parametrize("key_norm", [0, 1])
 @pytest.mark.parametrize("bits,G", [(4, 64), (2, 32)])
-def test_innerq_quantizer_edge_groups(bits, G, key_norm):
+def test_innerq_quantizer_edge_groups(bits, G, key_norm, via):
     H, S, R, L, A = 2, 4, 16, 100, 40
-    print(f"case InnerQ bits={bits} G={G} key_norm={key_norm}", flush=True)
+    print(f"case InnerQ bits={bits} G={G} key_norm={key_norm} via {via}", flush=True)
     T = L + A
     K = _planted(bits, G, H, T, 300 + bits, False)
     V = _planted(bits, G, H, T, 400 + bits, False)
@@ -130,7 +144,7 @@ def test_innerq_quantizer_edge_groups(bits, G, key_norm):
     torch.cuda.synchronize()
     compare_innerq_buffers(cache, ref)
     for i in range(L, T):
-        cache.append(_dev(K[:, :, i]), _dev(V[:, :, i]))
+        _push(cache, _dev(K[:, :, i]), _dev(V[:, :, i]), via)
         ref.append(K[:, :, i], V[:, :, i])
         torch.cuda.synchronize()
         compare_innerq_buffers(cache, ref)
