@@ -235,12 +235,16 @@ __device__ __forceinline__ void decode_meta(uint32_t s_word, uint32_t zhalf, flo
 // A share of the unit's fp16 list -- sink rows [0, nsink), then tokens
 // [n_main, n), whose keys and values are each quantized (rows below nq_k /
 // nq_v) or fp16 (ring slot t mod R, or k_new / v_new for token n - 1 of a
-// fused step): entries [ib, ie).  Plain dequantize-then-dot.  Scores: 16 lanes per token (8 channels each), four
-// tokens per wave at a time.  Softmax: one wave per head.  P.V: 16 token
-// slots x 16 channel octets.  Row loads of kRestBatch rounds are issued
-// before any of them is used, so the part costs a few memory round trips.
+// fused step): entries [ib, ie).  Plain dequantize-then-dot.  Scores: 16
+// lanes per token (8 channels each), four tokens per wave at a time.
+// Softmax: one wave per head.  P.V: 16 token slots x 16 channel octets.  Row
+// loads of kRestBatch rounds (16 tokens each) are issued before any of them
+// is used.  Two rounds cover the usual share (a split's part of a residual
+// of at most R tokens); eight made this rarely run code so long that a fused
+// decode step on the 2-bit GQA workload took 2.2 us longer (its instructions
+// are fetched cold once per call).
 // Leaves the share's (acc, max, sum) in out_acc / out_ml.
-constexpr int kRestBatch = 8;
+constexpr int kRestBatch = 2;
 
 // 8 channels (8 c .. 8 c + 7) of token i of the fp16 part, as raw fp16 pairs
 // (fp16 rows) or dequantized (quantized rows, via `quant`).
