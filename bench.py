@@ -120,9 +120,9 @@ def sample_units(w, host_bytes=512 << 20, seed=7):
 
 # decode kernel and its source files per kind
 KERNELS = {
-    0: ("decode_attn_kernel", ("kvq_attn.hip", "kvq_attn_common.h", "kvq_internal.h")),
-    1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_internal.h")),
-    "gqa4": ("gqa_mfma_kernel", ("kvq_attn_gqa.hip", "kvq_attn_common.h", "kvq_internal.h")),
+    0: ("decode_attn_kernel", ("kvq_attn.hip", "kvq_attn_common.h", "kvq_quant_common.h", "kvq_internal.h")),
+    1: ("innerq_attn_kernel", ("kvq_innerq.hip", "kvq_attn_common.h", "kvq_quant_common.h", "kvq_internal.h")),
+    "gqa4": ("gqa_mfma_kernel", ("kvq_attn_gqa.hip", "kvq_attn_common.h", "kvq_quant_common.h", "kvq_internal.h")),
 }
 
 
@@ -311,6 +311,32 @@ def cpu_baseline(w, sample, budget_s=10.0, pool_budget_s=6.0):
             "flush": {"seconds_extrapolated": round(fl_s, 4), "bytes": fb, "GB/s": round(fb / fl_s / 1e9, 4),
                       "cores": 1,
                       "sample": f"oracle append that quantizes, on {nunits} units, scaled to {w.units}"}}
+
+
+def one_launch_step(w, c):
+    """Whether kvq_decode_step on cache c (before the step) is one launch:
+    the new token is not a sink, no key group is quantized (KIVI), the
+    chunked residual's rings are aligned, and a token leaving a FIFO value
+    queue or the InnerQ window was quantized ahead by the previous step."""
+    st = c.c
+    n1, R = st.n_tokens + 1, w.residual
+    iq = w.scheme == kvq.KVQ_SCHEME_INNERQ
+    fifo = iq or w.v_policy == kvq.KVQ_V_FIFO
+    if st.n_tokens < w.sinks:
+        return False
+    if not iq and (n1 - st.nq_k >= R or (not fifo and st.nq_k != st.nq_v)):
+        return False
+    return not (fifo and n1 - st.nq_v > R and st.prequant != st.nq_v + 1)
+
+
+def ahead_bytes(w):
+    """Bytes of quantizing one leaving token ahead, all units: the fp16 row(s)
+    read, codes and metadata written (KIVI: the value row; InnerQ: key and
+    value rows)."""
+    d, b, G = w.head_dim, w.bits, w.group
+    mb = 4 if w.meta else 6
+    per_row = d * 2 + d * b // 8 + (d // G) * mb
+    return w.units * per_row * (2 if w.scheme == kvq.KVQ_SCHEME_INNERQ else 1)
 
 
 def prefill_bytes(w, L):
@@ -579,27 +605,31 @@ def main():
     torch.cuda.synchronize()
     print("# timed loop", file=sys.stderr, flush=True)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    flushed, step_bytes = [], []
+    flushed, single, ahead, step_bytes = [], [], [], []
     t0 = time.perf_counter()
     nbytes = 0
     for k, i in enumerate(range(args.warmup, total)):
         evs[k].record(stream)
         f0 = caches[0].flushes
+        single.append(one_launch_step(w, caches[0]))
         nb = step(i, True)
         nbytes += nb
         step_bytes.append(nb)
         flushed.append(caches[0].flushes != f0)
+        ahead.append(caches[0].c.prequant != 0)
     evs[steps].record(stream)
     t_enq = time.perf_counter() - t0   # host time to enqueue the loop
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     step_us = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)]
-    plain = [k for k in range(steps) if not flushed[k]]
+    plain = [k for k in range(steps) if single[k]]
     # the timed loop's launches: one fused append + attention launch per layer
-    # and step when no flush is due; its bytes add the new token's ring store
+    # and step when no key group is quantized; its bytes add the new token's
+    # ring stores and, when the step quantizes the next leaving token ahead,
+    # that row's read and quantized write
     fused_us = sum(step_us[k] for k in plain) / (len(plain) * layers) if plain else None
-    fused_bytes = (sum(step_bytes[k] for k in plain) / (len(plain) * layers) + w.units * w.head_dim * 2 * 2
-                   if plain else None)
+    fused_bytes = (sum(step_bytes[k] + layers * ahead_bytes(w) * ahead[k] for k in plain) / (len(plain) * layers)
+                   + w.units * w.head_dim * 2 * 2 if plain else None)
 
     # the same attention-only passes again after the loop (drift check)
     after_us, after_bytes, _, _ = timed_attention(args.reps)
@@ -618,12 +648,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # a decode step is one launch for the KIVI scheme with chunked values
-    # (no flush due); a FIFO value queue adds the small launch that quantizes
-    # the popped value, and InnerQ appends in a launch of its own: there the
-    # roofline takes the attention launch alone
-    one_launch = w.scheme == kvq.KVQ_SCHEME_KIVI and w.v_policy == kvq.KVQ_V_CHUNK
-    if fused_us is not None and one_launch:
+    # a decode step is one launch unless it quantizes a key group (or the
+    # token that leaves the queue or window was not quantized ahead)
+    one_launch = bool(plain) and len(plain) == steps
+    if fused_us is not None:
         roof_us, roof_bytes, roof_launch = fused_us, fused_bytes, "fused decode step (kvq_decode_step)"
     else:
         roof_us, roof_bytes, roof_launch = call_us, call_bytes, "attention only (kvq_decode_attention)"
@@ -666,6 +694,7 @@ def main():
                    "note": "untimed back-to-back attention calls before any timing (clocks reach steady state)"},
         "host_enqueue_us_per_launch": round(t_enq / (steps * layers) * 1e6, 2),
         "loop_steps_with_flush": int(sum(flushed)),
+        "loop_steps_single_launch": len(plain),
         "loop_step_us": {"median": round(sorted(step_us)[len(step_us) // 2], 1), "min": round(min(step_us), 1),
                          "max": round(max(step_us), 1), "first": [round(t, 1) for t in step_us[:8]],
                          "launches_per_step": layers if one_launch else None},

@@ -250,20 +250,24 @@ constexpr int kRestBatch = 2;
 // (fp16 rows) or dequantized (quantized rows, via `quant`).
 struct RestRow {
   const uint16_t *row;   // fp16 row, or null for a quantized one
-  int64_t t;             // token index when quantized
+  int t;                 // token index when quantized (below 2^25)
 };
 
-template <int BITS, int META>
-__device__ __forceinline__ void dequant8(const uint32_t *codes, const float *scale, const int16_t *zero, int64_t unit,
-                                         int64_t cap, int64_t t, int c8, int G, bool keys, float *out) {
+// (Index arithmetic with the compile-time group size and 32-bit token
+// indices: this code runs once per call, and its length is fetched cold.)
+template <int BITS, int GS, int META>
+__device__ __forceinline__ void dequant8(const uint32_t *codes, const float *scale, const int16_t *zero, int unit,
+                                         int64_t cap, int t, int c8, bool keys, float *out) {
   constexpr int PER = 32 / BITS;
   constexpr int W = kHeadDim / PER;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
-  const uint32_t w = codes[(unit * cap + t) * W + (8 * c8) / PER];
+  const int64_t row = (int64_t)unit * cap + t;
+  const uint32_t w = codes[row * W + (8 * c8) / PER];
   const int sh = ((8 * c8) % PER) * BITS;
-  // keys: (S, Z) per (group of G tokens, channel); values: per (token, group
-  // of G channels) -- the 8 channels share one value group since G >= 32
-  const int64_t mi = keys ? (unit * (cap / G) + t / G) * kHeadDim + 8 * c8 : (unit * cap + t) * (kHeadDim / G) + (8 * c8) / G;
+  // keys: (S, Z) per (group of GS tokens, channel); values: per (token, group
+  // of GS channels) -- the 8 channels share one value group since GS >= 32
+  const int64_t mi = keys ? ((int64_t)unit * (cap / GS) + t / GS) * kHeadDim + 8 * c8
+                          : row * (kHeadDim / GS) + (8 * c8) / GS;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float Sc, Z;
@@ -288,10 +292,10 @@ __device__ __forceinline__ void fp16x8(uint4 v, float *out) {
 
 static_assert(kGqaWaves == kHpg, "the fp16 part runs one wave per head in its softmax");
 
-template <int BITS, int META>
+template <int BITS, int GS, int META>
 __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const float *qsm, float *out_acc,
                               float *out_ml, int ib, int ie) {
-  const int G = a.c.group, R = a.c.residual, S = a.c.sinks;
+  const int R = a.c.residual, S = a.c.sinks;
   const int64_t cap = a.c.cap;
   const int ns = a.nsink;
   const int nt = ie - ib;                     // tokens [ib, ie) of the unit's fp16 list
@@ -299,14 +303,17 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
   float *s_sc = smem;                         // [kHpg][nt] scores, then weights
   float *s_red = smem + kHpg * kMaxRest;      // [kGqaWaves][kHpg][128]
   // row of local token li (list entry ib + li) for keys (k = true) or values
+  // token counts stay below 2^25, so 32-bit indices (and one 32-bit
+  // remainder) do here
+  const int n_main = (int)a.n_main, n_last = (int)a.n - 1, nqk = (int)a.nq_k, nqv = (int)a.nq_v;
   auto row_of = [&](int li, bool k) -> RestRow {
     const int i = ib + li;
     if (i < ns) return {(k ? a.c.k_sink : a.c.v_sink) + ((int64_t)unit * S + i) * kHeadDim, 0};
-    const int64_t t = a.n_main + (i - ns);
-    if (t < (k ? a.nq_k : a.nq_v)) return {nullptr, t};
-    if ((k ? a.k_new : a.v_new) != nullptr && t == a.n - 1)
+    const int t = n_main + (i - ns);
+    if (t < (k ? nqk : nqv)) return {nullptr, t};
+    if ((k ? a.k_new : a.v_new) != nullptr && t == n_last)
       return {(k ? a.k_new : a.v_new) + (int64_t)unit * kHeadDim, 0};
-    return {(k ? a.c.k_resid : a.c.v_resid) + ((int64_t)unit * R + t % R) * kHeadDim, 0};
+    return {(k ? a.c.k_resid : a.c.v_resid) + ((int64_t)unit * R + (int)((uint32_t)t % (uint32_t)R)) * kHeadDim, 0};
   };
 
   // ---- scores: lane j of token group sub takes channels 8j .. 8j + 7
@@ -335,7 +342,7 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
         if (rr[r].row != nullptr || rr[r].t < 0) {
           fp16x8(raw[r], kf);
         } else {
-          dequant8<BITS, META>(a.c.k_codes, a.c.k_scale, a.c.k_zero, unit, cap, rr[r].t, j, G, true, kf);
+          dequant8<BITS, GS, META>(a.c.k_codes, a.c.k_scale, a.c.k_zero, unit, cap, rr[r].t, j, true, kf);
         }
 #pragma unroll
         for (int h = 0; h < kHpg; ++h) {
@@ -394,7 +401,7 @@ __device__ void gqa_fp16_part(const AttnArgs &a, int unit, float *smem, const fl
         if (rr[r].row != nullptr) {
           fp16x8(raw[r], vf);
         } else {
-          dequant8<BITS, META>(a.c.v_codes, a.c.v_scale, a.c.v_zero, unit, cap, rr[r].t, c8, G, false, vf);
+          dequant8<BITS, GS, META>(a.c.v_codes, a.c.v_scale, a.c.v_zero, unit, cap, rr[r].t, c8, false, vf);
         }
 #pragma unroll
         for (int h = 0; h < kHpg; ++h) {
@@ -917,7 +924,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   if (ie > ib) {
     float *acc2 = st.acc + Gm::STAGE2;   // [kHpg][128], then (max, sum)[kHpg]
     float *ml2 = acc2 + kHpg * kHeadDim;
-    gqa_fp16_part<BITS, META>(a, unit, smem, qsm, acc2, ml2, ib, ie);
+    gqa_fp16_part<BITS, GS, META>(a, unit, smem, qsm, acc2, ml2, ib, ie);
     float f1[kHpg], f2[kHpg], mn[kHpg];
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) {
