@@ -117,6 +117,25 @@ kvq_status device_error(hipError_t e, const char *what) {
   return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Compute units of the current device (queried once per device).
+hipError_t compute_units(int *out) {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cached[dev].load() > 0) {
+    *out = cached[dev].load();
+    return hipSuccess;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < 64) cached[dev].store(n);
+  *out = n;
+  return hipSuccess;
+}
+
 int64_t main_tokens(const kvq_config *c, const kvq_cache *k) {
   const int64_t m = k->nq_k < k->nq_v ? k->nq_k : k->nq_v;
   return (m / c->group) * c->group;
@@ -452,6 +471,7 @@ kvq_status launch_innerq_attention(const kvq_config *cfg, const kvq_cache *cache
   a.k_new = k_new;
   a.v_new = v_new;
   a.prequant = prequant;
+  a.early = splits;
   a.nsink = 0;   // the InnerQ kernel derives its sinks from n and the config
   const hipError_t e = kvq::launch_innerq_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
@@ -509,7 +529,13 @@ kvq_status launch_attention(const kvq_config *cfg, const kvq_cache *cache, int64
   a.k_new = k_new;
   a.v_new = v_new;
   a.prequant = prequant >= 0 ? prequant - ns : -1;
-  hipError_t e = kvq::launch_decode_attention(a, stream);
+  int cus = 0;
+  hipError_t e = compute_units(&cus);
+  if (e != hipSuccess) return device_error(e, "device attributes");
+  const int units = cfg->batch * cfg->num_kv_heads;
+  a.early = cus / units;
+  if (a.early < 1 || a.early > a.splits) a.early = a.splits;
+  e = kvq::launch_decode_attention(a, stream);
   if (e != hipSuccess) return device_error(e, "decode attention");
   return KVQ_OK;
 }

@@ -920,7 +920,12 @@ void gqa_mfma_kernel(AttnArgs a) {
                                            ((int64_t)unit * a.c.residual + (a.n - 1) % a.c.residual) * kHeadDim);
     dst[ch] = src[ch];
   }
-  const int ib = (int)((int64_t)nrest * split / a.splits), ie = (int)((int64_t)nrest * (split + 1) / a.splits);
+  // The shares go to the leading a.early splits, whose workgroups all
+  // dispatch in the first round: they end a few microseconds before the
+  // second round's, which then no longer wait for the shares (3.6% off a
+  // fused decode step on the 2-bit GQA workload).
+  const int ib = split < a.early ? (int)((int64_t)nrest * split / a.early) : 0;
+  const int ie = split < a.early ? (int)((int64_t)nrest * (split + 1) / a.early) : 0;
   if (ie > ib) {
     float *acc2 = st.acc + Gm::STAGE2;   // [kHpg][128], then (max, sum)[kHpg]
     float *ml2 = acc2 + kHpg * kHeadDim;

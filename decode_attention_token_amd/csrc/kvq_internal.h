@@ -108,6 +108,9 @@ struct AttnArgs {
   int nparts;            // parts per unit (== splits); 1 means the kernel writes out directly
   int nsink;             // KIVI: fp16 sink tokens present (rows of c.k_sink); counters above
                          // then count the tokens after them
+  int early;             // matrix-core kernel: its leading splits whose workgroups all dispatch
+                         // in the first round (one per compute unit), in [1, splits]; they end
+                         // first, so the unit's fp16 tokens are shared among them
   float qscale;          // softmax_scale * log2(e)
   // Fused decode step: token n - 1 is read from k_new / v_new ([B*Hkv][128])
   // instead of the residual ring, and the last split writes it into its ring

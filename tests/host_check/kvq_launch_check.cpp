@@ -141,6 +141,14 @@ void check_resources(const kvq::CacheView &c) {
 }  // namespace
 
 extern "C" const char *hipGetErrorString(hipError_t) { return "stubbed launch"; }
+extern "C" hipError_t hipGetDevice(int *dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipDeviceGetAttribute(int *value, hipDeviceAttribute_t attr, int) {
+  *value = attr == hipDeviceAttributeMultiprocessorCount ? 256 : 0;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------- stubs
 namespace kvq {
@@ -299,6 +307,7 @@ hipError_t launch_decode_attention(const AttnArgs &a, hipStream_t) {
     need_fp16(c.v_sink, units, c.sinks, 0, a.nsink, "attention: value sinks");
   }
   expect(a.k_new == nullptr || a.n > a.nq_k, "fused token must be an fp16 token");
+  expect(a.early >= 1 && a.early <= a.splits, "early splits %d of %d", a.early, a.splits);
   if (a.prequant >= 0) {
     // its value is in the ring, not the fused token's slot, and not yet quantized
     expect(a.prequant >= a.nq_v && a.prequant < a.n - 1 && a.n - a.prequant == R,

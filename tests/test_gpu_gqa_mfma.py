@@ -90,6 +90,41 @@ def test_gqa_mfma_parity(w, checks):
                         compare_sink_unit(cache, ref, b, h)
 
 
+@pytest.mark.parametrize("policy,sinks", [(CHUNK, 0), (FIFO, 6)], ids=["chunk", "fifo-sinks"])
+def test_gqa_mfma_fp16_shares_on_leading_splits(policy, sinks):
+    """80 units: a launch of 8 or 16 splits per unit has its first 3 splits
+    in the first dispatch round (256 compute units), and only those take the
+    unit's fp16 tokens (sinks, the residual, the fused token).  Checked against
+    the oracle and the vector-ALU kernel at several split counts, and through
+    the fused step."""
+    w = _w(450 + sinks, 40, 700, 2, 32, 128, 2, policy, sinks, 0, 2)
+    print(f"case {w.name} units {w.units} policy {policy} sinks {sinks}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    qs = gen_queries(w, 0, "cuda")
+    cache, ref = _cache(w), _ref(w)
+    cache.prefill(k, v)
+    ref.prefill(host(k), host(v))
+    scale = 1.0 / math.sqrt(128)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    ref.append(host(kn[0]), host(vn[0]))
+    q = qs[0].contiguous()
+    want = oracle_attention(ref, host(q), scale)
+    for s in (8, 16, 0):
+        o = _attention(cache, q, "mfma", workspace=cache.workspace(splits=s), splits=s)
+        err = max_err(o, want)
+        print(f"  splits {s}: n={ref.n} rest={ref.n - (ref.nq_k // 32) * 32} err {err:.2e}", flush=True)
+        assert err <= ATOL, s
+    assert max_err(_attention(cache, q, "valu"), want) <= ATOL
+    # the fused step takes the same path
+    q = qs[1].contiguous()
+    out = cache.step(kn[1].contiguous(), vn[1].contiguous(), q, scale, workspace=cache.workspace(splits=8),
+                     splits=8)
+    ref.append(host(kn[1]), host(vn[1]))
+    torch.cuda.synchronize()
+    assert max_err(out, oracle_attention(ref, host(q), scale)) <= ATOL
+
+
 @pytest.mark.parametrize("bits,G", [(2, 32), (4, 64)])
 def test_gqa_mfma_split_counts_and_reruns(bits, G):
     w = _w(420 + bits, 2, 4000, bits, G, 128, 1)
