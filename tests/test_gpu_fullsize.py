@@ -62,3 +62,52 @@ def test_fullsize_sampled_parity(w, key_norm):
     print(f"  sampled units ok, worst attention err {worst:.2e}", flush=True)
     del k, v, cache
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", [LLAMA7B_4BIT, GQA_LONG, LONG_4BIT], ids=lambda x: x.name)
+def test_fullsize_decode_steps(w):
+    """The launch the bench times on these workloads: kvq_decode_step, one
+    launch per step (the new token from k_new / v_new; for the InnerQ window,
+    full after the prompt, the leaving token quantized one step ahead).  Three
+    steps, then sampled units bit-exact and their heads' outputs within 2e-3
+    of the oracle."""
+    print(f"workload {w.name}: 3 decode steps", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda", steps=3)
+    qs = gen_queries(w, 0, "cuda", steps=3)
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, w.max_tokens, w.v_policy, w.scheme, w.sinks)
+    cache = kvq.KVCache(cfg, "cuda")
+    cache.prefill(k, v)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    ws = cache.workspace()
+    for i in range(3):
+        out = cache.step(kn[i].contiguous(), vn[i].contiguous(), qs[i].contiguous(), scale, workspace=ws)
+    torch.cuda.synchronize()
+    if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+        assert cache.c.prequant == cache.nq_k + 1, "full window: the next leaving token is quantized ahead"
+    hpg = w.num_q_heads // w.num_kv_heads
+    worst = 0.0
+    for u in _sample_units(w, seed=1):
+        b, h = divmod(u, w.num_kv_heads)
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim)
+        else:
+            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, w.v_policy)
+        ref.prefill(host(k[b:b + 1, h:h + 1]), host(v[b:b + 1, h:h + 1]))
+        for i in range(3):
+            ref.append(host(kn[i][b:b + 1, h:h + 1]), host(vn[i][b:b + 1, h:h + 1]))
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            compare_innerq_unit(cache, ref, b, h, 0, 0)
+        else:
+            compare_unit_buffers(cache, ref, b, h, 0, 0)
+        K, V = ref.dequantized()
+        qh = host(qs[2][b:b + 1, h * hpg:(h + 1) * hpg])
+        want = oracle.attention(qh, K, V, scale)
+        got = host(out[b:b + 1, h * hpg:(h + 1) * hpg]).astype(np.float64)
+        err = float(np.abs(got - want).max())
+        worst = max(worst, err)
+        assert err <= ATOL, (u, err)
+    print(f"  sampled units ok, worst attention err {worst:.2e}", flush=True)
+    del k, v, cache
+    torch.cuda.empty_cache()
