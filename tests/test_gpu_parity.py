@@ -326,3 +326,48 @@ def test_wave_orders_agree(bits, G, L):
         outs[s] = host(o)
     assert float(np.abs(outs[1] - outs[4]).max()) <= split_tol(1)
     assert float(np.abs(outs[1] - outs[16]).max()) <= split_tol(1)
+
+
+def test_two_threads_two_streams():
+    """Two host threads each drive their own cache on their own stream at the
+    same time (prefill, then decode steps across a flush, FIFO and chunked
+    values, the matrix-core and vector kernels): every output equals the same
+    sequence run alone, bit for bit.  The library keeps no per-call global
+    state besides the thread-local error text."""
+    import threading
+    cases = [(_w(160, 2, 4, 2, 300, 2, 32, 64, 80, FIFO), kvq.KVQ_V_FIFO),
+             (_w(161, 2, 8, 2, 250, 4, 64, 64, 80), kvq.KVQ_V_CHUNK)]
+    print("two threads, two streams", flush=True)
+
+    def run(w, policy, stream, outs):
+        k, v = gen_prefill(w, 0, "cuda")
+        kn, vn = gen_new_tokens(w, 0, "cuda")
+        qs = gen_queries(w, 0, "cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            cfg, cache = make_cache(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads,
+                                    w.max_tokens, policy)
+            ws = cache.workspace()
+            cache.prefill(k, v, stream)
+            for i in range(w.steps):
+                outs.append(cache.step(kn[i].contiguous(), vn[i].contiguous(), qs[i].contiguous(), workspace=ws,
+                                       stream=stream).clone())
+        stream.synchronize()
+
+    alone = []
+    for w, p in cases:
+        o = []
+        run(w, p, torch.cuda.Stream(), o)
+        alone.append(o)
+    together = [[], []]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ts = [threading.Thread(target=run, args=(w, p, s, o)) for (w, p), s, o in zip(cases, streams, together)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    for a, b in zip(alone, together):
+        assert len(a) == len(b) == 80
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x, y), i
