@@ -399,10 +399,11 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
     need = 0 if w.scheme == kvq.KVQ_SCHEME_INNERQ else (w.residual - 1) - (c.n_tokens - c.nq_k)
     for i in range(need):
         c.append(kn[i], vn[i], stream.cuda_stream)
-    state = (c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes)
+    # (the rewind restores every host field, the quantize-ahead record too)
+    state = (c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes, c.c.prequant)
     times = []
     for _ in range(reps + 1):
-        c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes = state
+        c.c.n_tokens, c.c.nq_k, c.c.nq_v, c.c.flushes, c.c.prequant = state
         e0.record(stream)
         c.append(kn[-1], vn[-1], stream.cuda_stream)
         e1.record(stream)

@@ -214,7 +214,9 @@ typedef struct {
   int64_t prequant;     /* library-owned: 1 + the token whose quantized rows a
                            decode step has already written ahead of its leaving
                            the FIFO value queue (KIVI) or the window (InnerQ);
-                           0 = none */
+                           0 = none.  A caller that saves and restores the
+                           counters must restore this field with them (or set
+                           it to 0, which is always safe) */
 } kvq_cache;
 
 /* Validates cfg and fills *out with the buffer sizes.  Host only. */
