@@ -15,24 +15,21 @@ constexpr int kProbeThreads = 256;
 constexpr int kProbeDepth = 8;   // independent 16-byte loads in flight per thread
 
 // Grid-stride sweep of n16 16-byte words with kProbeDepth non-temporal loads
-// in flight per thread.  The words are folded into a per-thread xor that is
+// in flight per thread (each load predicated on its index, so one loop
+// covers the tail).  The words are folded into a per-thread xor that is
 // stored only if it equals a value no buffer of ones produces, so the loads
 // stay live while the kernel writes (almost) nothing.
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16,
                                                                     uint32_t *__restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kProbeDepth - 1) * stride < n16; i += kProbeDepth * stride) {
+  for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += kProbeDepth * stride) {
     u32x4 v[kProbeDepth];
 #pragma unroll
-    for (int k = 0; k < kProbeDepth; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+    for (int k = 0; k < kProbeDepth; ++k)
+      v[k] = i + k * stride < n16 ? __builtin_nontemporal_load(p + i + k * stride) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < kProbeDepth; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(p + i);
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) out[0] = acc;
 }
@@ -46,9 +43,12 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *out, hipS
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // 32 workgroups of 256 threads per compute unit, several residency rounds
-  // (read 6.7 TB/s over 4 GiB; 8 per unit read 6.1-6.2 TB/s)
-  int64_t blocks = (int64_t)(cus > 0 ? cus : 256) * 32;
+  // One workgroup of 256 threads per compute unit, 8 loads in flight per
+  // thread: 32 KB in flight per unit.  Over 4 GiB this read 7.34 TB/s; more in
+  // flight read less (64 KB per unit: 6.6-6.9 TB/s, 128 KB: 6.1 TB/s; 32
+  // workgroups per unit in several residency rounds: 6.5-6.7 TB/s), as did
+  // less (16 KB: 5.4-6.6 TB/s).
+  int64_t blocks = (int64_t)(cus > 0 ? cus : 256);
   const int64_t need = (n16 + kProbeThreads - 1) / kProbeThreads;
   if (blocks > need) blocks = need;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s,
