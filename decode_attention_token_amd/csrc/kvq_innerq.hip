@@ -443,9 +443,13 @@ void innerq_attn_kernel(AttnArgs a) {
   const int t0i = (int)t0, tb0i = (int)tb0, nqi = (int)nq;
   const int s0 = (int)((int64_t)tsteps * split / a.splits);
   const int s1 = (int)((int64_t)tsteps * (split + 1) / a.splits);
-  const int ws0 = s0 + (s1 - s0) * wave / kWaves;
-  const int ws1 = s0 + (s1 - s0) * (wave + 1) / kWaves;
-  const int nsteps = ws1 - ws0;
+  // a wave's steps: a contiguous eighth of the split, or (a.interleave,
+  // chosen on the host for long splits) every eighth step, so the
+  // workgroup's waves read neighbouring steps at any one time
+  const int ws0 = a.interleave ? s0 + wave : s0 + (s1 - s0) * wave / kWaves;
+  const int wstride = a.interleave ? kWaves : 1;
+  const int nsteps = a.interleave ? (s1 - s0 - wave + kWaves - 1) / kWaves
+                                  : s0 + (s1 - s0) * (wave + 1) / kWaves - ws0;
 
   // query slice of this lane, in log2 units and divided by the unpack scale,
   // and its plain sum (the zero-point term of the lane's group)
@@ -493,7 +497,7 @@ void innerq_attn_kernel(AttnArgs a) {
 
   auto load = [&](Buf &bf, int s) {
     s = s < nsteps ? s : nsteps - 1;   // past the end: reload the last step (never processed)
-    const uint32_t tb = (uint32_t)(tb0 + (int64_t)(ws0 + s) * TPS);   // first token of the step
+    const uint32_t tb = (uint32_t)(tb0 + (int64_t)(ws0 + wstride * s) * TPS);   // first token of the step
     const uint32_t vc = code_lane + tb * (W * 4);
     const uint32_t vm = meta_lane + tb * NG;
     bload_words<WPL>(rkc, vc, 0, bf.kw);
@@ -507,7 +511,7 @@ void innerq_attn_kernel(AttnArgs a) {
   };
 
   auto process = [&](const Buf &bf, int s) {
-    const int tok = tb0i + (ws0 + s) * TPS + tl;   // token indices fit 32 bits (capacity <= 2^25)
+    const int tok = tb0i + (ws0 + wstride * s) * TPS + tl;   // token indices fit 32 bits (capacity <= 2^25)
     const bool valid = tok >= t0i && tok < nqi;  // rows outside may hold any bits
     const float kz = (float)(int16_t)(bf.kz & 0xffffu);
     const float vz = (float)(int16_t)(bf.vz & 0xffffu);

@@ -101,8 +101,8 @@ struct AttnArgs {
   int64_t n, nq_k, nq_v;
   int64_t n_main;        // tokens [0, n_main) covered by whole key and value groups
   int splits;            // workgroups per unit over [0, n_main) (>= 1 when resid_main or sinks)
-  int interleave;        // KIVI vector-ALU kernel: waves take every eighth key group of their
-                         // split instead of a contiguous eighth
+  int interleave;        // vector-ALU kernels: waves take every eighth key group (KIVI) or
+                         // 16-token step (InnerQ) of their split instead of a contiguous eighth
   int resid_main;        // 1: the last split takes tokens [n_main, n) (keys and values each
                          // quantized or fp16 per token)
   int nparts;            // parts per unit (== splits); 1 means the kernel writes out directly

@@ -239,3 +239,26 @@ def test_innerq_key_norm_parity(w, checks):
             err = max_err(out, oracle_attention(ref, host(q), scale))
             print(f"  step {step}: n={ref.n} nq={ref.nq} err={err:.2e}", flush=True)
             assert err <= ATOL
+
+
+@pytest.mark.parametrize("splits", [1, 4, 0])
+def test_innerq_wave_orders_agree(splits):
+    """9000 tokens: with one split a wave's contiguous share would span more
+    than 32 KiB of key codes, so its waves take every eighth step; with four
+    splits each wave keeps a contiguous range.  Both orders match the oracle
+    and each other within the split tolerance."""
+    w = _w(240, 1, 4, 4, 9000, 4, 64, 32, 4, 1)
+    print(f"case {w.name} splits {splits}", flush=True)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda")
+    q = gen_queries(w, 0, "cuda")[0].contiguous()
+    _, cache, ref = _cache_and_ref(w)
+    cache.prefill(k, v)
+    cache.append(kn[0].contiguous(), vn[0].contiguous())
+    ref.prefill(host(k), host(v))
+    ref.append(host(kn[0]), host(vn[0]))
+    want = oracle_attention(ref, host(q), 1 / math.sqrt(128))
+    out = cache.attention(q, workspace=cache.workspace(splits=splits), splits=splits)
+    torch.cuda.synchronize()
+    assert max_err(out, want) <= ATOL
+    compare_innerq_buffers(cache, ref)
