@@ -71,9 +71,9 @@ def stream_ceiling(dev, stream, reps=5, settle_s=0.5, batches=3):
     """GB/s of kvq_stream_read_probe over a 4 GiB buffer (16x the MALL),
     timed with HIP events on the given stream: the median of `batches`
     batches of `reps` reads, after settle_s seconds of untimed reads.  For
-    a fraction of a second after large device buffers are freed, reads run
-    about 6% slower (the bench frees its side-timing buffers just before);
-    the settle keeps that out of the ceiling."""
+    up to 0.6 s after large device buffers are returned to the driver, reads
+    run about 6% slower; the bench returns none before its timings, and the
+    settle is a second guard."""
     buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
     out = torch.zeros(1, dtype=torch.int32, device=dev)
     sp = stream.cuda_stream
@@ -118,7 +118,8 @@ def build_caches(w, layers, max_tokens, dev, schedule=kvq.KVQ_SCHED_FIXED, kerne
         torch.cuda.synchronize()
         del k, v
         caches.append(c)
-    torch.cuda.empty_cache()
+    # (no torch.cuda.empty_cache(): returning the prefill temporaries to the
+    # driver slows every read of the device by about 6% for up to 0.6 s)
     return cfg, caches
 
 
@@ -424,8 +425,7 @@ def time_prefill_and_flush(w, dev, stream, reps=5):
         times.append(e0.elapsed_time(e1) * 1e3)
     fl_us = sorted(times[1:])[len(times[1:]) // 2]
     pb, fb = prefill_bytes(w, L), flush_bytes(w)
-    del k, v, c
-    torch.cuda.empty_cache()
+    del k, v, c   # kept in torch's cache: freeing them would slow the reads timed next
     return {"prefill": {"us": round(pre_us, 1), "bytes": pb, "GB/s": round(pb / pre_us / 1e3, 1),
                         "frac": round(pb / pre_us / 1e3 / HBM_PEAK_GBS, 4), "tokens": L},
             "flush": {"us": round(fl_us, 2), "bytes": fb, "GB/s": round(fb / fl_us / 1e3, 1),
@@ -572,11 +572,10 @@ def main():
                 nb += attn_bytes(w, c.n_tokens, c.nq_k, c.nq_v)
         return nb
 
-    # Steady state: the device's clocks ramp under sustained load, and for a
-    # fraction of a second after large buffers are freed (the prefill
-    # temporaries, just above) reads run up to 6% slower, so before anything
-    # is timed the attention kernel runs back to back (untimed) for at least
-    # settle_s.
+    # Steady state: the device's clocks ramp under sustained load (and for up
+    # to 0.6 s after large buffers are returned to the driver, which the bench
+    # avoids, reads run about 6% slower), so before anything is timed the
+    # attention kernel runs back to back (untimed) for at least settle_s.
     last = total - 1
 
     def attention_pass():
@@ -706,8 +705,7 @@ def main():
                            "after_loop": {"avg_call_us": round(after_us, 2), "bytes_per_call": int(after_bytes),
                                           "n_tokens": caches[0].n_tokens}},
         "settle": {"seconds": round(settle_s, 3), "attention_calls": settle_calls,
-                   "note": "untimed back-to-back attention calls before any timing (clocks reach steady state; "
-                           "the slow reads that follow freeing the prefill temporaries are over)"},
+                   "note": "untimed back-to-back attention calls before any timing (clocks reach steady state)"},
         "host_enqueue_us_per_launch": round(t_enq / (steps * layers) * 1e6, 2),
         "loop_steps_with_flush": int(sum(flushed)),
         "loop_steps_single_launch": len(plain),
