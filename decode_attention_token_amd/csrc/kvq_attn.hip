@@ -25,8 +25,8 @@
 // value queue, keys may be quantized while their values are still fp16).
 // Within a wave, LPT lanes share a
 // token and each owns 128 / LPT channels, so a wave step reads contiguous key
-// and value rows with 8- or 16-byte loads; loads run two steps ahead of the
-// arithmetic through a ring of three register buffers.  Each wave keeps its
+// and value rows with 8- or 16-byte loads; loads run one step ahead of the
+// arithmetic through a ring of two register buffers.  Each wave keeps its
 // own online-softmax state with a wave-uniform running maximum that is raised
 // only when a score exceeds it by more than a margin, so the rescale branch is
 // rare and uniform.  A unit with one part writes its output directly;
