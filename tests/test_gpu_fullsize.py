@@ -111,3 +111,64 @@ def test_fullsize_decode_steps(w):
     print(f"  sampled units ok, worst attention err {worst:.2e}", flush=True)
     del k, v, cache
     torch.cuda.empty_cache()
+
+
+# The bench's variant rows at full size: the value queue, packed metadata, the
+# work-queue schedule, the vector-ALU kernel on the grouped-query shape, and
+# per-channel key scales.  Same check as above after three decode steps.
+VARIANTS = [
+    ("llama2-7b-fifo", LLAMA7B_2BIT, dict(v_policy=kvq.KVQ_V_FIFO)),
+    ("llama2-7b-meta16", LLAMA7B_2BIT, dict(meta=kvq.KVQ_META_F16)),
+    ("b64-4bit-meta16", LLAMA7B_4BIT, dict(meta=kvq.KVQ_META_F16)),
+    ("gqa-queue", GQA_LONG, dict(schedule=kvq.KVQ_SCHED_QUEUE)),
+    ("gqa-valu", GQA_LONG, dict(kernel=kvq.KVQ_KERNEL_VALU)),
+    ("gqa-fifo", GQA_LONG, dict(v_policy=kvq.KVQ_V_FIFO)),
+    ("innerq-keynorm", LONG_4BIT, dict(key_norm=kvq.KVQ_KEYNORM_PROMPT)),
+]
+
+
+@pytest.mark.parametrize("name,w,opts", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_fullsize_bench_variants(name, w, opts):
+    print(f"workload {w.name} variant {name}: 3 decode steps", flush=True)
+    policy = opts.get("v_policy", w.v_policy)
+    meta = opts.get("meta", kvq.KVQ_META_F32)
+    key_norm = opts.get("key_norm", kvq.KVQ_KEYNORM_NONE)
+    k, v = gen_prefill(w, 0, "cuda")
+    kn, vn = gen_new_tokens(w, 0, "cuda", steps=3)
+    qs = gen_queries(w, 0, "cuda", steps=3)
+    cfg = kvq.make_config(w.bits, w.group, w.residual, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                          w.max_tokens, policy, w.scheme, w.sinks, meta, opts.get("schedule", kvq.KVQ_SCHED_FIXED),
+                          opts.get("kernel", kvq.KVQ_KERNEL_AUTO), key_norm)
+    cache = kvq.KVCache(cfg, "cuda")
+    cache.prefill(k, v)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    ws = cache.workspace()
+    for i in range(3):
+        out = cache.step(kn[i].contiguous(), vn[i].contiguous(), qs[i].contiguous(), scale, workspace=ws)
+    torch.cuda.synchronize()
+    hpg = w.num_q_heads // w.num_kv_heads
+    worst = 0.0
+    for u in _sample_units(w, seed=2):
+        b, h = divmod(u, w.num_kv_heads)
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            ref = oracle.InnerQCache(w.bits, w.group, w.residual, w.sinks, 1, 1, w.head_dim, key_norm=bool(key_norm))
+        else:
+            ref = oracle.QuantizedKVCache(w.bits, w.group, w.residual, 1, 1, w.head_dim, policy,
+                                          oracle.META_F16 if meta == kvq.KVQ_META_F16 else oracle.META_F32)
+        ref.prefill(host(k[b:b + 1, h:h + 1]), host(v[b:b + 1, h:h + 1]))
+        for i in range(3):
+            ref.append(host(kn[i][b:b + 1, h:h + 1]), host(vn[i][b:b + 1, h:h + 1]))
+        if w.scheme == kvq.KVQ_SCHEME_INNERQ:
+            compare_innerq_unit(cache, ref, b, h, 0, 0)
+        else:
+            compare_unit_buffers(cache, ref, b, h, 0, 0)
+        K, V = ref.dequantized()
+        qh = host(qs[2][b:b + 1, h * hpg:(h + 1) * hpg])
+        want = oracle.attention(qh, K, V, scale)
+        got = host(out[b:b + 1, h * hpg:(h + 1) * hpg]).astype(np.float64)
+        err = float(np.abs(got - want).max())
+        worst = max(worst, err)
+        assert err <= ATOL, (u, err)
+    print(f"  sampled units ok, worst attention err {worst:.2e}", flush=True)
+    del k, v, cache
+    torch.cuda.empty_cache()
