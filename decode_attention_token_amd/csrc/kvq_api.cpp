@@ -321,13 +321,9 @@ kvq_status kvq_quantize_prefill(const kvq_config *cfg, kvq_cache *cache, const u
   hipError_t e = kvq::launch_copy_rows(cv.k_sink, cv.v_sink, cfg->sink_tokens, k, v, len, 0, (int)ns, 0, units,
                                        stream);
   if (e != hipSuccess) return device_error(e, "copy sink tokens");
-  if (nq_k > 0) {
-    e = kvq::launch_quantize_keys(cv, units, k, len, ns, (int)(nq_k / G), 0, stream);
-    if (e != hipSuccess) return device_error(e, "quantize keys");
-  }
-  if (nq_v > 0) {
-    e = kvq::launch_quantize_values(cv, units, v, len, ns, (int)nq_v, 0, stream);
-    if (e != hipSuccess) return device_error(e, "quantize values");
+  if (nq_k > 0 || nq_v > 0) {
+    e = kvq::launch_quantize_kv(cv, units, k, v, len, ns, (int)(nq_k / G), (int)nq_v, stream);
+    if (e != hipSuccess) return device_error(e, "quantize keys and values");
   }
   if (L > nq_k) {
     e = kvq::launch_copy_to_residual(cv, units, k, nullptr, len, ns + nq_k, (int)(L - nq_k), (int)(nq_k % R), true,

@@ -57,6 +57,13 @@ hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t 
                                   int64_t src_rows, int64_t src_row0, int count,
                                   int64_t dst_row0, hipStream_t s);
 
+// A prefill's quantization: `ngroups` key groups per unit (into groups 0 ..)
+// and `count` value rows per unit (into rows 0 ..), both from source rows
+// src_row0 + i of [unit][src_rows][128] fp16; one launch at G = 32, the two
+// quantizer launches otherwise.
+hipError_t launch_quantize_kv(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
+                              int64_t src_rows, int64_t src_row0, int ngroups, int count, hipStream_t s);
+
 // Copy rows [row0, row0 + count) of src ([unit][src_rows][128] fp16) into
 // residual slots slot0 + i of both rings (keys from ksrc, values from vsrc).
 hipError_t launch_copy_to_residual(const CacheView &c, int units, const uint16_t *ksrc,

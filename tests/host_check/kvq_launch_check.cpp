@@ -173,6 +173,26 @@ hipError_t launch_quantize_values(const CacheView &c, int units, const uint16_t 
   return hipSuccess;
 }
 
+hipError_t launch_quantize_kv(const CacheView &c, int units, const uint16_t *ksrc, const uint16_t *vsrc,
+                              int64_t src_rows, int64_t src_row0, int ngroups, int count, hipStream_t) {
+  if (units <= 0 || (ngroups <= 0 && count <= 0)) return hipSuccess;
+  ++g_launches;
+  const int64_t kblocks = ngroups > 0 ? ((int64_t)units * ngroups + 3) / 4 : 0;
+  const int64_t vblocks = count > 0 ? ((int64_t)units * count + 127) / 128 : 0;
+  expect((int64_t)units * (ngroups > 0 ? ngroups : 0) <= INT32_MAX - 4, "prefill key grid");
+  expect((int64_t)units * (count > 0 ? count : 0) <= INT32_MAX - 256, "prefill value grid");
+  expect(kblocks + vblocks <= INT32_MAX, "prefill grid");
+  if (ngroups > 0) {
+    need_fp16(ksrc, units, src_rows, src_row0, (int64_t)ngroups * c.group, "prefill keys: source");
+    need_key_groups(c, units, 0, ngroups, "prefill keys: cache");
+  }
+  if (count > 0) {
+    need_fp16(vsrc, units, src_rows, src_row0, count, "prefill values: source");
+    need_rows(c, true, units, 0, count, "prefill values: cache");
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_flush(const CacheView &c, int units, const uint16_t *k_new, const uint16_t *v_new, int slot,
                         int64_t dst_group0, int64_t dst_row0, hipStream_t) {
   if (units <= 0) return hipSuccess;
