@@ -12,7 +12,7 @@
 // Buffers are fake address ranges registered by size (nothing is ever
 // dereferenced), so the sweep reaches max_tokens = 2^25.
 //
-// The driver runs (1) the validation paths of every entry point, checking
+// The main program runs (1) the validation paths of every entry point, checking
 // the status, that kvq_last_error explains it and that the cache struct is
 // left unchanged, and (2) seeded sequences of prefill, append, attention and
 // decode steps over a sweep of the supported shapes: bits, group size,
@@ -378,7 +378,7 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *out, hipS
 
 }  // namespace kvq
 
-// ---------------------------------------------------------------- driver
+// ---------------------------------------------------------------- main program
 namespace {
 
 struct Setup {

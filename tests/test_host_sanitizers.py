@@ -3,8 +3,8 @@
 kvq_launch_check.cpp, whose stubs stand in for the kernel launches and check
 every launch's index ranges against the kvq_layout buffer sizes, the ring
 liveness of the fp16 tokens an attention launch reads and the 32-bit offsets,
-over a sweep of the supported shapes up to 2^25 tokens; the driver also runs
-the validation paths of every entry point.  A planted mistake (a buffer
+over a sweep of the supported shapes up to 2^25 tokens; its main program also
+runs the validation paths of every entry point.  A planted mistake (a buffer
 registered 16 bytes short) must make the checker abort."""
 import os
 import shutil
