@@ -30,10 +30,12 @@
 //    tokens.  Output lane (column n, row block r) holds 4 tokens' scores for
 //    column n; only columns of the step's own group slot are used.
 //  * value codes are transposed to tokens-along-K through LDS: each wave
-//    writes its step's bf16 codes as token rows and reads them back with the
-//    gfx950 transposing LDS read (16-bit elements), so lane (channel, r)
-//    holds the codes of tokens 4r..4r+3 of each block -- exactly the token
-//    set whose scores the same lane index holds in the key output.
+//    writes its step's codes as token rows and reads them back with a gfx950
+//    transposing LDS read, so lane (channel, r) holds the codes of tokens
+//    4r..4r+3 of each block -- exactly the token set whose scores the same
+//    lane index holds in the key output.  2-bit codes travel as 4-bit fields
+//    (a quarter of the bytes of bf16; converted to bf16 after the read),
+//    4-bit codes as bf16.
 //  * value MFMA (16x16x32): A = w limbs, rows = (head, 32-channel slice),
 //    K = the 32 tokens; B = transposed codes, columns = 16 channels.  The
 //    weights move from the key output lanes to the A lanes with one quad
@@ -71,7 +73,9 @@ typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kHpg = 4;   // query heads per kv head on this path
 // Tokens the fp16 part can take: sinks (<= 512), the residual (<= 512) and a
@@ -160,13 +164,34 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Row length (u16) of the per-wave bf16 value-code tile.
+// Row length (u16) of the per-wave bf16 value-code tile (4-bit codes).
 constexpr int kVRow = kHeadDim + 16;
+// 2-bit codes go through a per-wave tile of 4-bit fields instead: a token row
+// is 64 bytes (rows kNRow bytes apart), and the step's second 16-token block
+// starts kNBlk bytes after the first.  With 80-byte rows and the second block
+// 64 bytes further on, the sixteen 8-byte rows one 16-lane group of a
+// transposing read takes (tokens 4 kq + e and 16 + 4 kq + e, two 16-channel
+// chunks) cover all 32 four-byte banks once, and the eight 16-byte row
+// pieces a group of lanes writes fall in different bank quads.
+constexpr int kNRow = 80;
+constexpr int kNBlk = 16 * kNRow + 64;
+static_assert(2 * kNBlk <= 32 * kVRow * 2, "nibble tile fits the tile area");
 // Row length (floats) of the per-wave key-metadata staging, [4 groups][kKmRow].
 constexpr int kKmRow = kHeadDim + 4;
 
 // Channel offset (within 8) of element e of word r of a pass: 0,2 | 1,3 | 4,6 | 5,7.
 __device__ __host__ constexpr int pass_chan(int r, int e) { return (r >> 1) * 4 + (r & 1) + 2 * e; }
+
+// Channel (within 16) of 4-bit field f of a tile chunk: even channels in the
+// first word, odd ones in the second.
+__device__ __host__ constexpr int nib_chan(int f) { return f < 8 ? 2 * f : 2 * f - 15; }
+
+// Fields 2B and 2B + 1 of a word of 2-bit codes held as 4-bit fields, as a
+// bf16 pair (fp4 field c is worth c / 2, so scale 2 gives the code itself).
+template <int B>
+__device__ __forceinline__ uint32_t nib_bf16(uint32_t f) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 2.0f, B));
+}
 
 template <int GS>
 struct GqaGeo {
@@ -513,7 +538,7 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *kmZ = kmS + Gm::KM;
   float *lvS = kmZ + Gm::KM;
   float *lvZ = lvS + Gm::VM;
-  uint16_t *vt = reinterpret_cast<uint16_t *>(lvZ + Gm::VM);   // bf16 value codes [32][kVRow]
+  uint16_t *vt = reinterpret_cast<uint16_t *>(lvZ + Gm::VM);   // value-code tile (bf16 [32][kVRow], or 4-bit fields)
 
   // scaled query of the unit's four heads
   for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads)
@@ -528,6 +553,20 @@ void gqa_mfma_kernel(AttnArgs a) {
   // c0 + 4 (j mod 4) .. + 3
   uint16_t *vt_w = vt + i16 * kVRow + 32 * kq;
   const uint16_t *vt_r = vt + (4 * kq + (i16 >> 2)) * kVRow + 4 * (i16 & 3);
+  // 2-bit codes: lane (token i16 of block k, kq) writes its 32 codes as 4-bit
+  // fields at row i16 of block k, bytes 16 kq ..: chunk 2 kq + x (8 bytes)
+  // holds channels 16 (2 kq + x) + {0, 2, .., 14} in its first word and
+  // + {1, 3, .., 15} in its second, so field f of a chunk is channel
+  // 16 chunk + nib_chan(f).  A transposing 4-bit read returns to lane i of a
+  // 16-lane group field i of the 8-byte row each lane j of the group points
+  // at, in lane order; lane j points at token 4 kq + (j mod 4) of block
+  // (j / 4) mod 2, chunk 2 u + j / 8.  So lane (column i16, kq) receives, in
+  // its first word, the codes of channel 16 (2u) + nib_chan(i16) for tokens
+  // 4 kq + e and 16 + 4 kq + e (e = 0..3, in that order: the key-output token
+  // order), and the same for chunk 2u + 1 in its second word.
+  uint8_t *const nt = reinterpret_cast<uint8_t *>(vt);
+  uint8_t *const nt_w = nt + i16 * kNRow + 16 * kq;
+  const uint8_t *const nt_r = nt + ((i16 >> 2) & 1) * kNBlk + (4 * kq + (i16 & 3)) * kNRow + 8 * (i16 >> 3);
 
   // online-softmax state
   float m[kHpg], mthr[kHpg];
@@ -722,17 +761,23 @@ void gqa_mfma_kernel(AttnArgs a) {
     // step, LA steps ahead; its first step is at least SPC away)
     if (kk == (LA == 3 ? 0 : 1)) stage_kmeta(kmr);
     stage_vmeta(bf.vs, bf.vz);
-    // bf16 value codes of both blocks into the tile
+    // value codes of both blocks into the tile: 4-bit fields (2-bit codes)
+    // or bf16 (4-bit codes)
     static_for<2>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      using C = CodesBf16<BITS>;
       const uint32_t *w = bf.vw + k * WPL;
-      static_for<4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
-            make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
-                       C::template word<4 * q + 3>(w));
-      });
+      if constexpr (BITS == 2) {
+        *reinterpret_cast<uint4 *>(nt_w + k * kNBlk) =
+            make_uint4(w[0] & 0x33333333u, (w[0] >> 2) & 0x33333333u, w[1] & 0x33333333u, (w[1] >> 2) & 0x33333333u);
+      } else {
+        using C = CodesBf16<BITS>;
+        static_for<4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
+              make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
+                         C::template word<4 * q + 3>(w));
+        });
+      }
     });
     wave_sync();
     sc[0] += sl2[0];
@@ -804,15 +849,31 @@ void gqa_mfma_kernel(AttnArgs a) {
     }
 
     // values: 16 channel positions at a time, transposed by the LDS reads
-    static_for<8>([&](auto cc) {
-      constexpr int cb = decltype(cc)::value;
-      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * cb));
-      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * kVRow + 16 * cb));
-      const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
-      const u32x4 bv = {h0[0], h0[1], h1[0], h1[1]};
-      acc[cb] = mma_x32(ahi, bv, acc[cb]);
-      acc[cb] = mma_x32(alo, bv, acc[cb]);
-    });
+    if constexpr (BITS == 2) {
+      // one 4-bit transposing read per pair of 16-channel chunks; fields 2q,
+      // 2q + 1 of a word are the tokens of bf16 word q of the operand
+      static_for<4>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const i32x2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(nt_r + 16 * u));
+        static_for<2>([&](auto xc) {
+          constexpr int x = decltype(xc)::value, cb = 2 * u + x;
+          const uint32_t f = (uint32_t)r[x];
+          const u32x4 bv = {nib_bf16<0>(f), nib_bf16<1>(f), nib_bf16<2>(f), nib_bf16<3>(f)};
+          acc[cb] = mma_x32(ahi, bv, acc[cb]);
+          acc[cb] = mma_x32(alo, bv, acc[cb]);
+        });
+      });
+    } else {
+      static_for<8>([&](auto cc) {
+        constexpr int cb = decltype(cc)::value;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * cb));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * kVRow + 16 * cb));
+        const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
+        const u32x4 bv = {h0[0], h0[1], h1[0], h1[1]};
+        acc[cb] = mma_x32(ahi, bv, acc[cb]);
+        acc[cb] = mma_x32(alo, bv, acc[cb]);
+      });
+    }
   };
 
   if (nsteps > 0) {
@@ -882,7 +943,8 @@ void gqa_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const int pp = 16 * (cb & 1) + i16;
-      const int ch = 32 * (cb >> 1) + 8 * (pp >> 3) + pass_chan((pp >> 1) & 3, pp & 1);
+      const int ch = BITS == 2 ? 16 * cb + nib_chan(i16)
+                               : 32 * (cb >> 1) + 8 * (pp >> 3) + pass_chan((pp >> 1) & 3, pp & 1);
       rows[(wave * kHpg + kq) * kHeadDim + ch] = acc[cb][cb >> 1] + vbs[cb >> 1];
     }
   }
