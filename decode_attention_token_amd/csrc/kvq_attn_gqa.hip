@@ -33,9 +33,9 @@
 //    writes its step's codes as token rows and reads them back with a gfx950
 //    transposing LDS read, so lane (channel, r) holds the codes of tokens
 //    4r..4r+3 of each block -- exactly the token set whose scores the same
-//    lane index holds in the key output.  2-bit codes travel as 4-bit fields
-//    (a quarter of the bytes of bf16; converted to bf16 after the read),
-//    4-bit codes as bf16.
+//    lane index holds in the key output.  The codes travel as 4-bit fields
+//    (2-bit codes) or bytes (4-bit codes), a quarter or half of the bytes of
+//    bf16, and are converted to bf16 after the read.
 //  * value MFMA (16x16x32): A = w limbs, rows = (head, 32-channel slice),
 //    K = the 32 tokens; B = transposed codes, columns = 16 channels.  The
 //    weights move from the key output lanes to the A lanes with one quad
@@ -71,10 +71,7 @@ typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kHpg = 4;   // query heads per kv head on this path
@@ -164,9 +161,8 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Row length (u16) of the per-wave bf16 value-code tile (4-bit codes).
-constexpr int kVRow = kHeadDim + 16;
-// 2-bit codes go through a per-wave tile of 4-bit fields instead: a token row
+// Value codes are transposed through a per-wave LDS tile.  2-bit codes go
+// through it as 4-bit fields: a token row
 // is 64 bytes (rows kNRow bytes apart), and the step's second 16-token block
 // starts kNBlk bytes after the first.  With 80-byte rows and the second block
 // 64 bytes further on, the sixteen 8-byte rows one 16-lane group of a
@@ -175,7 +171,17 @@ constexpr int kVRow = kHeadDim + 16;
 // pieces a group of lanes writes fall in different bank quads.
 constexpr int kNRow = 80;
 constexpr int kNBlk = 16 * kNRow + 64;
-static_assert(2 * kNBlk <= 32 * kVRow * 2, "nibble tile fits the tile area");
+// 4-bit codes go through it as bytes: a token row is 128 bytes (rows kBRow
+// bytes apart, the second block kBBlk bytes after the first).  With 144-byte
+// rows and the second block 64 bytes further on, the eight 16-byte row pieces
+// one 16-lane group of a transposing 8-bit read takes (tokens 4 kq + e and
+// 16 + 4 kq + e, one 16-channel chunk) fall in different bank quads, and so do
+// the eight row pieces a group of lanes writes.
+constexpr int kBRow = 144;
+constexpr int kBBlk = 16 * kBRow + 64;
+// Bytes of the tile area: the byte tile's extent, which holds the 4-bit one.
+constexpr int kTileBytes = kBBlk + 16 * kBRow;
+static_assert(kNBlk + 16 * kNRow <= kTileBytes && kTileBytes % 16 == 0, "tile area");
 // Row length (floats) of the per-wave key-metadata staging, [4 groups][kKmRow].
 constexpr int kKmRow = kHeadDim + 4;
 
@@ -193,6 +199,17 @@ __device__ __forceinline__ uint32_t nib_bf16(uint32_t f) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f, 2.0f, B));
 }
 
+// Channel (within 16) of byte p of a byte-tile chunk: the even codes of a
+// code word, then its odd codes, for two code words.
+__device__ __host__ constexpr int byte_chan(int p) { return 8 * (p >> 3) + 2 * (p & 3) + ((p >> 2) & 1); }
+
+// Bytes 2H and 2H + 1 of a word of 4-bit codes held as bytes, as a bf16 pair
+// (an fp8 e4m3 byte c < 16 is worth c / 512, so scale 512 gives the code).
+template <int H>
+__device__ __forceinline__ uint32_t byte_bf16(uint32_t f) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f, 512.0f, H == 1));
+}
+
 template <int GS>
 struct GqaGeo {
   static constexpr int SPG = GS / 32;                 // 32-token steps per key group
@@ -206,11 +223,8 @@ struct GqaGeo {
   // value S and Z of a step [VGR][32]
   static constexpr int KM = 4 * kKmRow;
   static constexpr int VM = VGR * 32;
-  // value codes of a step as bf16, [32 tokens][kVRow] u16 (rows padded by 16
-  // elements, so the four rows one 16-lane group of a transposing read takes
-  // lie on disjoint banks: 13% fewer LDS bank-conflict cycles than a padding
-  // of 8)
-  static constexpr int VT = 32 * kVRow / 2;
+  // value codes of a step (the tile area, in floats)
+  static constexpr int VT = kTileBytes / 4;
   static constexpr int PER_WAVE = 2 * KM + 2 * VM + VT;
   static constexpr int ROWS = kGqaWaves * kHpg * kHeadDim;   // combine rows [wave][h][128]
   static constexpr int STAGING = kGqaWaves * PER_WAVE;
@@ -538,21 +552,13 @@ void gqa_mfma_kernel(AttnArgs a) {
   float *kmZ = kmS + Gm::KM;
   float *lvS = kmZ + Gm::KM;
   float *lvZ = lvS + Gm::VM;
-  uint16_t *vt = reinterpret_cast<uint16_t *>(lvZ + Gm::VM);   // value-code tile (bf16 [32][kVRow], or 4-bit fields)
+  uint8_t *const nt = reinterpret_cast<uint8_t *>(lvZ + Gm::VM);   // value-code tile (4-bit fields or bytes)
 
   // scaled query of the unit's four heads
   for (int i = tid; i < kHpg * kHeadDim; i += kGqaThreads)
     qsm[i] = h2f(a.q[((int64_t)(b * a.hq + hk * kHpg)) * kHeadDim + i]) * a.qscale;
   __syncthreads();
 
-  // value codes: lane (token i16 of block k, kq) writes its 32 bf16 codes
-  // (convert order) at row 16k + i16, positions 32 kq ..; the transposed
-  // reads then give lane (column i16, kq) positions c0 + i16 of tokens
-  // 4 kq + e (first read) and 16 + 4 kq + e (second read), e = 0..3: input
-  // lane j of a 16-lane group supplies row 4 kq + j / 4, positions
-  // c0 + 4 (j mod 4) .. + 3
-  uint16_t *vt_w = vt + i16 * kVRow + 32 * kq;
-  const uint16_t *vt_r = vt + (4 * kq + (i16 >> 2)) * kVRow + 4 * (i16 & 3);
   // 2-bit codes: lane (token i16 of block k, kq) writes its 32 codes as 4-bit
   // fields at row i16 of block k, bytes 16 kq ..: chunk 2 kq + x (8 bytes)
   // holds channels 16 (2 kq + x) + {0, 2, .., 14} in its first word and
@@ -564,9 +570,20 @@ void gqa_mfma_kernel(AttnArgs a) {
   // its first word, the codes of channel 16 (2u) + nib_chan(i16) for tokens
   // 4 kq + e and 16 + 4 kq + e (e = 0..3, in that order: the key-output token
   // order), and the same for chunk 2u + 1 in its second word.
-  uint8_t *const nt = reinterpret_cast<uint8_t *>(vt);
   uint8_t *const nt_w = nt + i16 * kNRow + 16 * kq;
   const uint8_t *const nt_r = nt + ((i16 >> 2) & 1) * kNBlk + (4 * kq + (i16 & 3)) * kNRow + 8 * (i16 >> 3);
+  // 4-bit codes: lane (token i16 of block k, kq) writes its 32 codes as bytes
+  // at row i16 of block k, bytes 32 kq ..: chunk 2 kq + x (16 bytes) holds
+  // the even and then the odd codes of code words 2x and 2x + 1, so byte p of
+  // a chunk is channel 16 chunk + byte_chan(p).  A transposing 8-bit read
+  // returns to lane i of a 16-lane group, as its byte e, byte i mod 8 of the
+  // 8-byte piece lane 2e + i / 8 points at; lane j points at token
+  // 4 kq + (e mod 4) of block e / 4 (e = j / 2), bytes 8 (j mod 2) of the
+  // chunk.  So lane (column i16, kq) receives the codes of channel
+  // 16 chunk + byte_chan(i16) for tokens 4 kq + e and 16 + 4 kq + e (e = 0..3,
+  // the key-output token order), one chunk per read.
+  uint8_t *const bt_w = nt + i16 * kBRow + 32 * kq;
+  const uint8_t *const bt_r = nt + ((i16 >> 3) & 1) * kBBlk + (4 * kq + ((i16 >> 1) & 3)) * kBRow + 8 * (i16 & 1);
 
   // online-softmax state
   float m[kHpg], mthr[kHpg];
@@ -762,7 +779,7 @@ void gqa_mfma_kernel(AttnArgs a) {
     if (kk == (LA == 3 ? 0 : 1)) stage_kmeta(kmr);
     stage_vmeta(bf.vs, bf.vz);
     // value codes of both blocks into the tile: 4-bit fields (2-bit codes)
-    // or bf16 (4-bit codes)
+    // or bytes (4-bit codes)
     static_for<2>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const uint32_t *w = bf.vw + k * WPL;
@@ -770,13 +787,10 @@ void gqa_mfma_kernel(AttnArgs a) {
         *reinterpret_cast<uint4 *>(nt_w + k * kNBlk) =
             make_uint4(w[0] & 0x33333333u, (w[0] >> 2) & 0x33333333u, w[1] & 0x33333333u, (w[1] >> 2) & 0x33333333u);
       } else {
-        using C = CodesBf16<BITS>;
-        static_for<4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          *reinterpret_cast<uint4 *>(vt_w + k * 16 * kVRow + 8 * q) =
-              make_uint4(C::template word<4 * q>(w), C::template word<4 * q + 1>(w), C::template word<4 * q + 2>(w),
-                         C::template word<4 * q + 3>(w));
-        });
+        *reinterpret_cast<uint4 *>(bt_w + k * kBBlk) =
+            make_uint4(w[0] & 0x0F0F0F0Fu, (w[0] >> 4) & 0x0F0F0F0Fu, w[1] & 0x0F0F0F0Fu, (w[1] >> 4) & 0x0F0F0F0Fu);
+        *reinterpret_cast<uint4 *>(bt_w + k * kBBlk + 16) =
+            make_uint4(w[2] & 0x0F0F0F0Fu, (w[2] >> 4) & 0x0F0F0F0Fu, w[3] & 0x0F0F0F0Fu, (w[3] >> 4) & 0x0F0F0F0Fu);
       }
     });
     wave_sync();
@@ -864,12 +878,13 @@ void gqa_mfma_kernel(AttnArgs a) {
         });
       });
     } else {
+      // one 8-bit transposing read per 16-channel chunk; bytes 2q, 2q + 1 of
+      // the pair of words are the tokens of bf16 word q of the operand
       static_for<8>([&](auto cc) {
         constexpr int cb = decltype(cc)::value;
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * cb));
-        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt_r + 16 * kVRow + 16 * cb));
-        const u32x2 h0 = __builtin_bit_cast(u32x2, r0), h1 = __builtin_bit_cast(u32x2, r1);
-        const u32x4 bv = {h0[0], h0[1], h1[0], h1[1]};
+        const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(bt_r + 16 * cb));
+        const u32x4 bv = {byte_bf16<0>((uint32_t)r[0]), byte_bf16<1>((uint32_t)r[0]), byte_bf16<0>((uint32_t)r[1]),
+                          byte_bf16<1>((uint32_t)r[1])};
         acc[cb] = mma_x32(ahi, bv, acc[cb]);
         acc[cb] = mma_x32(alo, bv, acc[cb]);
       });
@@ -942,9 +957,7 @@ void gqa_mfma_kernel(AttnArgs a) {
     // its 32-channel slice is cb / 2, the accumulator row to keep
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      const int pp = 16 * (cb & 1) + i16;
-      const int ch = BITS == 2 ? 16 * cb + nib_chan(i16)
-                               : 32 * (cb >> 1) + 8 * (pp >> 3) + pass_chan((pp >> 1) & 3, pp & 1);
+      const int ch = 16 * cb + (BITS == 2 ? nib_chan(i16) : byte_chan(i16));
       rows[(wave * kHpg + kq) * kHeadDim + ch] = acc[cb][cb >> 1] + vbs[cb >> 1];
     }
   }
